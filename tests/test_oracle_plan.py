@@ -1,0 +1,134 @@
+"""Pins of the oracle planner: the pages' worked examples plus invariants."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import plan as PL
+from tests.conftest import load_golden
+
+
+@pytest.mark.parametrize("alpha,beta", [(0, 1), (2, 1)])
+def test_lpt_worked_example(alpha, beta):
+    g = load_golden("lpt_example.json")
+    p = PL.make_plan(g["kv_lens"], None, 1, 1, g["num_ctas"], alpha=alpha, beta=beta)
+    assert p.total_work == g["total_work"]
+    assert p.chunk_limit == g["expected_chunk_limit"]
+    a_chunks = [it.kv_len for it in p.items if it.req == 0]
+    assert a_chunks == g["expected_chunks_of_A"]
+    order = sorted(range(len(p.items)), key=lambda m: -p.items[m].kv_len)
+    assert [p.items[m].kv_len for m in order] == g["expected_sorted_lengths"]
+    names = {}
+    for m, it in enumerate(p.items):
+        names[m] = "ABCD"[it.req] + (str(it.kv_start // p.chunk_limit) if it.req == 0 else "")
+    got = [[names[m] for m in q] for q in p.queues]
+    assert got == g["expected_cta_contents"]
+    assert sum(p.items[m].kv_len for m in p.queues[3]) == g["expected_cta3_total"]
+    if alpha == 0:
+        assert p.worker_cost[3] == g["expected_cta3_total"]
+    # A was split into four chunks and merges in KV order; B, C, D write directly
+    assert len(p.merge_tiles) == 1 and p.tiles[p.merge_tiles[0]].req == 0
+    slots = p.merge_slots[0]
+    starts = [next(it.kv_start for it in p.items if it.slot == s) for s in slots]
+    assert starts == sorted(starts) == [0, 313, 626, 939]
+    assert all(it.slot == -1 for it in p.items if it.req != 0)
+
+
+def test_tile_choice_example():
+    g = load_golden("tile_choice.json")
+    assert PL.choose_tile_q(g["qo_lens"]) == g["expected_tile"]
+    assert PL.choose_tile_q([200]) == 128 and PL.choose_tile_q([17]) == 32
+
+
+def test_gqa_packing_examples():
+    g = load_golden("gqa_packing.json")
+    e = g["eq3_example"]
+    p = PL.make_plan([10], [e["L_q"]], e["g"], 1, 1, tile_q=16)
+    assert p.tiles[0].row_end - p.tiles[0].row_start == e["expected_rows"]
+    o = g["overview_example"]
+    p = PL.make_plan([10], [o["qo_len"]], o["g"] * 2, 2, 1)
+    assert p.tiles[0].row_end == o["expected_packed"] and p.tile_q == o["expected_tile"]
+
+
+def test_capacity_arithmetic():
+    g = load_golden("capacity.json")
+    n = PL.partial_capacity_bound(g["C"], g["T_q"], g["H_q"], g["d"])
+    assert n == g["expected_elements"]
+    mib, tol = g["expected_mib_at_4_bytes"]
+    assert abs(n * 4 / 2**20 - mib) <= tol
+
+
+def _random_case(rng):
+    B = int(rng.integers(0, 12))
+    kv = rng.integers(0, 3000, size=B)
+    if rng.random() < 0.3:
+        kv[rng.random(B) < 0.3] = 0
+    causal = bool(rng.random() < 0.5)
+    qo = None if rng.random() < 0.4 else rng.integers(1, 300, size=B)
+    Hk = int(rng.choice([1, 2, 8]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    C = int(rng.integers(1, 70))
+    tq = int(rng.choice([0, 0, 16, 64]))
+    return kv, qo, Hk * g, Hk, C, tq, causal
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_invariants(seed):
+    rng = np.random.default_rng(seed)
+    kv, qo, Hq, Hk, C, tq, causal = _random_case(rng)
+    p = PL.make_plan(kv, qo, Hq, Hk, C, tile_q=tq, causal=causal)
+    again = PL.make_plan(kv, qo, Hq, Hk, C, tile_q=tq, causal=causal)
+    assert p == again  # identical input -> identical plan
+    g = Hq // Hk
+    qol = [1] * len(kv) if qo is None else list(qo)
+    # every visible (tile, token) covered exactly once, chunks <= L
+    for t_id, t in enumerate(p.tiles):
+        cov = np.zeros(t.vis, dtype=int)
+        for m in t.items:
+            it = p.items[m]
+            assert it.tile == t_id and 0 < it.kv_len <= p.chunk_limit
+            cov[it.kv_start : it.kv_start + it.kv_len] += 1
+        assert np.all(cov == 1)
+        last_pos = (t.row_end - 1) // g
+        l_kv, l_qo = int(kv[t.req]), int(qol[t.req])
+        exp_vis = max(0, min(l_kv, l_kv - l_qo + last_pos + 1)) if causal else l_kv
+        assert t.vis == exp_vis
+    # every item assigned, each worker's queue holds it once
+    seen = sorted(m for q in p.queues for m in q)
+    assert seen == list(range(len(p.items)))
+    # greedy property: each item went to a least-loaded worker at its turn
+    order = sorted(range(len(p.items)), key=lambda m: -p.items[m].kv_len)
+    load = [0] * C
+    for m in order:
+        w = p.items[m].worker
+        assert load[w] == min(load) and w == load.index(min(load))
+        load[w] += 2 * qol[p.items[m].req] + p.items[m].kv_len
+    assert load == p.worker_cost
+    # slots: exactly the chunks of split tiles, numbered 0.. in assignment order
+    split = [m for m in order if len(p.tiles[p.items[m].tile].items) > 1]
+    assert [p.items[m].slot for m in split] == list(range(len(split)))
+    assert p.num_slots == len(split)
+    # reduction map lists split and empty tiles in creation order, slots by kv_start
+    exp_tiles = [i for i, t in enumerate(p.tiles) if len(t.items) != 1]
+    assert p.merge_tiles == exp_tiles
+    for t_id, slots in zip(p.merge_tiles, p.merge_slots):
+        starts = [next(it.kv_start for it in p.items if it.slot == s) for s in slots]
+        assert starts == sorted(starts) and len(slots) == len(p.tiles[t_id].items)
+    # eq. 13 in packed rows: partial slots < 2 C, so partial scalars <= 2 C T_q H_kv (d+1)
+    assert p.num_slots <= 2 * C
+    d = 128
+    assert p.num_slots * p.tile_q * Hk * (d + 1) <= PL.partial_capacity_bound(C, p.tile_q, Hk, d)
+
+
+def test_empty_batch_and_zero_work():
+    p = PL.make_plan([], None, 4, 1, 8)
+    assert p.items == [] and p.tiles == [] and p.chunk_limit == 0
+    p = PL.make_plan([0, 0], None, 4, 1, 8)
+    assert p.items == [] and p.merge_tiles == [0, 1] and p.merge_slots == [[], []]
+
+
+def test_causal_long_query_short_kv_has_empty_tiles():
+    # bottom-right alignment: with 64 queries and 8 keys, the first 56 positions see nothing
+    p = PL.make_plan([8], [64], 1, 1, 4, tile_q=16, causal=True)
+    assert [t.vis for t in p.tiles] == [0, 0, 0, 8]
+    assert p.merge_tiles[:3] == [0, 1, 2]
