@@ -1,0 +1,262 @@
+"""Python binding of libbsr_attn: argument marshalling only.
+
+Every step of the attention path runs in the HIP library; this module converts
+numpy/torch arguments into the pointers and sizes of include/bsr_attn.h.  PyTorch
+supplies device memory and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+from typing import Optional
+
+import numpy as np
+
+from . import _lib
+from ._lib import check, lib
+
+
+def _i32(a):
+    a = np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+    return a, a.ctypes.data_as(_lib.i32p)
+
+
+def _stream(stream=None):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.float32:
+        return _lib.DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return _lib.DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+class Plan:
+    """Host plan: the load-balanced split-KV partition of one batch (bsr_plan_create)."""
+
+    def __init__(
+        self,
+        kv_indptr,
+        kv_indices,
+        last_page_len,
+        *,
+        num_pages: int,
+        num_qo_heads: int,
+        num_kv_heads: int,
+        head_dim: int,
+        page_size: int,
+        qo_indptr=None,
+        causal: bool = False,
+        num_workers: int = 0,
+        tile_q: int = 0,
+        alpha: int = 2,
+        beta: int = 1,
+    ):
+        kv_indptr, p_ip = _i32(kv_indptr)
+        kv_indices, p_ix = _i32(kv_indices)
+        last_page_len, p_last = _i32(last_page_len)
+        if qo_indptr is not None:
+            qo_indptr, p_qo = _i32(qo_indptr)
+        else:
+            p_qo = C.cast(None, _lib.i32p)
+        d = _lib.PlanDesc(
+            batch=len(kv_indptr) - 1,
+            qo_indptr=p_qo,
+            kv_indptr=p_ip,
+            kv_indices=p_ix,
+            last_page_len=p_last,
+            num_pages=int(num_pages),
+            num_qo_heads=int(num_qo_heads),
+            num_kv_heads=int(num_kv_heads),
+            head_dim=int(head_dim),
+            page_size=int(page_size),
+            causal=int(bool(causal)),
+            num_workers=int(num_workers),
+            tile_q=int(tile_q),
+            alpha=int(alpha),
+            beta=int(beta),
+        )
+        h = C.c_void_p()
+        check(lib().bsr_plan_create(C.byref(d), C.byref(h)))
+        self._h = h
+        self.num_qo_heads = int(num_qo_heads)
+        self.num_kv_heads = int(num_kv_heads)
+        self.head_dim = int(head_dim)
+        self.decode = qo_indptr is None
+        self.batch = len(kv_indptr) - 1
+        self.total_q = self.batch if qo_indptr is None else int(qo_indptr[-1])
+        self._ws = None
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            try:
+                lib().bsr_plan_destroy(h)
+            except Exception:
+                pass
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def workspace_bytes(self) -> int:
+        n = C.c_size_t()
+        check(lib().bsr_plan_workspace_bytes(self._h, C.byref(n)))
+        return int(n.value)
+
+    def upload(self, workspace, stream=None):
+        """Copy the plan metadata into ``workspace`` (a device uint8 tensor)."""
+        check(lib().bsr_plan_upload(self._h, C.c_void_p(workspace.data_ptr()),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+        self._ws = workspace
+        return workspace
+
+    def export(self) -> dict:
+        v = _lib.PlanView()
+        check(lib().bsr_plan_export(self._h, C.byref(v)))
+
+        def arr(ptr, n, cols=1, dt=np.int32):
+            if n == 0:
+                return np.zeros((0, cols) if cols > 1 else (0,), dtype=dt)
+            a = np.ctypeslib.as_array(ptr, shape=(n * cols,)).copy().astype(dt)
+            return a.reshape(n, cols) if cols > 1 else a
+
+        C_ = v.num_workers
+        nm = v.num_merge
+        merge_ptr = arr(v.merge_ptr, nm + 1)
+        return {
+            "batch": v.batch,
+            "group_size": v.group_size,
+            "tile_q": v.tile_q,
+            "num_workers": C_,
+            "num_slots": v.num_slots,
+            "total_work": v.total_work,
+            "chunk_limit": v.chunk_limit,
+            "tiles": arr(v.tiles, v.num_tiles, 5),
+            "items": arr(v.items, v.num_items, 8),
+            "queue_ptr": arr(v.queue_ptr, C_ + 1),
+            "queue_items": arr(v.queue_items, v.num_items),
+            "worker_cost": arr(v.worker_cost, C_, dt=np.int64),
+            "merge_tiles": arr(v.merge_tiles, nm),
+            "merge_ptr": merge_ptr,
+            "merge_slots": arr(v.merge_slots, int(merge_ptr[-1]) if nm else 0),
+        }
+
+
+def plan(*args, **kw) -> Plan:
+    return Plan(*args, **kw)
+
+
+def alloc_workspace(p: Plan, device="cuda"):
+    import torch
+
+    return torch.empty(max(p.workspace_bytes(), 256), dtype=torch.uint8, device=device)
+
+
+def _run(fn, p: Plan, ws, q, k_cache, v_cache, o, lse, sm_scale, stream):
+    import torch
+
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(p.head_dim)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[0], p.num_qo_heads, dtype=torch.float32, device=q.device)
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("o", o), ("lse", lse)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype == o.dtype) or lse.dtype != torch.float32:
+        raise TypeError("q/k/v/o must share one dtype and lse must be float32")
+    if tuple(q.shape) != (p.total_q, p.num_qo_heads, p.head_dim) or q.shape != o.shape:
+        raise ValueError(f"q/o shape {tuple(q.shape)} != {(p.total_q, p.num_qo_heads, p.head_dim)}")
+    if k_cache.shape[-2:] != (p.num_kv_heads, p.head_dim) or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache/v_cache must be [num_pages, page_size, num_kv_heads, head_dim]")
+    check(
+        fn(
+            p.handle,
+            C.c_void_p(ws.data_ptr()),
+            C.c_void_p(q.data_ptr()),
+            C.c_void_p(k_cache.data_ptr()),
+            C.c_void_p(v_cache.data_ptr()),
+            C.c_void_p(o.data_ptr()),
+            C.cast(C.c_void_p(lse.data_ptr()), C.POINTER(C.c_float)),
+            _dtype_code(q),
+            float(sm_scale),
+            _stream(stream),
+        )
+    )
+    return o, lse
+
+
+def run_decode(p: Plan, ws, q, k_cache, v_cache, o=None, lse=None, sm_scale=None, stream=None):
+    """bsr_run_decode: one query per request; returns (O, LSE)."""
+    return _run(lib().bsr_run_decode, p, ws, q, k_cache, v_cache, o, lse, sm_scale, stream)
+
+
+def run_prefill(p: Plan, ws, q, k_cache, v_cache, o=None, lse=None, sm_scale=None, stream=None):
+    """bsr_run_prefill: ragged (causal per plan) queries; returns (O, LSE)."""
+    return _run(lib().bsr_run_prefill, p, ws, q, k_cache, v_cache, o, lse, sm_scale, stream)
+
+
+def merge_state(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, stream=None):
+    """bsr_merge_state: (O_a, LSE_a) (+) (O_b, LSE_b) for [rows, heads, d] states."""
+    import torch
+
+    if o_out is None:
+        o_out = torch.empty_like(o_a)
+    if lse_out is None:
+        lse_out = torch.empty_like(lse_a)
+    rows, heads, d = o_a.shape
+    for t in (o_a, lse_a, o_b, lse_b, o_out, lse_out):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("merge_state arguments must be contiguous device tensors")
+    if o_b.shape != o_a.shape or o_out.shape != o_a.shape or lse_a.shape != (rows, heads):
+        raise ValueError("merge_state shape mismatch")
+    fp = C.POINTER(C.c_float)
+    check(
+        lib().bsr_merge_state(
+            C.c_void_p(o_a.data_ptr()), C.cast(C.c_void_p(lse_a.data_ptr()), fp),
+            C.c_void_p(o_b.data_ptr()), C.cast(C.c_void_p(lse_b.data_ptr()), fp),
+            C.c_void_p(o_out.data_ptr()), C.cast(C.c_void_p(lse_out.data_ptr()), fp),
+            rows, heads, d, _dtype_code(o_a), _stream(stream),
+        )
+    )
+    return o_out, lse_out
+
+
+def debug_gather_rows(p: Plan, ws, total_tokens: int, stream=None):
+    """bsr_debug_gather_rows: int64 physical row of every logical token."""
+    import torch
+
+    rows = torch.full((max(total_tokens, 1),), -1, dtype=torch.int64, device=ws.device)
+    check(lib().bsr_debug_gather_rows(p.handle, C.c_void_p(ws.data_ptr()), C.c_void_p(rows.data_ptr()), _stream(stream)))
+    return rows[:total_tokens]
+
+
+def query_num_workers(kind: str, num_qo_heads: int, num_kv_heads: int, head_dim: int, device: int = 0) -> int:
+    out = C.c_int32()
+    k = {"decode": 0, "prefill": 1}[kind]
+    check(lib().bsr_query_num_workers(device, k, num_qo_heads, num_kv_heads, head_dim, C.byref(out)))
+    return int(out.value)
+
+
+def timing_enable(on: bool = True):
+    check(lib().bsr_timing_enable(1 if on else 0))
+
+
+def timing_read():
+    am, an, mm, mn = C.c_double(), C.c_int64(), C.c_double(), C.c_int64()
+    check(lib().bsr_timing_read(C.byref(am), C.byref(an), C.byref(mm), C.byref(mn)))
+    return {"attn_ms": am.value, "attn_launches": an.value, "merge_ms": mm.value, "merge_launches": mn.value}
+
+
+def version() -> str:
+    return lib().bsr_version().decode()

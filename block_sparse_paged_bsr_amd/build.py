@@ -1,0 +1,83 @@
+"""Build libbsr_attn.so in-tree with hipcc for gfx950.
+
+Usage: ``python -m block_sparse_paged_bsr_amd.build`` (or ``build()`` from Python).
+Every call recompiles every source; objects go to ``_build/`` next to this file.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+OUT = os.path.join(HERE, "libbsr_attn.so")
+BUILD = os.path.join(HERE, "_build")
+
+SOURCES = [
+    os.path.join(CSRC, "plan.cpp"),
+    os.path.join(CSRC, "api.hip"),
+    os.path.join(CSRC, "kernels", "attn_f32.hip"),
+    os.path.join(CSRC, "kernels", "attn_prefill_bf16.hip"),
+    os.path.join(CSRC, "kernels", "attn_decode_bf16.hip"),
+    os.path.join(CSRC, "kernels", "merge.hip"),
+]
+
+ARCH = os.environ.get("BSR_OFFLOAD_ARCH", "gfx950")
+
+COMMON = [
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Wno-unused-function",
+    f"-I{os.path.join(ROOT, 'include')}",
+]
+# Packed fp32 (v_pk_*_f32) code generation is switched off for every HIP source.
+HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _hipcc():
+    for c in ("/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def _compile(src):
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [_hipcc()] + COMMON
+    if src.endswith(".hip"):
+        cmd += HIP_FLAGS + ["-x", "hip"]
+    cmd += ["-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature: harmless
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(ln for ln in r.stderr.splitlines() if noise not in ln)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{err}")
+    if err.strip():
+        sys.stderr.write(err + "\n")
+    return obj
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = OUT + ".tmp"
+    cmd = [_hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
+    os.replace(tmp, OUT)
+    if verbose:
+        print(f"built {OUT}")
+    return OUT
+
+
+if __name__ == "__main__":
+    build()

@@ -1,0 +1,365 @@
+// C ABI of libbsr_attn (include/bsr_attn.h): validation, workspace upload, kernel
+// dispatch and optional per-kernel event timing.  No call aborts or throws across the
+// ABI; every error returns a bsr_status and leaves a message in bsr_last_error().
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <sstream>
+#include <string>
+#include <vector>
+
+#include "bsr_internal.h"
+#include "kernels/launch.h"
+
+namespace bsr {
+
+static thread_local std::string g_error;
+void set_error(const std::string& msg) { g_error = msg; }
+
+namespace {
+
+int hip_fail(const char* what, hipError_t e) {
+  std::ostringstream os;
+  os << what << ": " << hipGetErrorName(e) << " (" << hipGetErrorString(e) << ")";
+  set_error(os.str());
+  return BSR_HIP_ERROR;
+}
+
+int invalid(const std::string& m) {
+  set_error(m);
+  return BSR_INVALID_ARG;
+}
+
+int unsupported(const std::string& m) {
+  set_error(m);
+  return BSR_UNSUPPORTED;
+}
+
+// ---- optional per-kernel timing ----
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  struct Pair {
+    hipEvent_t start, stop;
+    int kind;  // 0 attention, 1 merge
+  };
+  std::vector<Pair> pending;
+  double ms[2] = {0.0, 0.0};
+  int64_t count[2] = {0, 0};
+};
+Timing g_timing;
+
+bool timing_on() {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  return g_timing.on;
+}
+
+// Records a start event; returns it (or nullptr when timing is off / on failure).
+hipEvent_t timing_start(hipStream_t s) {
+  if (!timing_on()) return nullptr;
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventRecord(e, s) != hipSuccess) {
+    (void)hipEventDestroy(e);
+    return nullptr;
+  }
+  return e;
+}
+
+void timing_stop(hipEvent_t start, hipStream_t s, int kind) {
+  if (!start) return;
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess || hipEventRecord(e, s) != hipSuccess) {
+    if (e) (void)hipEventDestroy(e);
+    (void)hipEventDestroy(start);
+    return;
+  }
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.pending.push_back({start, e, kind});
+}
+
+int p_shift_of(int P) {
+  if (P <= 0 || (P & (P - 1))) return -1;
+  int s = 0;
+  while ((1 << s) < P) ++s;
+  return s;
+}
+
+RunArgs make_args(const bsr_plan* p, const void* ws) {
+  const char* base = static_cast<const char*>(ws);
+  RunArgs a{};
+  a.req = reinterpret_cast<const ReqRec*>(base + p->ws.req);
+  a.indices = reinterpret_cast<const int32_t*>(base + p->ws.indices);
+  a.items = reinterpret_cast<const ItemRec*>(base + p->ws.items);
+  a.qptr = reinterpret_cast<const int32_t*>(base + p->ws.qptr);
+  a.merge = reinterpret_cast<const MergeRec*>(base + p->ws.merge);
+  a.mslots = reinterpret_cast<const int32_t*>(base + p->ws.mslots);
+  a.part_o = reinterpret_cast<float*>(const_cast<char*>(base) + p->ws.part_o);
+  a.part_lse = reinterpret_cast<float*>(const_cast<char*>(base) + p->ws.part_lse);
+  a.B = p->B;
+  a.Hq = p->Hq;
+  a.Hk = p->Hk;
+  a.g = p->g;
+  a.d = p->d;
+  a.P = p->P;
+  a.Tq = p->Tq;
+  a.C = p->C;
+  a.causal = p->causal;
+  a.num_merge = int32_t(p->merge_tiles.size());
+  a.p_shift = p_shift_of(p->P);
+  return a;
+}
+
+int run_common(const bsr_plan* p, const void* ws, const void* q, const void* k, const void* v,
+               void* o, float* lse, int32_t dtype, float sm_scale, void* stream, bool decode_call) {
+  if (!p) return invalid("plan is NULL");
+  if (!ws) return invalid("workspace is NULL");
+  if (ws != p->uploaded_ws) return invalid("workspace was not uploaded for this plan (call bsr_plan_upload first)");
+  if (dtype != BSR_DTYPE_F32 && dtype != BSR_DTYPE_BF16) return invalid("unknown dtype");
+  if (decode_call && !p->decode)
+    return invalid("bsr_run_decode needs a plan with one query per request (qo_indptr == NULL); use bsr_run_prefill");
+  if (!(sm_scale == sm_scale)) return invalid("sm_scale is NaN");
+  if (p->B == 0) return BSR_OK;
+  if (!q || !k || !v || !o || !lse) return invalid("q, k_cache, v_cache, o and lse must be non-NULL");
+  const bool any_tokens = p->total_kv_tokens > 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RunArgs a = make_args(p, ws);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.sm_scale = sm_scale;
+
+  hipError_t e = hipSuccess;
+  if (!p->items.empty()) {
+    hipEvent_t t0 = timing_start(s);
+    if (dtype == BSR_DTYPE_F32) {
+      if (!attn_f32_supported(p->d)) return unsupported("fp32 head_dim must be one of 16, 32, 64, 128, 256");
+      e = launch_attn_f32(a, s);
+    } else {
+      const bool dec_ok = p->decode && decode_bf16_supported(p->d, p->g, p->Tq);
+      if (dec_ok) {
+        e = launch_decode_bf16(a, s);
+      } else {
+        if (!prefill_bf16_supported(p->d, p->Tq)) return unsupported("bf16 head_dim must be 64 or 128");
+        e = launch_prefill_bf16(a, s);
+      }
+    }
+    timing_stop(t0, s, 0);
+    if (e != hipSuccess) return hip_fail("attention kernel launch", e);
+  } else if (dtype == BSR_DTYPE_BF16 && !prefill_bf16_supported(p->d, p->Tq)) {
+    return unsupported("bf16 head_dim must be 64 or 128");
+  } else if (dtype == BSR_DTYPE_F32 && !attn_f32_supported(p->d)) {
+    return unsupported("fp32 head_dim must be one of 16, 32, 64, 128, 256");
+  }
+  (void)any_tokens;
+  if (a.num_merge > 0) {
+    hipEvent_t t1 = timing_start(s);
+    e = launch_merge(a, dtype, s);
+    timing_stop(t1, s, 1);
+    if (e != hipSuccess) return hip_fail("merge kernel launch", e);
+  }
+  return BSR_OK;
+}
+
+}  // namespace
+}  // namespace bsr
+
+using namespace bsr;
+
+extern "C" {
+
+const char* bsr_last_error(void) { return g_error.c_str(); }
+
+const char* bsr_version(void) { return "bsr_attn 0.1.0 (gfx950)"; }
+
+int bsr_plan_create(const bsr_plan_desc* desc, bsr_plan** out) {
+  if (!out) return invalid("out is NULL");
+  *out = nullptr;
+  bsr_plan* p = new (std::nothrow) bsr_plan();
+  if (!p) return invalid("out of host memory");
+  int rc;
+  try {
+    rc = build_plan(desc, p);
+  } catch (const std::bad_alloc&) {
+    set_error("out of host memory while planning");
+    rc = BSR_INVALID_ARG;
+  }
+  if (rc != BSR_OK) {
+    delete p;
+    return rc;
+  }
+  *out = p;
+  return BSR_OK;
+}
+
+void bsr_plan_destroy(bsr_plan* p) {
+  if (!p) return;
+  if (p->upload_event) {
+    (void)hipEventSynchronize(static_cast<hipEvent_t>(p->upload_event));
+    (void)hipEventDestroy(static_cast<hipEvent_t>(p->upload_event));
+  }
+  if (p->pinned) (void)hipHostFree(p->pinned);
+  delete p;
+}
+
+int bsr_plan_workspace_bytes(const bsr_plan* p, size_t* bytes) {
+  if (!p || !bytes) return invalid("plan and bytes must be non-NULL");
+  *bytes = p->ws.total;
+  return BSR_OK;
+}
+
+int bsr_plan_upload(bsr_plan* p, void* dev_ws, size_t ws_bytes, void* stream) {
+  if (!p || !dev_ws) return invalid("plan and dev_ws must be non-NULL");
+  if (ws_bytes < p->ws.total) {
+    std::ostringstream os;
+    os << "workspace has " << ws_bytes << " bytes, the plan needs " << p->ws.total;
+    set_error(os.str());
+    return BSR_CAPACITY;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (!p->pinned) {
+    e = hipHostMalloc(&p->pinned, p->meta.size(), hipHostMallocDefault);
+    if (e != hipSuccess) {
+      p->pinned = nullptr;
+      return hip_fail("hipHostMalloc(plan staging)", e);
+    }
+    std::memcpy(p->pinned, p->meta.data(), p->meta.size());
+  }
+  if (!p->upload_event) {
+    hipEvent_t ev;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail("hipEventCreate", e);
+    p->upload_event = ev;
+  }
+  e = hipMemcpyAsync(dev_ws, p->pinned, p->meta.size(), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail("hipMemcpyAsync(plan upload)", e);
+  e = hipEventRecord(static_cast<hipEvent_t>(p->upload_event), s);
+  if (e != hipSuccess) return hip_fail("hipEventRecord", e);
+  p->uploaded_ws = dev_ws;
+  return BSR_OK;
+}
+
+int bsr_plan_export(const bsr_plan* p, bsr_plan_view* v) {
+  if (!p || !v) return invalid("plan and view must be non-NULL");
+  v->batch = p->B;
+  v->num_qo_heads = p->Hq;
+  v->num_kv_heads = p->Hk;
+  v->head_dim = p->d;
+  v->page_size = p->P;
+  v->causal = p->causal;
+  v->group_size = p->g;
+  v->tile_q = p->Tq;
+  v->num_workers = p->C;
+  v->num_slots = p->num_slots;
+  v->total_work = p->W;
+  v->chunk_limit = p->L;
+  v->num_tiles = int32_t(p->tiles.size() / 5);
+  v->tiles = p->tiles.data();
+  v->num_items = int32_t(p->items.size() / 8);
+  v->items = p->items.data();
+  v->queue_ptr = p->queue_ptr.data();
+  v->queue_items = p->queue_items.data();
+  v->worker_cost = p->worker_cost.data();
+  v->num_merge = int32_t(p->merge_tiles.size());
+  v->merge_tiles = p->merge_tiles.data();
+  v->merge_ptr = p->merge_ptr.data();
+  v->merge_slots = p->merge_slots.data();
+  return BSR_OK;
+}
+
+int bsr_run_decode(const bsr_plan* plan, const void* ws, const void* q, const void* k_cache,
+                   const void* v_cache, void* o, float* lse, int32_t dtype, float sm_scale,
+                   void* stream) {
+  return run_common(plan, ws, q, k_cache, v_cache, o, lse, dtype, sm_scale, stream, true);
+}
+
+int bsr_run_prefill(const bsr_plan* plan, const void* ws, const void* q, const void* k_cache,
+                    const void* v_cache, void* o, float* lse, int32_t dtype, float sm_scale,
+                    void* stream) {
+  return run_common(plan, ws, q, k_cache, v_cache, o, lse, dtype, sm_scale, stream, false);
+}
+
+int bsr_merge_state(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                    void* o_out, float* lse_out, int64_t rows, int32_t heads, int32_t head_dim,
+                    int32_t dtype, void* stream) {
+  if (rows < 0 || heads < 0 || head_dim < 1) return invalid("rows, heads must be >= 0 and head_dim >= 1");
+  if (dtype != BSR_DTYPE_F32 && dtype != BSR_DTYPE_BF16) return invalid("unknown dtype");
+  if (rows * int64_t(heads) > (int64_t(1) << 31) / 16) return invalid("too many states");
+  if (rows * heads == 0) return BSR_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o_out || !lse_out) return invalid("NULL state pointer");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_merge_state(o_a, lse_a, o_b, lse_b, o_out, lse_out, rows, heads, head_dim, dtype, s);
+  if (e != hipSuccess) return hip_fail("merge_state launch", e);
+  return BSR_OK;
+}
+
+int bsr_debug_gather_rows(const bsr_plan* p, const void* ws, int64_t* rows_dev, void* stream) {
+  if (!p || !ws) return invalid("plan and ws must be non-NULL");
+  if (ws != p->uploaded_ws) return invalid("workspace was not uploaded for this plan");
+  if (p->total_kv_tokens == 0) return BSR_OK;
+  if (!rows_dev) return invalid("rows_dev is NULL");
+  RunArgs a = make_args(p, ws);
+  hipError_t e = launch_gather_rows(a, rows_dev, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("gather_rows launch", e);
+  return BSR_OK;
+}
+
+int bsr_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (auto& pr : g_timing.pending) {
+    (void)hipEventDestroy(pr.start);
+    (void)hipEventDestroy(pr.stop);
+  }
+  g_timing.pending.clear();
+  g_timing.ms[0] = g_timing.ms[1] = 0.0;
+  g_timing.count[0] = g_timing.count[1] = 0;
+  g_timing.on = on != 0;
+  return BSR_OK;
+}
+
+int bsr_timing_read(double* attn_ms, int64_t* attn_launches, double* merge_ms, int64_t* merge_launches) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (auto& pr : g_timing.pending) {
+    hipError_t e = hipEventSynchronize(pr.stop);
+    if (e != hipSuccess) return hip_fail("hipEventSynchronize", e);
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, pr.start, pr.stop);
+    if (e != hipSuccess) return hip_fail("hipEventElapsedTime", e);
+    g_timing.ms[pr.kind] += ms;
+    g_timing.count[pr.kind] += 1;
+    (void)hipEventDestroy(pr.start);
+    (void)hipEventDestroy(pr.stop);
+  }
+  g_timing.pending.clear();
+  if (attn_ms) *attn_ms = g_timing.ms[0];
+  if (attn_launches) *attn_launches = g_timing.count[0];
+  if (merge_ms) *merge_ms = g_timing.ms[1];
+  if (merge_launches) *merge_launches = g_timing.count[1];
+  return BSR_OK;
+}
+
+int bsr_query_num_workers(int32_t device, int32_t kind, int32_t num_qo_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t* out) {
+  if (!out || num_kv_heads < 1 || num_qo_heads < 1 || num_qo_heads % num_kv_heads)
+    return invalid("bad arguments to bsr_query_num_workers");
+  int cus = 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return hip_fail("hipDeviceGetAttribute", e);
+  const int g = num_qo_heads / num_kv_heads;
+  int per_cu = 1, per_worker = num_kv_heads;
+  if (kind == 0 && decode_bf16_supported(head_dim, g, 128)) {
+    per_cu = decode_bf16_blocks_per_cu(head_dim, g);
+    per_worker = num_kv_heads * decode_bf16_waves_per_kv_head(g);
+  } else if (head_dim == 64 || head_dim == 128) {
+    per_cu = prefill_bf16_blocks_per_cu(head_dim);
+  }
+  *out = std::max(1, cus * per_cu / per_worker);
+  return BSR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Internal declarations shared by the host planner, the C-ABI layer and the kernels.
+// Nothing here is part of the public ABI (include/bsr_attn.h).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/bsr_attn.h"
+
+namespace bsr {
+
+// ---- device metadata records (int32, written by the planner, read by kernels) ----
+
+// Per request: where its queries and pages live.
+struct ReqRec {
+  int32_t q_start;     // first query row in Q/O
+  int32_t q_len;       // l_qo
+  int32_t page_start;  // kv_indptr[i]
+  int32_t kv_len;      // l_kv
+  int32_t tok_start;   // prefix sum of l_kv (debug gather output offset)
+  int32_t pad[3];
+};
+static_assert(sizeof(ReqRec) == 32, "ReqRec layout");
+
+// Per work item, stored in queue order (worker w runs items [qptr[w], qptr[w+1])).
+struct ItemRec {
+  int32_t req;
+  int32_t row_start;  // packed GQA rows [row_start, row_end) of the request
+  int32_t row_end;
+  int32_t kv_start;   // logical tokens [kv_start, kv_end) of the request
+  int32_t kv_end;
+  int32_t slot;       // partial slot, or -1: write the final output
+  int32_t tile;
+  int32_t pad;
+};
+static_assert(sizeof(ItemRec) == 32, "ItemRec layout");
+
+// Per tile written by the merge pass (split tiles and empty tiles).
+struct MergeRec {
+  int32_t req;
+  int32_t row_start;
+  int32_t row_end;
+  int32_t slot_begin;  // into the merge slot list
+  int32_t slot_count;  // 0 => empty state
+  int32_t pad[3];
+};
+static_assert(sizeof(MergeRec) == 32, "MergeRec layout");
+
+// Byte offsets of the workspace sections (all 256-byte aligned).
+struct WsLayout {
+  size_t req = 0, indices = 0, items = 0, qptr = 0, merge = 0, mslots = 0;
+  size_t meta_bytes = 0;  // end of metadata
+  size_t part_o = 0, part_lse = 0;
+  size_t total = 0;
+};
+
+}  // namespace bsr
+
+struct bsr_plan {
+  // description
+  int32_t B = 0, Hq = 0, Hk = 0, d = 0, P = 1, causal = 0, C = 1, g = 1, Tq = 16;
+  int32_t alpha = 2, beta = 1, num_pages = 0;
+  bool decode = true;  // qo_indptr == NULL
+  std::vector<int32_t> qo_indptr, kv_indptr, kv_indices, last_page_len;
+  std::vector<int32_t> qo_len, kv_len;
+  int32_t max_qo_len = 0;
+  int64_t total_kv_tokens = 0;
+  // partition
+  int64_t W = 0, L = 0;
+  std::vector<int32_t> tiles;        // [num_tiles][5]
+  std::vector<int32_t> items;        // [num_items][8], creation order
+  std::vector<int32_t> queue_ptr;    // [C+1]
+  std::vector<int32_t> queue_items;  // [num_items]
+  std::vector<int64_t> worker_cost;  // [C]
+  std::vector<int32_t> merge_tiles, merge_ptr, merge_slots;
+  int32_t num_slots = 0;
+  // device image
+  bsr::WsLayout ws;
+  std::vector<uint8_t> meta;  // host copy of the metadata region (ws.meta_bytes)
+  void* pinned = nullptr;     // pinned staging (allocated at first upload)
+  void* upload_event = nullptr;
+  const void* uploaded_ws = nullptr;
+};
+
+namespace bsr {
+// host planner (plan.cpp); returns BSR_OK or an error with the message set
+int build_plan(const bsr_plan_desc* desc, bsr_plan* p);
+void set_error(const std::string& msg);
+}  // namespace bsr

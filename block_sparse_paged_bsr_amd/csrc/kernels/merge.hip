@@ -1,0 +1,137 @@
+// Attention-state merge kernels and the debug row gather.
+//
+// The merge is the reduction operator of attention states, (O, LSE) (+) (O, LSE):
+// eq. 5-6 and Algorithm 1 of "FlashInfer: Making Attention Fit the Serving
+// Workload" (§3.1-3.3), "FlashInfer 原理" §④.  The partial -> final reduction map of
+// the plan ("FlashInfer: Engineering a Customizable, Block-Sparse Attention Engine
+// for LLM Inference Serving" §VIII.5) lists, for every split query tile, its partial
+// slots in KV order; each output element folds them in that fixed order with a
+// shared maximum, so the result does not depend on which worker finished first
+// (§VIII.3: no atomics).  Folding k states with one shared maximum m gives the same
+// value as the left fold of pairwise merges in exact arithmetic: both equal
+// sum_s e^(lse_s - m) O_s / sum_s e^(lse_s - m).
+#include "common.cuh"
+#include "launch.h"
+
+namespace bsr {
+
+namespace {
+
+template <typename T>
+__device__ __forceinline__ void store_out(T* p, float v);
+template <>
+__device__ __forceinline__ void store_out<float>(float* p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float v) { *p = uint16_t(f2bf_bits(v)); }
+
+template <typename T>
+__device__ __forceinline__ float load_in(const T* p);
+template <>
+__device__ __forceinline__ float load_in<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float load_in<uint16_t>(const uint16_t* p) { return __uint_as_float(uint32_t(*p) << 16); }
+
+}  // namespace
+
+// One workgroup per (merge tile, KV head); threads cover (row, d) elements.
+template <typename OutT>
+__global__ __launch_bounds__(256) void merge_partials_kernel(RunArgs a) {
+  const int mt = blockIdx.x, hk = blockIdx.y;
+  const MergeRec mr = a.merge[mt];
+  const ReqRec rq = a.req[mr.req];
+  const int nrows = mr.row_end - mr.row_start;
+  const int D = a.d;
+  OutT* O = static_cast<OutT*>(a.o);
+  for (int idx = threadIdx.x; idx < nrows * D; idx += blockDim.x) {
+    const int lr = idx / D, e = idx - lr * D;
+    const int row = mr.row_start + lr;
+    const int pos = row / a.g, hq = hk * a.g + row % a.g;
+    float mx = kNegInf;
+    for (int k = 0; k < mr.slot_count; ++k) {
+      const int s = a.mslots[mr.slot_begin + k];
+      mx = fmaxf(mx, a.part_lse[(int64_t(s) * a.Hk + hk) * a.Tq + lr]);
+    }
+    float num = 0.f, den = 0.f;
+    if (mx != kNegInf) {
+      for (int k = 0; k < mr.slot_count; ++k) {
+        const int s = a.mslots[mr.slot_begin + k];
+        const int64_t prow = (int64_t(s) * a.Hk + hk) * a.Tq + lr;
+        const float ls = a.part_lse[prow];
+        const float wgt = ls == kNegInf ? 0.f : expf(ls - mx);
+        num += wgt * a.part_o[prow * D + e];
+        den += wgt;
+      }
+    }
+    const int64_t orow = int64_t(rq.q_start + pos) * a.Hq + hq;
+    store_out<OutT>(O + orow * D + e, mx == kNegInf ? 0.f : num / den);
+    if (e == 0) a.lse[orow] = mx == kNegInf ? kNegInf : mx + logf(den);
+  }
+}
+
+// Elementwise merge of two state arrays.  A 16-lane group owns one (row, head) state,
+// reads both LSEs before any store, and so tolerates o_out/lse_out aliasing an input.
+template <typename T>
+__global__ __launch_bounds__(256) void merge_state_kernel(const T* oa, const float* la, const T* ob,
+                                                         const float* lb, T* oo, float* lo,
+                                                         int64_t nstates, int D) {
+  const int64_t st = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 4;
+  const int sub = threadIdx.x & 15;
+  if (st >= nstates) return;
+  const float a_l = la[st], b_l = lb[st];
+  const bool va = a_l != kNegInf, vb = b_l != kNegInf;
+  const float mx = fmaxf(a_l, b_l);
+  const float wa = va ? expf(a_l - mx) : 0.f;
+  const float wb = vb ? expf(b_l - mx) : 0.f;
+  const float den = wa + wb;
+  for (int e = sub; e < D; e += 16) {
+    const float xa = va ? load_in<T>(oa + st * D + e) : 0.f;
+    const float xb = vb ? load_in<T>(ob + st * D + e) : 0.f;
+    float r;
+    if (va && vb) r = (wa * xa + wb * xb) / den;
+    else if (va) r = xa;
+    else if (vb) r = xb;
+    else r = 0.f;
+    store_out<T>(oo + st * D + e, r);
+  }
+  if (sub == 0) lo[st] = (va || vb) ? mx + logf(den) : kNegInf;
+}
+
+// Physical row of every logical token, with the attention kernels' address function.
+__global__ __launch_bounds__(256) void gather_rows_kernel(RunArgs a, int64_t* rows) {
+  const ReqRec rq = a.req[blockIdx.x];
+  for (int t = threadIdx.x; t < rq.kv_len; t += blockDim.x)
+    rows[int64_t(rq.tok_start) + t] = page_row(a.indices, rq.page_start, t, a.P, a.p_shift);
+}
+
+hipError_t launch_merge(const RunArgs& a, int dtype, hipStream_t s) {
+  if (a.num_merge == 0) return hipSuccess;
+  dim3 grid(a.num_merge, a.Hk), block(256);
+  if (dtype == BSR_DTYPE_F32) hipLaunchKernelGGL(merge_partials_kernel<float>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(merge_partials_kernel<uint16_t>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_state(const void* oa, const float* la, const void* ob, const float* lb,
+                              void* oo, float* lo, int64_t rows, int heads, int d, int dtype,
+                              hipStream_t s) {
+  const int64_t nst = rows * heads;
+  if (nst == 0) return hipSuccess;
+  const int64_t blocks = (nst * 16 + 255) / 256;
+  if (dtype == BSR_DTYPE_F32)
+    hipLaunchKernelGGL(merge_state_kernel<float>, dim3(blocks), dim3(256), 0, s,
+                       static_cast<const float*>(oa), la, static_cast<const float*>(ob), lb,
+                       static_cast<float*>(oo), lo, nst, d);
+  else
+    hipLaunchKernelGGL(merge_state_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(oa), la, static_cast<const uint16_t*>(ob), lb,
+                       static_cast<uint16_t*>(oo), lo, nst, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const RunArgs& a, int64_t* rows, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(a.B), dim3(256), 0, s, a, rows);
+  return hipGetLastError();
+}
+
+}  // namespace bsr

@@ -121,6 +121,7 @@ def batch_attention(
     qo_indptr=None,
     causal=False,
     requests=None,
+    query_subset=None,
 ):
     """Attention of every (query, head) of a ragged batch over its own paged KV.
 
@@ -128,6 +129,9 @@ def batch_attention(
     dtype, upcast exactly to float64).  ``qo_indptr`` None means one query per
     request (decode).  Returns O [total_q, H_qo, d] and LSE [total_q, H_qo] in
     float64; only rows of ``requests`` (default all) are filled, the rest stay NaN.
+    ``query_subset`` maps a request to the query positions (0-based within the
+    request) to evaluate; each query row is independent of the others, so a subset
+    is the same definition on fewer rows.
     """
     assert num_qo_heads % num_kv_heads == 0
     g = num_qo_heads // num_kv_heads
@@ -147,16 +151,19 @@ def batch_attention(
         rows = physical_rows(kv_indptr, kv_indices, last_page_len, page_size, i)
         q0, q1 = int(qo_indptr[i]), int(qo_indptr[i + 1])
         l_qo, l_kv = q1 - q0, len(rows)
-        allowed = causal_allowed(l_qo, l_kv) if causal else None
+        sel = np.arange(l_qo)
+        if query_subset is not None and i in query_subset:
+            sel = np.asarray(query_subset[i], dtype=np.int64)
+        allowed = causal_allowed(l_qo, l_kv)[sel] if causal else None
         K_i = k_flat[rows].astype(np.float64)  # [l_kv, H_kv, d]
         V_i = v_flat[rows].astype(np.float64)
         for h in range(num_qo_heads):
             hk = h // g
             o, s = attention_one_head(
-                q[q0:q1, h].astype(np.float64), K_i[:, hk], V_i[:, hk], sm_scale, allowed
+                q[q0 + sel, h].astype(np.float64), K_i[:, hk], V_i[:, hk], sm_scale, allowed
             )
-            O[q0:q1, h] = o
-            lse[q0:q1, h] = s
+            O[q0 + sel, h] = o
+            lse[q0 + sel, h] = s
     return O, lse
 
 

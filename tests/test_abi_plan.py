@@ -1,0 +1,180 @@
+"""C-ABI checks that need no GPU: exports, host planner parity with the oracle, errors.
+
+bsr_plan_create/export/destroy/workspace_bytes are pure host code, so they run here.
+"""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from block_sparse_paged_bsr_amd import _lib
+from block_sparse_paged_bsr_amd import api
+from block_sparse_paged_bsr_amd import inputs as I
+from oracle import plan as PL
+from tests.conftest import ROOT, load_golden
+
+HEADER = os.path.join(ROOT, "include", "bsr_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libbsr_attn.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|void|const char\*)\s+(bsr_\w+)\s*\(", src, re.M)))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert len(names) >= 14
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\b(bsr_\w+)\b", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert sorted(_lib.EXPORTED) == names
+    L = _lib.lib()
+    for n in names:
+        assert hasattr(L, n)
+    assert "gfx950" in api.version()
+
+
+def _oracle_as_export(p):
+    tiles = np.array([[t.req, t.row_start, t.row_end, t.vis, len(t.items)] for t in p.tiles], dtype=np.int32).reshape(-1, 5)
+    items = np.array([[it.req, it.tile, it.row_start, it.row_end, it.kv_start, it.kv_len, it.worker, it.slot]
+                      for it in p.items], dtype=np.int32).reshape(-1, 8)
+    qptr = np.concatenate([[0], np.cumsum([len(q) for q in p.queues])]).astype(np.int32)
+    qitems = np.array([m for q in p.queues for m in q], dtype=np.int32)
+    mptr = np.concatenate([[0], np.cumsum([len(s) for s in p.merge_slots])]).astype(np.int32)
+    mslots = np.array([s for ss in p.merge_slots for s in ss], dtype=np.int32)
+    return {
+        "tile_q": p.tile_q, "total_work": p.total_work, "chunk_limit": p.chunk_limit,
+        "num_slots": p.num_slots, "group_size": p.group_size, "tiles": tiles, "items": items,
+        "queue_ptr": qptr, "queue_items": qitems, "worker_cost": np.array(p.worker_cost, dtype=np.int64),
+        "merge_tiles": np.array(p.merge_tiles, dtype=np.int32), "merge_ptr": mptr, "merge_slots": mslots,
+    }
+
+
+def _assert_same(lib_plan, oracle_plan):
+    a = lib_plan.export()
+    b = _oracle_as_export(oracle_plan)
+    for k, v in b.items():
+        if isinstance(v, np.ndarray):
+            assert np.array_equal(a[k].reshape(v.shape), v), k
+        else:
+            assert a[k] == v, k
+
+
+def _lib_plan(kv_lens, qo_lens, Hq, Hk, C_, P=16, tq=0, causal=False, alpha=2, beta=1, d=128):
+    kv_lens = np.asarray(kv_lens, dtype=np.int64)
+    ip, ix, last = I.page_table_from_lengths(kv_lens, P, np.arange(int(((kv_lens + P - 1) // P).sum())))
+    qo = None if qo_lens is None else np.concatenate([[0], np.cumsum(qo_lens)])
+    return api.Plan(ip, ix, last, num_pages=max(len(ix), 1), num_qo_heads=Hq, num_kv_heads=Hk,
+                    head_dim=d, page_size=P, qo_indptr=qo, causal=causal, num_workers=C_,
+                    tile_q=tq, alpha=alpha, beta=beta)
+
+
+@pytest.mark.parametrize("alpha,beta", [(0, 1), (2, 1)])
+def test_lpt_example_bit_exact(alpha, beta):
+    g = load_golden("lpt_example.json")
+    lp = _lib_plan(g["kv_lens"], None, 1, 1, g["num_ctas"], P=1, alpha=alpha, beta=beta)
+    op = PL.make_plan(g["kv_lens"], None, 1, 1, g["num_ctas"], alpha=alpha, beta=beta)
+    _assert_same(lp, op)
+    assert lp.export()["chunk_limit"] == g["expected_chunk_limit"]
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_random_plans_bit_exact(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(0, 14))
+    kv = rng.integers(0, 5000, size=B)
+    kv[rng.random(B) < 0.15] = 0
+    qo = None if rng.random() < 0.4 else rng.integers(1, 400, size=B)
+    Hk = int(rng.choice([1, 2, 8]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    C_ = int(rng.integers(1, 300))
+    tq = int(rng.choice([0, 0, 16, 32, 128]))
+    causal = bool(rng.random() < 0.5) and qo is not None
+    alpha, beta = [(2, 1), (0, 1), (3, 2)][int(rng.integers(0, 3))]
+    P = int(rng.choice([1, 4, 16]))
+    lp = _lib_plan(kv, qo, Hk * g, Hk, C_, P=P, tq=tq, causal=causal, alpha=alpha, beta=beta)
+    op = PL.make_plan(kv, qo, Hk * g, Hk, C_, tile_q=tq, causal=causal, alpha=alpha, beta=beta)
+    _assert_same(lp, op)
+
+
+def test_workload_plans_bit_exact():
+    lens = I.decode_lengths(0)
+    lp = _lib_plan(lens, None, 32, 8, 256)
+    op = PL.make_plan(lens, None, 32, 8, 256)
+    _assert_same(lp, op)
+    pl = np.random.default_rng(0).integers(256, 4096, size=16, endpoint=True)
+    lp = _lib_plan(pl, pl, 32, 8, 64, causal=True)
+    op = PL.make_plan(pl, pl, 32, 8, 64, causal=True)
+    _assert_same(lp, op)
+
+
+def test_workspace_bound_eq13():
+    lens = I.decode_lengths(1)
+    for C_ in (16, 100, 256, 1000):
+        p = _lib_plan(lens, None, 32, 8, C_)
+        e = p.export()
+        assert e["num_slots"] < 2 * C_
+        part = e["num_slots"] * e["tile_q"] * 8 * (128 + 1)
+        assert part <= PL.partial_capacity_bound(C_, e["tile_q"], 8, 128)
+        assert p.workspace_bytes() >= part * 4
+
+
+def _desc_errors():
+    good = dict(kv_indptr=[0, 2, 3], kv_indices=[0, 1, 2], last_page_len=[4, 1], num_pages=3,
+                num_qo_heads=4, num_kv_heads=2, head_dim=128, page_size=4)
+    cases = [
+        dict(kv_indptr=[1, 2, 3]),
+        dict(kv_indptr=[0, 3, 2]),
+        dict(kv_indices=[0, 1, 3]),
+        dict(kv_indices=[0, -1, 2]),
+        dict(last_page_len=[5, 1]),
+        dict(last_page_len=[0, 1]),
+        dict(num_qo_heads=3),
+        dict(page_size=0),
+        dict(head_dim=0),
+        dict(tile_q=24),
+        dict(qo_indptr=[0, 2, 1]),
+        dict(qo_indptr=[1, 2, 3]),
+    ]
+    return good, cases
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_invalid_descriptions(i):
+    good, cases = _desc_errors()
+    kw = dict(good)
+    kw.update(cases[i])
+    ip, ix, last = kw.pop("kv_indptr"), kw.pop("kv_indices"), kw.pop("last_page_len")
+    with pytest.raises(_lib.BsrError) as ei:
+        api.Plan(ip, ix, last, **kw)
+    assert ei.value.status == _lib.BSR_INVALID_ARG
+    assert _lib.lib().bsr_last_error().decode()
+
+
+def test_empty_request_must_have_zero_last():
+    with pytest.raises(_lib.BsrError):
+        api.Plan([0, 0], [], [1], num_pages=1, num_qo_heads=1, num_kv_heads=1, head_dim=128, page_size=4)
+    p = api.Plan([0, 0], [], [0], num_pages=1, num_qo_heads=1, num_kv_heads=1, head_dim=128, page_size=4)
+    e = p.export()
+    assert e["items"].shape[0] == 0 and e["merge_tiles"].tolist() == [0]
+
+
+def test_null_arguments_rejected_without_gpu():
+    L = _lib.lib()
+    assert L.bsr_plan_create(None, C.byref(C.c_void_p())) == _lib.BSR_INVALID_ARG
+    n = C.c_size_t()
+    assert L.bsr_plan_workspace_bytes(None, C.byref(n)) == _lib.BSR_INVALID_ARG
+    p = _lib_plan([10], None, 4, 1, 4)
+    # run calls before any upload are rejected on the host, before touching the GPU
+    rc = L.bsr_run_decode(p.handle, C.c_void_p(1234), None, None, None, None, None, 1, 0.1, None)
+    assert rc == _lib.BSR_INVALID_ARG
+    assert "uploaded" in L.bsr_last_error().decode()
+    assert L.bsr_debug_gather_rows(p.handle, None, None, None) == _lib.BSR_INVALID_ARG
+    assert L.bsr_merge_state(None, None, None, None, None, None, -1, 1, 1, 1, None) == _lib.BSR_INVALID_ARG
+    assert L.bsr_merge_state(None, None, None, None, None, None, 1, 1, 1, 7, None) == _lib.BSR_INVALID_ARG
