@@ -3,216 +3,201 @@
 // Decode reads every KV byte once and does O(g) arithmetic per byte (operational
 // intensity O(g * l_qo): "FlashInfer: Engineering a Customizable, Block-Sparse
 // Attention Engine for LLM Inference Serving" §II.3-II.4; eq. 2 of "FlashInfer:
-// Making Attention Fit the Serving Workload"), so the kernel is built around HBM
-// traffic: every wave streams the KV rows of one KV head for all G query heads of its
-// group (head-group fusion, eq. 3), with one 16-byte load per lane per row chunk.
+// Making Attention Fit the Serving Workload"), so the kernel is organised around HBM
+// traffic: one wave streams the KV rows of one KV head once and serves all g <= 16
+// query heads of the group with them (head-group fusion, eq. 3 of the review).
 //
-// Layout of a 16-token step (lane = n + 16 j, n = token within the step, j = 0..3):
-//   - the lane loads K[token n][kb*32 + j*8 .. +8] and V[token n][kb*32 + j*8 .. +8]
-//     for kb = 0 .. D/32-1 (page lookup per token through the BSR indices, eq. 7);
-//   - S = Q_rep K^T on v_mfma_f32_16x16x32_bf16, where the 16 rows of Q_rep repeat the
-//     G query heads (row r -> head r mod G): the K fragment is exactly the B operand,
-//     and every lane receives the G scores of its own token n;
-//   - each lane keeps its own online-softmax partial sums (l, acc) for its token
-//     subsequence, sharing one running maximum per head across the wave (the step
-//     maximum is a 16-lane butterfly), so rescaling happens only when the maximum
-//     grows; the 16 lanes of a row are summed once at the end of the work item.
-// A work item writes the final (O, LSE) or, for a split request, a partial state that
-// the merge pass folds in the planned order.
+// A 16-token step, lane = n + 16 j (n = 0..15, j = 0..3):
+//   loads   K[token n][kb*32 + j*8 .. +8] and V[token n][kb*32 + j*8 .. +8] for
+//           kb = 0 .. D/32-1, 16 bytes each, rows found through the page table (eq. 7);
+//           the next step's rows are requested before the current step is computed.
+//   scores  S^T = K Q^T on v_mfma_f32_16x16x32_bf16: the K fragment is the A operand
+//           as loaded, Q^T (column n = query head n mod g) is the B operand; lane (n, j)
+//           receives the scores of tokens 4j..4j+3 for head n.
+//   softmax per head (one column per lane group), in log2 units, with the running
+//           maximum of the online-softmax recurrence ("FlashInfer: Engineering ...",
+//           §II.2); the accumulator is rescaled only when the maximum grows.
+//   output  O^T += V^T P^T on v_mfma_f32_16x16x16_bf16: P^T is the score accumulator
+//           converted to bf16 in place (B operand), V^T comes from the step's V rows
+//           staged in a wave-private LDS tile and read back with the transposing
+//           LDS read of gfx950 (ds_read_b64_tr_b16, A operand).
+// A work item writes the final (O, LSE) or a partial state folded by the merge pass.
 #include "common.cuh"
 #include "launch.h"
 
 namespace bsr {
 
-namespace {
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, shfl_xor(v, 1));
-  v = fmaxf(v, shfl_xor(v, 2));
-  v = fmaxf(v, shfl_xor(v, 4));
-  v = fmaxf(v, shfl_xor(v, 8));
-  return v;
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += shfl_xor(v, 1);
-  v += shfl_xor(v, 2);
-  v += shfl_xor(v, 4);
-  v += shfl_xor(v, 8);
-  return v;
-}
-}  // namespace
-
-// D: head dim; G: query heads handled by one wave (divides 4).
-template <int D, int G>
+template <int D>
 __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
-  constexpr int KB = D / 32;
-  const int w = blockIdx.x;
-  const int HW = a.g / G;  // waves per KV head
-  const int hk = blockIdx.y / HW, hw = blockIdx.y % HW;
+  constexpr int KB = D / 32;  // k-blocks of the score product
+  constexpr int DB = D / 16;  // d-blocks of the output product
+  constexpr int VS = D + 8;   // LDS row stride (elements); 16-byte aligned rows
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[16 * VS];
+
+  const int w = blockIdx.x, hk = blockIdx.y;
   const int lane = threadIdx.x, n = lane & 15, j = lane >> 4;
+  const int g = a.g;
   const float c = a.sm_scale * kLog2e;
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
   const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
   uint16_t* __restrict__ O = static_cast<uint16_t*>(a.o);
+  const int head_col = n < g ? n : n % g;  // query head offset served by column n
 
   for (int it = a.qptr[w]; it < a.qptr[w + 1]; ++it) {
     const ItemRec item = a.items[it];
     const ReqRec rq = a.req[item.req];
-    // A operand: row n of Q_rep = query head hk*g + hw*G + (n mod G)
-    const int hq_row = hk * a.g + hw * G + (n % G);
-    const uint16_t* qp = Q + (int64_t(rq.q_start) * a.Hq + hq_row) * D;
-    bf16x8 qa[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) qa[kb] = *reinterpret_cast<const bf16x8*>(qp + kb * 32 + j * 8);
+    const int kv_end = item.kv_end;
 
-    float m[G], l[G];
-    float acc[G][KB][8];
+    // Q^T as the B operand: column n = query head hk*g + head_col
+    const uint16_t* qp = Q + (int64_t(rq.q_start) * a.Hq + hk * g + head_col) * D + j * 8;
+    bf16x8 qb[KB];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      m[h] = kNegInf;
-      l[h] = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][kb][e] = 0.f;
-    }
+    for (int kb = 0; kb < KB; ++kb) qb[kb] = *reinterpret_cast<const bf16x8*>(qp + kb * 32);
 
-    for (int t0 = item.kv_start; t0 < item.kv_end; t0 += 16) {
-      const int t = t0 + n;
-      const bool valid = t < item.kv_end;
-      const int tc = valid ? t : item.kv_end - 1;
-      const int64_t base = (page_row(a.indices, rq.page_start, tc, a.P, a.p_shift) * a.Hk + hk) * D + j * 8;
-      u32x4 kr[KB], vr[KB];
+    float m = kNegInf, l = 0.f;
+    f32x4 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // page of this lane's token (lane n of a step) for the current, next and
+    // next-but-one steps: the index load runs two steps ahead of the row loads
+    const int pg_start = rq.page_start;
+    auto page_of = [&](int t) -> int32_t {
+      const int tc = min(t, kv_end - 1);
+      return a.indices[pg_start + (a.p_shift >= 0 ? (tc >> a.p_shift) : tc / a.P)];
+    };
+    auto row_base = [&](int t, int32_t page) -> int64_t {
+      const int tc = min(t, kv_end - 1);
+      const int off = a.p_shift >= 0 ? (tc & ((1 << a.p_shift) - 1)) : tc - (tc / a.P) * a.P;
+      return ((int64_t(page) * a.P + off) * a.Hk + hk) * D + j * 8;
+    };
+    int32_t pg_next = page_of(item.kv_start + 16 + n);
+    u32x4 kr[KB], vr[KB];
+    {
+      const int64_t base = row_base(item.kv_start + n, page_of(item.kv_start + n));
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         kr[kb] = *reinterpret_cast<const u32x4*>(K + base + kb * 32);
         vr[kb] = *reinterpret_cast<const u32x4*>(V + base + kb * 32);
       }
+    }
+
+    for (int t0 = item.kv_start; t0 < kv_end; t0 += 16) {
+      const bool has_next = t0 + 16 < kv_end;
+      const int32_t pg_after = page_of(t0 + 32 + n);
+      // request the next step's rows before touching this step's data
+      u32x4 kn[KB], vn[KB];
+      if (has_next) {
+        const int64_t base = row_base(t0 + 16 + n, pg_next);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          kn[kb] = *reinterpret_cast<const u32x4*>(K + base + kb * 32);
+          vn[kb] = *reinterpret_cast<const u32x4*>(V + base + kb * 32);
+        }
+      }
+      pg_next = pg_after;
+
+      // scores S^T[token 4j+i][head n]
       f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], __builtin_bit_cast(bf16x8, kr[kb]), S, 0, 0, 0);
-      // S[i] = score of query head (4j + i) mod G = i mod G for this lane's token n
-      float p[G];
+        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kb]), qb[kb], S, 0, 0, 0);
+
+      // stage V rows (token n) for the transposing read below
+      __syncthreads();
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float s = valid ? S[h] * c : kNegInf;
-        const float mt = row16_max(s);
-        if (mt > m[h]) {  // wave-uniform: every row of the wave holds the same scores
-          const float corr = exp2f(m[h] - mt);
-          l[h] *= corr;
+      for (int kb = 0; kb < KB; ++kb) *reinterpret_cast<u32x4*>(Vs + n * VS + kb * 32 + j * 8) = vr[kb];
+      __syncthreads();
+
+      float s[4];
+      float mt = kNegInf;
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][kb][e] *= corr;
-          m[h] = mt;
-        }
-        p[h] = exp2f(s - m[h]);
-        l[h] += p[h];
+      for (int i = 0; i < 4; ++i) {
+        s[i] = (t0 + 4 * j + i) < kv_end ? S[i] * c : kNegInf;
+        mt = fmaxf(mt, s[i]);
       }
+      mt = fmaxf(mt, shfl_xor(mt, 16));
+      mt = fmaxf(mt, shfl_xor(mt, 32));
+      if (mt > m) {  // the running maximum grew: rescale this head's state
+        const float corr = exp2f(m - mt);
+        l *= corr;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int db = 0; db < DB; ++db) oacc[db] *= corr;
+        m = mt;
+      }
+      float p[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v0 = bf16_lo(vr[kb][e]), v1 = bf16_hi(vr[kb][e]);
+      for (int i = 0; i < 4; ++i) {
+        p[i] = exp2f(s[i] - m);
+        l += p[i];
+      }
+      const s16x4 pb = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
+      // V^T operand: ds_read_b64_tr_b16 gives lane 16G+i the values V[token 4G+e][d0+i],
+      // e = 0..3, when lane 16G+4e+q addresses V[token 4G+e][d0+4q .. +4]
+      const uint16_t* vtr = Vs + (4 * j + ((lane >> 2) & 3)) * VS + 4 * (lane & 3);
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            acc[h][kb][2 * e] += p[h] * v0;
-            acc[h][kb][2 * e + 1] += p[h] * v1;
-          }
-        }
-    }
+      for (int db = 0; db < DB; ++db) {
+        const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vtr + db * 16));
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, oacc[db], 0, 0, 0);
+      }
 
-    // sum the 16 token lanes of each row
+      if (has_next) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      l[h] = row16_sum(l[h]);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][kb][e] = row16_sum(acc[h][kb][e]);
-    }
-
-    // lane n writes the (head, kb) fragment number n; lanes j cover the 8-wide pieces
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const bool empty = !(l[h] > 0.f);
-      const float inv = empty ? 0.f : 1.f / l[h];
-      const float lse = empty ? kNegInf : (m[h] + log2f(l[h])) * kLn2;
-      const int hq = hk * a.g + hw * G + h;
-      const int prow_in_tile = hw * G + h;  // packed row of a one-token request
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        if (n != h * KB + kb) continue;
-        const int dofs = kb * 32 + j * 8;
-        if (item.slot < 0) {
-          uint16_t* op = O + (int64_t(rq.q_start) * a.Hq + hq) * D + dofs;
-          u32x4 ov;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = pack_bf16x2(acc[h][kb][2 * e] * inv, acc[h][kb][2 * e + 1] * inv);
-          *reinterpret_cast<u32x4*>(op) = ov;
-        } else {
-          const int64_t prow = (int64_t(item.slot) * a.Hk + hk) * a.Tq + prow_in_tile;
-          float* pp = a.part_o + prow * D + dofs;
-          f32x4 o0, o1;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o0[e] = acc[h][kb][e] * inv;
-            o1[e] = acc[h][kb][4 + e] * inv;
-          }
-          *reinterpret_cast<f32x4*>(pp) = o0;
-          *reinterpret_cast<f32x4*>(pp + 4) = o1;
+        for (int kb = 0; kb < KB; ++kb) {
+          kr[kb] = kn[kb];
+          vr[kb] = vn[kb];
         }
       }
-      if (lane == 0) {
-        if (item.slot < 0) a.lse[int64_t(rq.q_start) * a.Hq + hq] = lse;
-        else a.part_lse[(int64_t(item.slot) * a.Hk + hk) * a.Tq + prow_in_tile] = lse;
+    }
+
+    // lane (n, j) summed tokens 4j..4j+3 of every step; add the four token groups
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    if (n < g) {
+      const int hq = hk * g + n;
+      const bool empty = !(l > 0.f);
+      const float inv = empty ? 0.f : 1.f / l;
+      const float lse = empty ? kNegInf : (m + log2f(l)) * kLn2;
+      if (item.slot < 0) {
+        uint16_t* op = O + (int64_t(rq.q_start) * a.Hq + hq) * D + 4 * j;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const f32x4 v = oacc[db] * inv;
+          *reinterpret_cast<u32x2*>(op + db * 16) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+        if (j == 0) a.lse[int64_t(rq.q_start) * a.Hq + hq] = lse;
+      } else {
+        const int64_t prow = (int64_t(item.slot) * a.Hk + hk) * a.Tq + n;  // packed row = head offset
+        float* pp = a.part_o + prow * D + 4 * j;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(pp + db * 16) = oacc[db] * inv;
+        if (j == 0) a.part_lse[prow] = lse;
       }
     }
   }
 }
-
-namespace {
-int group_per_wave(int g) { return g <= 4 ? g : 4; }
-}  // namespace
 
 bool decode_bf16_supported(int d, int g, int Tq) {
-  if (!(d == 64 || d == 128)) return false;
-  if (g < 1 || g > Tq) return false;
-  return g == 1 || g == 2 || g == 4 || g % 4 == 0;
+  return (d == 64 || d == 128) && g >= 1 && g <= 16 && g <= Tq;
 }
 
-int decode_bf16_waves_per_kv_head(int g) { return g / group_per_wave(g); }
+int decode_bf16_waves_per_kv_head(int) { return 1; }
 
-template <int D>
-static const void* decode_fn(int G) {
-  switch (G) {
-    case 1: return reinterpret_cast<const void*>(&attn_decode_bf16_kernel<D, 1>);
-    case 2: return reinterpret_cast<const void*>(&attn_decode_bf16_kernel<D, 2>);
-    default: return reinterpret_cast<const void*>(&attn_decode_bf16_kernel<D, 4>);
-  }
-}
-
-int decode_bf16_blocks_per_cu(int d, int g) {
-  const int G = group_per_wave(g);
+int decode_bf16_blocks_per_cu(int d, int) {
   int nb = 1;
-  const void* f = d == 64 ? decode_fn<64>(G) : decode_fn<128>(G);
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, 64, 0);
+  hipError_t e = hipErrorInvalidValue;
+  if (d == 64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<64>, 64, 0);
+  if (d == 128) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<128>, 64, 0);
   return (e == hipSuccess && nb > 0) ? nb : 1;
 }
 
 hipError_t launch_decode_bf16(const RunArgs& a, hipStream_t s) {
-  const int G = group_per_wave(a.g);
-  dim3 grid(a.C, a.Hk * (a.g / G)), block(64);
-#define BSR_DEC(DD, GG) hipLaunchKernelGGL((attn_decode_bf16_kernel<DD, GG>), grid, block, 0, s, a)
-  if (a.d == 64) {
-    if (G == 1) BSR_DEC(64, 1); else if (G == 2) BSR_DEC(64, 2); else BSR_DEC(64, 4);
-  } else if (a.d == 128) {
-    if (G == 1) BSR_DEC(128, 1); else if (G == 2) BSR_DEC(128, 2); else BSR_DEC(128, 4);
-  } else {
-    return hipErrorInvalidValue;
-  }
-#undef BSR_DEC
+  dim3 grid(a.C, a.Hk), block(64);
+  if (a.d == 64) hipLaunchKernelGGL(attn_decode_bf16_kernel<64>, grid, block, 0, s, a);
+  else if (a.d == 128) hipLaunchKernelGGL(attn_decode_bf16_kernel<128>, grid, block, 0, s, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -33,38 +33,72 @@ __device__ __forceinline__ float load_in<uint16_t>(const uint16_t* p) { return _
 
 }  // namespace
 
-// One workgroup per (merge tile, KV head); threads cover (row, d) elements.
+// One workgroup per (merge tile, KV head).  Phase 1: the maximum and denominator of
+// every row's partial LSEs, with the tile's slot list staged in LDS.  Phase 2: every
+// (row, d) element folds the partial outputs in slot order.
+constexpr int kMergeThreads = 256;
+constexpr int kSlotsInLds = 1024;
+
 template <typename OutT>
-__global__ __launch_bounds__(256) void merge_partials_kernel(RunArgs a) {
-  const int mt = blockIdx.x, hk = blockIdx.y;
-  const MergeRec mr = a.merge[mt];
+__global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a) {
+  __shared__ int s_slot[kSlotsInLds];
+  __shared__ float s_m[128], s_den[128];
+  const int hk = blockIdx.y, tid = threadIdx.x;
+  const MergeRec mr = a.merge[blockIdx.x];
   const ReqRec rq = a.req[mr.req];
-  const int nrows = mr.row_end - mr.row_start;
+  const int nrows = mr.row_end - mr.row_start;  // <= T_q <= 128
+  const int ns = mr.slot_count;
   const int D = a.d;
-  OutT* O = static_cast<OutT*>(a.o);
-  for (int idx = threadIdx.x; idx < nrows * D; idx += blockDim.x) {
-    const int lr = idx / D, e = idx - lr * D;
-    const int row = mr.row_start + lr;
-    const int pos = row / a.g, hq = hk * a.g + row % a.g;
-    float mx = kNegInf;
-    for (int k = 0; k < mr.slot_count; ++k) {
-      const int s = a.mslots[mr.slot_begin + k];
-      mx = fmaxf(mx, a.part_lse[(int64_t(s) * a.Hk + hk) * a.Tq + lr]);
+  const int* __restrict__ slots = a.mslots + mr.slot_begin;
+  const bool cached = ns <= kSlotsInLds;
+  if (cached)
+    for (int k = tid; k < ns; k += kMergeThreads) s_slot[k] = slots[k];
+  __syncthreads();
+  auto slot_at = [&](int k) { return cached ? s_slot[k] : slots[k]; };
+  auto lse_at = [&](int s, int r) { return a.part_lse[(int64_t(s) * a.Hk + hk) * a.Tq + r]; };
+
+  // phase 1: tpr lanes of one wave per row
+  int rp2 = 1;
+  while (rp2 < nrows) rp2 <<= 1;
+  const int tpr = min(64, kMergeThreads / rp2);
+  const int r = tid / tpr, sub = tid % tpr;
+  float mx = kNegInf;
+  if (r < nrows)
+    for (int k = sub; k < ns; k += tpr) mx = fmaxf(mx, lse_at(slot_at(k), r));
+  for (int o = 1; o < tpr; o <<= 1) mx = fmaxf(mx, shfl_xor(mx, o));
+  float den = 0.f;
+  if (r < nrows && mx != kNegInf)
+    for (int k = sub; k < ns; k += tpr) {
+      const float l = lse_at(slot_at(k), r);
+      den += l == kNegInf ? 0.f : expf(l - mx);
     }
-    float num = 0.f, den = 0.f;
-    if (mx != kNegInf) {
-      for (int k = 0; k < mr.slot_count; ++k) {
-        const int s = a.mslots[mr.slot_begin + k];
+  for (int o = 1; o < tpr; o <<= 1) den += shfl_xor(den, o);
+  if (r < nrows && sub == 0) {
+    s_m[r] = mx;
+    s_den[r] = den;
+  }
+  __syncthreads();
+
+  // phase 2: weighted sum of the partial outputs, slot order fixed by the plan
+  OutT* O = static_cast<OutT*>(a.o);
+  for (int idx = tid; idx < nrows * D; idx += kMergeThreads) {
+    const int lr = idx / D, e = idx - lr * D;
+    const float m = s_m[lr];
+    float acc = 0.f;
+    if (m != kNegInf) {
+#pragma unroll 4
+      for (int k = 0; k < ns; ++k) {
+        const int s = slot_at(k);
         const int64_t prow = (int64_t(s) * a.Hk + hk) * a.Tq + lr;
-        const float ls = a.part_lse[prow];
-        const float wgt = ls == kNegInf ? 0.f : expf(ls - mx);
-        num += wgt * a.part_o[prow * D + e];
-        den += wgt;
+        const float l = a.part_lse[prow];
+        const float wgt = l == kNegInf ? 0.f : expf(l - m);
+        acc += wgt * a.part_o[prow * D + e];
       }
     }
-    const int64_t orow = int64_t(rq.q_start + pos) * a.Hq + hq;
-    store_out<OutT>(O + orow * D + e, mx == kNegInf ? 0.f : num / den);
-    if (e == 0) a.lse[orow] = mx == kNegInf ? kNegInf : mx + logf(den);
+    const int row = mr.row_start + lr;
+    const int64_t orow = int64_t(rq.q_start + row / a.g) * a.Hq + hk * a.g + row % a.g;
+    store_out<OutT>(O + orow * D + e, m == kNegInf ? 0.f : acc / s_den[lr]);
+    if (e == 0) a.lse[orow] = m == kNegInf ? kNegInf : m + logf(s_den[lr]);
   }
 }
 
