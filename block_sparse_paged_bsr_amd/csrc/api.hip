@@ -120,7 +120,8 @@ int run_common(const bsr_plan* p, const void* ws, const void* q, const void* k, 
   if (dtype != BSR_DTYPE_F32 && dtype != BSR_DTYPE_BF16) return invalid("unknown dtype");
   if (decode_call && !p->decode)
     return invalid("bsr_run_decode needs a plan with one query per request (qo_indptr == NULL); use bsr_run_prefill");
-  if (!(sm_scale == sm_scale)) return invalid("sm_scale is NaN");
+  if (!(sm_scale > 0.f) || sm_scale == __builtin_huge_valf())
+    return invalid("sm_scale must be positive and finite");
   if (p->B == 0) return BSR_OK;
   if (!q || !k || !v || !o || !lse) return invalid("q, k_cache, v_cache, o and lse must be non-NULL");
   const bool any_tokens = p->total_kv_tokens > 0;

@@ -160,7 +160,8 @@ int bsr_plan_export(const bsr_plan* plan, bsr_plan_view* view);
  * Exact attention, eq. 1 of "FlashInfer: Making Attention Fit the Serving Workload"
  * (§2.1), computed tile by tile with the online-softmax recurrence and split across
  * workers as planned; partial states are combined with the merge of eq. 6.  Runs the
- * attention kernel and, if the plan split any request, the merge kernel.
+ * attention kernel and, if the plan split any request, the merge kernel.  sm_scale must
+ * be positive and finite (1/sqrt(d) for the standard operator).
  */
 int bsr_run_decode(const bsr_plan* plan, const void* ws, const void* q, const void* k_cache,
                    const void* v_cache, void* o, float* lse, int32_t dtype, float sm_scale,
