@@ -3,15 +3,21 @@
 One step = one bsr_run_decode call on the batch-64 paged decode workload (bf16,
 KV lengths U[512, 8192], page size 16, 32 query / 8 KV heads, head_dim 128): the
 attention kernel over the planned split-KV partition plus the merge of the partial
-states.  The plan is built once and reused by every step (it is per generation step
-and shared by all layers).  Inputs are resident in HBM before timing; three copies of
+states.  The plan is built once and reused by every step (one plan per generation
+step serves all layers).  Inputs are resident in HBM before timing; three copies of
 the KV pool are rotated so the last-level cache cannot serve a step from the previous
-one.  The same JSON line also reports the ragged causal prefill (TFLOP/s), the
-vector-sparse (page size 1) runs next to their contiguous twins, the composable
-shared-prefix decode, the roofline of the dominant kernel, and the fp64 CPU oracle
-timed on a bounded sample as a baseline.
+one.  The same JSON line also reports
+  - the ragged causal prefill (batch 16, q_len = kv_len U[256, 4096]) in TFLOP/s,
+  - page size 1 (rows scattered over a 2^20-row pool) next to the same contents laid
+    out contiguously, for the decode batch and for a batch-8 2048-token causal prefill,
+  - the composable shared-prefix decode (16 groups x 4 requests, 2048-token prefix
+    per group at 4 queries per block row + private suffixes, merged) and its
+    single-level baseline,
+  - the roofline of the dominant kernel, timed with HIP events on its launch stream,
+  - the fp64 CPU oracle timed on the host cores as a baseline.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--only NAME]
+                       [--copy-calib]
 """
 from __future__ import annotations
 
@@ -30,30 +36,32 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "paged decode HBM GB/s (% of peak); causal prefill TFLOPS (% bf16 MFMA peak)"
+H_QO, H_KV, D = 32, 8, 128
+SM = 1.0 / math.sqrt(D)
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def decode_bytes(kv_lens, B, Hq, Hk, d, nnz, elt=2):
-    """Algorithmic bytes of one decode call: K and V read once, Q read, O and LSE written,
-    plus the page table (indices, indptr, last-page lengths)."""
-    kv = int(np.sum(kv_lens)) * Hk * d * elt * 2
-    qo = 2 * B * Hq * d * elt
-    return kv + qo + B * Hq * 4 + nnz * 4 + (B + 1) * 4 + B * 4
+def decode_bytes(kv_lens, B, nnz, elt=2):
+    """Algorithmic bytes of one decode call: K and V read once (one KV head serves its g
+    query heads), Q read, O and LSE written, page table (indices, indptr, last lengths)."""
+    kv = int(np.sum(kv_lens)) * H_KV * D * elt * 2
+    qo = 2 * B * H_QO * D * elt
+    return kv + qo + B * H_QO * 4 + nnz * 4 + (B + 1) * 4 + B * 4
 
 
-def prefill_flops(lens, Hq, d):
-    """QK^T and PV flops over the unmasked (causal) pairs only."""
-    return float(sum(4.0 * d * Hq * l * (l + 1) / 2 for l in lens))
+def prefill_flops(lens):
+    """QK^T and PV flops over the unmasked (causal, bottom-right) pairs only."""
+    return float(sum(4.0 * D * H_QO * l * (l + 1) / 2 for l in lens))
 
 
 def time_calls(fn, steps, warmup):
     import torch
 
-    for _ in range(warmup):
-        fn(0)
+    for s in range(warmup):
+        fn(s)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
@@ -81,8 +89,8 @@ def per_call_ms(fn, n):
 
 
 def kernel_times(fn, n):
-    """Average per-launch durations of the attention and merge kernels, measured with HIP
-    events that the library records on the launch stream around each kernel."""
+    """Average per-launch durations of the attention and merge kernels, from HIP events
+    the library records on the launch stream around each kernel."""
     import torch
     from block_sparse_paged_bsr_amd import api
 
@@ -96,100 +104,207 @@ def kernel_times(fn, n):
             t["merge_ms"] / max(t["merge_launches"], 1), t["merge_launches"])
 
 
-def bench_decode(args):
-    import torch
-    from block_sparse_paged_bsr_amd import api, inputs
+def make_plan(b, kind, causal=False):
+    from block_sparse_paged_bsr_amd import api
 
-    b = inputs.batched_decode_bf16(seed=0, poison=False)
+    C = api.query_num_workers(kind, H_QO, H_KV, D)
+    return api.Plan(b.kv_indptr, b.kv_indices, b.last_page_len, num_pages=b.num_pages,
+                    num_qo_heads=H_QO, num_kv_heads=H_KV, head_dim=D, page_size=b.page_size,
+                    qo_indptr=b.qo_indptr, causal=causal, num_workers=C)
+
+
+def run_case(b, kind, steps, warmup, rotate=1, causal=False):
+    """Plan once, upload, then time steps of run_decode / run_prefill."""
+    import torch
+    from block_sparse_paged_bsr_amd import api
+
     q, k, v = b.torch_values("cuda")
-    C = api.query_num_workers("decode", 32, 8, 128)
     t0 = time.perf_counter()
-    p = api.Plan(b.kv_indptr, b.kv_indices, b.last_page_len, num_pages=b.num_pages, num_qo_heads=32,
-                 num_kv_heads=8, head_dim=128, page_size=16, num_workers=C)
+    p = make_plan(b, kind, causal)
     plan_us = (time.perf_counter() - t0) * 1e6
     ws = api.alloc_workspace(p)
     p.upload(ws)
-    pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(2)]
+    pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(rotate - 1)]
     o = torch.empty_like(q)
-    lse = torch.empty(q.shape[0], 32, dtype=torch.float32, device="cuda")
-    sm = 1.0 / math.sqrt(128)
+    lse = torch.empty(q.shape[0], H_QO, dtype=torch.float32, device="cuda")
+    fn = api.run_decode if kind == "decode" else api.run_prefill
 
     def step(s):
         kk, vv = pools[s % len(pools)]
-        api.run_decode(p, ws, q, kk, vv, o=o, lse=lse, sm_scale=sm)
+        fn(p, ws, q, kk, vv, o=o, lse=lse, sm_scale=SM)
 
-    ms = time_calls(step, args.steps, args.warmup)
-    med, mn, p90 = per_call_ms(step, 50)
-    attn_ms, n_attn, merge_ms, n_merge = kernel_times(step, 50)
-    nbytes = decode_bytes(b.kv_lens, b.batch, 32, 8, 128, len(b.kv_indices))
+    ms = time_calls(step, steps, warmup)
     e = p.export()
-    return {
-        "ms_per_step": ms,
-        "gbs": nbytes / (ms * 1e-3) / 1e9,
-        "bytes": nbytes,
-        "median_ms": med, "min_ms": mn, "p90_ms": p90,
-        "attn_kernel_ms": attn_ms, "merge_kernel_ms": merge_ms,
-        "attn_launches": n_attn, "merge_launches": n_merge,
-        "plan_host_us": plan_us, "num_workers": C, "num_items": int(e["items"].shape[0]),
-        "num_slots": e["num_slots"], "tokens": int(b.kv_lens.sum()), "batch": b,
-    }
+    res = {"ms": ms, "plan_us": plan_us, "num_workers": e["num_workers"],
+           "items": int(e["items"].shape[0]), "slots": e["num_slots"], "step": step,
+           "out": (o, lse)}
+    return res
+
+
+def bench_decode(args):
+    from block_sparse_paged_bsr_amd import inputs
+
+    b = inputs.batched_decode_bf16(seed=0, poison=False)
+    r = run_case(b, "decode", args.steps, args.warmup, rotate=3)
+    med, mn, p90 = per_call_ms(r["step"], 50 if not args.quick else 10)
+    attn_ms, n_attn, merge_ms, n_merge = kernel_times(r["step"], 50 if not args.quick else 10)
+    nbytes = decode_bytes(b.kv_lens, b.batch, len(b.kv_indices))
+    r.update({"gbs": nbytes / (r["ms"] * 1e-3) / 1e9, "bytes": nbytes, "median_ms": med, "min_ms": mn,
+              "p90_ms": p90, "attn_kernel_ms": attn_ms, "merge_kernel_ms": merge_ms,
+              "tokens": int(b.kv_lens.sum()), "batch": b})
+    return r
 
 
 def bench_prefill(args):
+    from block_sparse_paged_bsr_amd import inputs
+
+    b = inputs.ragged_prefill_bf16(seed=0, poison=False)
+    r = run_case(b, "prefill", max(5, args.steps // 5), 2, causal=True)
+    attn_ms, _, merge_ms, _ = kernel_times(r["step"], 5)
+    fl = prefill_flops(b.kv_lens)
+    return {"ms": r["ms"], "tflops": fl / (r["ms"] * 1e-3) / 1e12, "flops": fl, "attn_kernel_ms": attn_ms,
+            "merge_kernel_ms": merge_ms, "num_workers": r["num_workers"], "batch": b}
+
+
+def bench_vector_sparse(args):
+    """Page size 1 over a 2^20-row pool vs the same contents contiguous."""
+    from block_sparse_paged_bsr_amd import inputs
+
+    out = {}
+    lens = inputs.decode_lengths(0)
+    a, c = inputs.vector_sparse_pair(0, lens, pool_rows=1 << 20)
+    nbytes = decode_bytes(lens, len(lens), len(a.kv_indices))
+    ra = run_case(a, "decode", args.steps, args.warmup)
+    rc = run_case(c, "decode", args.steps, args.warmup)
+    out["decode"] = {"paged_us": round(ra["ms"] * 1e3, 2), "contiguous_us": round(rc["ms"] * 1e3, 2),
+                     "paged_gbs": round(nbytes / (ra["ms"] * 1e-3) / 1e9, 1),
+                     "contiguous_gbs": round(nbytes / (rc["ms"] * 1e-3) / 1e9, 1),
+                     "paged_over_contiguous_time": round(ra["ms"] / rc["ms"], 4)}
+    del a, c, ra, rc
+    plens = [2048] * 8
+    a, c = inputs.vector_sparse_pair(1, plens, plens, pool_rows=1 << 20, causal=True)
+    fl = prefill_flops(plens)
+    ra = run_case(a, "prefill", max(5, args.steps // 5), 2, causal=True)
+    rc = run_case(c, "prefill", max(5, args.steps // 5), 2, causal=True)
+    out["prefill"] = {"paged_us": round(ra["ms"] * 1e3, 2), "contiguous_us": round(rc["ms"] * 1e3, 2),
+                      "paged_tflops": round(fl / (ra["ms"] * 1e-3) / 1e12, 1),
+                      "contiguous_tflops": round(fl / (rc["ms"] * 1e-3) / 1e12, 1),
+                      "paged_over_contiguous_time": round(ra["ms"] / rc["ms"], 4)}
+    return out
+
+
+def bench_composable(args):
+    """Two BSR views (shared prefix at 4 queries per block row, private suffixes) merged,
+    vs the single-level view (each request reads prefix ++ suffix itself)."""
     import torch
     from block_sparse_paged_bsr_amd import api, inputs
 
-    b = inputs.ragged_prefill_bf16(seed=0, poison=False)
+    b = inputs.shared_prefix_decode(seed=0, poison=False)
     q, k, v = b.torch_values("cuda")
-    C = api.query_num_workers("prefill", 32, 8, 128)
-    p = api.Plan(b.kv_indptr, b.kv_indices, b.last_page_len, num_pages=b.num_pages, num_qo_heads=32,
-                 num_kv_heads=8, head_dim=128, page_size=16, qo_indptr=b.qo_indptr, causal=True,
-                 num_workers=C)
-    ws = api.alloc_workspace(p)
-    p.upload(ws)
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[0], 32, dtype=torch.float32, device="cuda")
-    sm = 1.0 / math.sqrt(128)
+    C1 = api.query_num_workers("prefill", H_QO, H_KV, D)
+    C2 = api.query_num_workers("decode", H_QO, H_KV, D)
+    p1 = api.Plan(b.l1_kv_indptr, b.l1_kv_indices, b.l1_last_page_len, num_pages=b.num_pages,
+                  num_qo_heads=H_QO, num_kv_heads=H_KV, head_dim=D, page_size=b.page_size,
+                  qo_indptr=b.l1_qo_indptr, causal=False, num_workers=C1)
+    p2 = api.Plan(b.l2_kv_indptr, b.l2_kv_indices, b.l2_last_page_len, num_pages=b.num_pages,
+                  num_qo_heads=H_QO, num_kv_heads=H_KV, head_dim=D, page_size=b.page_size, num_workers=C2)
+    pf = api.Plan(b.full_kv_indptr, b.full_kv_indices, b.full_last_page_len, num_pages=b.num_pages,
+                  num_qo_heads=H_QO, num_kv_heads=H_KV, head_dim=D, page_size=b.page_size, num_workers=C2)
+    w1, w2, wf = api.alloc_workspace(p1), api.alloc_workspace(p2), api.alloc_workspace(pf)
+    p1.upload(w1)
+    p2.upload(w2)
+    pf.upload(wf)
+    R = q.shape[0]
+    o1, o2, o = (torch.empty_like(q) for _ in range(3))
+    l1, l2, l = (torch.empty(R, H_QO, dtype=torch.float32, device="cuda") for _ in range(3))
 
-    def step(s):
-        api.run_prefill(p, ws, q, k, v, o=o, lse=lse, sm_scale=sm)
+    # the pool (~280 MB) is near the last-level cache size: rotate three copies
+    pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(2)]
 
-    n = max(3, args.steps // 4)
-    ms = time_calls(step, n, 2)
-    attn_ms, _, merge_ms, _ = kernel_times(step, 5)
-    fl = prefill_flops(b.kv_lens, 32, 128)
-    return {"ms": ms, "tflops": fl / (ms * 1e-3) / 1e12, "flops": fl, "attn_kernel_ms": attn_ms,
-            "merge_kernel_ms": merge_ms, "num_workers": C, "lens_sum": int(b.kv_lens.sum())}
+    def composed(s):
+        kk, vv = pools[s % 3]
+        api.run_prefill(p1, w1, q, kk, vv, o=o1, lse=l1, sm_scale=SM)
+        api.run_decode(p2, w2, q, kk, vv, o=o2, lse=l2, sm_scale=SM)
+        api.merge_state(o1, l1, o2, l2, o_out=o, lse_out=l)
+
+    def single(s):
+        kk, vv = pools[s % 3]
+        api.run_decode(pf, wf, q, kk, vv, o=o, lse=l, sm_scale=SM)
+
+    ms_c = time_calls(composed, args.steps, args.warmup)
+    ms_s = time_calls(single, args.steps, args.warmup)
+    per = H_KV * D * 2 * 2
+    qol = 2 * R * H_QO * D * 2 + R * H_QO * 4
+    comp_bytes = b.groups * b.prefix_len * per + int(b.suffix_lens.sum()) * per + qol
+    single_bytes = int((b.prefix_len + b.suffix_lens).sum()) * per + qol
+    return {"composable_us": round(ms_c * 1e3, 2), "single_level_us": round(ms_s * 1e3, 2),
+            "speedup": round(ms_s / ms_c, 3), "composable_bytes": comp_bytes, "single_level_bytes": single_bytes,
+            "composable_gbs_counted": round(comp_bytes / (ms_c * 1e-3) / 1e9, 1),
+            "single_level_gbs": round(single_bytes / (ms_s * 1e-3) / 1e9, 1),
+            "traffic_ratio_eq15": round(single_bytes / comp_bytes, 3)}
 
 
 def cpu_baseline(dec):
-    """The fp64 numpy oracle on a bounded sample of the decode batch (first requests until
-    ~15 s of CPU work), reported in the same unit (GB/s of algorithmic bytes)."""
+    """The fp64 numpy oracle, as it stands, on the decode batch (whole requests until ~12 s
+    of CPU work), reported in the same unit (GB/s of algorithmic bytes)."""
     from oracle import attention as A
 
     b = dec["batch"]
     cores = len(os.sched_getaffinity(0))
-    done, nbytes = [], 0
+    done = []
     t0 = time.perf_counter()
-    for i in range(b.batch):
-        A.batch_attention(b.q_f32, b.k_f32, b.v_f32, b.kv_indptr, b.kv_indices, b.last_page_len, 16,
-                          32, 8, 1.0 / math.sqrt(128), requests=[i])
-        done.append(i)
-        if time.perf_counter() - t0 > 15.0:
-            break
+    reps = 0
+    while time.perf_counter() - t0 < 12.0:
+        for i in range(b.batch):
+            A.batch_attention(b.q_f32, b.k_f32, b.v_f32, b.kv_indptr, b.kv_indices, b.last_page_len,
+                              16, H_QO, H_KV, SM, requests=[i])
+            done.append(i)
+            if time.perf_counter() - t0 > 12.0:
+                break
+        reps += 1
     dt = time.perf_counter() - t0
     lens = b.kv_lens[done]
-    nbytes = decode_bytes(lens, len(done), 32, 8, 128, int(sum((l + 15) // 16 for l in lens)))
+    nbytes = decode_bytes(lens, len(done), int(sum((l + 15) // 16 for l in lens)))
     try:
         import threadpoolctl
 
         blas = max((x.get("num_threads", 1) for x in threadpoolctl.threadpool_info()), default=1)
     except Exception:
         blas = None
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "blas_threads": blas,
-            "sample": f"fp64 numpy oracle on the first {len(done)} of 64 decode requests "
-                      f"({int(lens.sum())} KV tokens), {dt:.1f} s wall"}
+            "sample": f"fp64 numpy oracle, {len(done)} request evaluations of the batch-64 decode "
+                      f"({int(lens.sum())} KV tokens, {reps} pass(es)), {dt:.1f} s wall"}
+
+
+def measured_traffic():
+    """HBM bytes per launch of the decode kernel from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy), or None if the kernel source has
+    changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "decode_batch64_traffic.json")
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
+def copy_calibration():
+    """A plain 512 MiB device copy (torch), so counter runs can scale FETCH_SIZE/WRITE_SIZE."""
+    import torch
+
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 x {n} bytes")
 
 
 def main():
@@ -198,18 +313,32 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="decode only, no CPU baseline")
+    ap.add_argument("--only", choices=["decode", "prefill", "vector", "composable"], default=None)
+    ap.add_argument("--copy-calib", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this attention path has no multi-GPU part "
-              "(every GPU would run the same kernels on its own requests); use --gpus 1",
+        print("bench.py measures one GPU: every GPU would run the same kernels on its own "
+              "requests and KV heads, there is no cross-GPU step to time; use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
     import torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     log(f"device: {torch.cuda.get_device_name(0)}  torch {torch.__version__}")
+    if args.copy_calib:
+        copy_calibration()
+    if args.only == "prefill":
+        pf = bench_prefill(args)
+        log(f"prefill: {pf['ms']*1e3:.1f} us, {pf['tflops']:.1f} TFLOP/s")
+        return
+    if args.only == "vector":
+        log(json.dumps(bench_vector_sparse(args)))
+        return
+    if args.only == "composable":
+        log(json.dumps(bench_composable(args)))
+        return
     dec = bench_decode(args)
-    log(f"decode: {dec['ms_per_step']*1e3:.1f} us/step, {dec['gbs']:.0f} GB/s; attn kernel "
+    log(f"decode: {dec['ms']*1e3:.1f} us/step, {dec['gbs']:.0f} GB/s; attn kernel "
         f"{dec['attn_kernel_ms']*1e3:.1f} us, merge {dec['merge_kernel_ms']*1e3:.1f} us")
     out = {
         "metric": METRIC,
@@ -218,7 +347,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(dec["ms_per_step"], 5),
+        "ms_per_step": round(dec["ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -228,20 +357,22 @@ def main():
             "workload": "batched paged decode bf16: batch 64, KV lengths U[512,8192], page size 16, "
                         "32 query / 8 KV heads, head_dim 128, split-KV + merge",
             "tokens": dec["tokens"], "algorithmic_bytes": dec["bytes"],
-            "num_workers": dec["num_workers"], "work_items": dec["num_items"],
-            "partial_slots": dec["num_slots"], "plan_host_us": round(dec["plan_host_us"], 1),
+            "num_workers": dec["num_workers"], "work_items": dec["items"],
+            "partial_slots": dec["slots"], "plan_host_us": round(dec["plan_us"], 1),
             "median_us": round(dec["median_ms"] * 1e3, 2), "min_us": round(dec["min_ms"] * 1e3, 2),
             "p90_us": round(dec["p90_ms"] * 1e3, 2),
             "pct_hbm_peak": round(100 * dec["gbs"] / HBM_PEAK_GBS, 2),
+            "kv_pool_rotation": 3,
         },
     }
     ach = dec["bytes"] / (dec["attn_kernel_ms"] * 1e-3) / 1e9
     out["roofline"] = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-                       "kernel": "attn_decode_bf16_kernel<128,4>",
+                       "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                       "kernel": "attn_decode_bf16_kernel<128>",
                        "kernel_avg_us": round(dec["attn_kernel_ms"] * 1e3, 2),
                        "merge_avg_us": round(dec["merge_kernel_ms"] * 1e3, 2)}
     if not args.quick:
+        del dec["step"], dec["out"]
         pf = bench_prefill(args)
         log(f"prefill: {pf['ms']*1e3:.1f} us, {pf['tflops']:.1f} TFLOP/s")
         out["prefill"] = {"workload": "ragged causal prefill bf16: batch 16, q_len = kv_len U[256,4096], "
@@ -251,6 +382,14 @@ def main():
                           "attn_kernel_ms": round(pf["attn_kernel_ms"], 4),
                           "merge_kernel_ms": round(pf["merge_kernel_ms"], 4),
                           "flops": pf["flops"], "num_workers": pf["num_workers"]}
+        torch.cuda.empty_cache()
+        vs = bench_vector_sparse(args)
+        log(f"vector sparse: {vs}")
+        out["vector_sparse"] = vs
+        torch.cuda.empty_cache()
+        cp = bench_composable(args)
+        log(f"composable: {cp}")
+        out["composable"] = cp
         out["cpu_baseline"] = cpu_baseline(dec)
     print(json.dumps(out), flush=True)
 
