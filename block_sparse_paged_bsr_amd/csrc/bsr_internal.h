@@ -7,7 +7,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/bsr_attn.h"
+#include "bsr_attn.h"
 
 namespace bsr {
 
