@@ -202,7 +202,9 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
     heap.pop();
     queues[k.second].push_back(m);
     items[m].worker = k.second;
-    k.first += int64_t(p->alpha) * p->qo_len[items[m].req] + int64_t(p->beta) * items[m].kl;
+    // the item's query length: positions covered by its tile's packed rows
+    const int64_t positions = (items[m].r1 - 1) / p->g - items[m].r0 / p->g + 1;
+    k.first += int64_t(p->alpha) * positions + int64_t(p->beta) * items[m].kl;
     p->worker_cost[k.second] = k.first;
     heap.push(k);
   }

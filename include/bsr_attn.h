@@ -75,7 +75,8 @@ typedef struct bsr_plan_desc {
   int32_t causal;               /* 1: key k visible to query q iff k <= q + l_kv - l_qo */
   int32_t num_workers;          /* C: persistent workers; 0 => default for 256 CUs */
   int32_t tile_q;               /* packed query rows per tile; 0 => tile rule */
-  int32_t alpha, beta;          /* cost = alpha*l_qo + beta*chunk_len; both 0 => (2, 1) */
+  int32_t alpha, beta;          /* item cost = alpha * (query positions of its tile) +
+                                   beta * chunk_len; both 0 => (2, 1) */
 } bsr_plan_desc;
 
 /*
@@ -88,7 +89,8 @@ typedef struct bsr_plan_desc {
  *   W = sum_i ceil(pq_i / T_q) * l_kv(i);  chunk limit L = max(1, ceil(W / C));
  *   each query tile's visible KV range is cut into chunks of at most L tokens;
  *   chunks are stably sorted by length, descending, and each goes to the worker of
- *   least accumulated cost (ties: lower worker id).  A tile with one chunk writes its
+ *   least accumulated cost (ties: lower worker id); an item costs alpha times the query
+ *   positions of its tile (1 in decode) plus beta times its chunk length (eq. 11).  A tile with one chunk writes its
  *   final output; chunks of split tiles get partial slots, folded by the merge pass in
  *   KV order (deterministic, no atomics).
  * Copies every host array, so the caller may free them on return.  Pure host code:

@@ -20,8 +20,9 @@ scheduler as the pages describe it:
 
 Readings taken where the pages leave a detail open (each is listed in the design doc):
 the query-tile set is {16, 32, 64, 128} (a tile is a multiple of the 16-row matrix
-instruction; 128 when the average exceeds 64); the per-item cost uses the request's
-query length; chunks are counted in tokens and may start inside a page; a causal
+instruction; 128 when the average exceeds 64); the per-item cost charges the query
+positions of the item's own tile (one for a decode request, at most T_q / g for a
+prefill tile) plus its chunk length; chunks are counted in tokens and may start inside a page; a causal
 tile's visible KV range ends at the tile's last query position; ties in the heap go
 to the lower worker id; a tile with exactly one chunk writes its final output, the
 chunks of split tiles get partial slots 0, 1, 2, ... in assignment order, and each
@@ -75,6 +76,11 @@ class Plan:
     merge_tiles: List[int]  # tiles that the merge pass writes (split or empty)
     merge_slots: List[List[int]]  # ordered slot list per merge tile
     num_slots: int
+
+
+def tile_positions(item, g):
+    """Query positions covered by the packed rows [row_start, row_end) of a tile."""
+    return (item.row_end - 1) // g - item.row_start // g + 1
 
 
 def choose_tile_q(packed_lens, tile_q=0):
@@ -151,7 +157,7 @@ def make_plan(
         c, w = heapq.heappop(heap)
         queues[w].append(m)
         items[m].worker = w
-        c += alpha * qo_lens[items[m].req] + beta * items[m].kv_len
+        c += alpha * tile_positions(items[m], g) + beta * items[m].kv_len
         cost[w] = c
         heapq.heappush(heap, (c, w))
 

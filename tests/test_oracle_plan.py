@@ -102,7 +102,10 @@ def test_invariants(seed):
     for m in order:
         w = p.items[m].worker
         assert load[w] == min(load) and w == load.index(min(load))
-        load[w] += 2 * qol[p.items[m].req] + p.items[m].kv_len
+        it = p.items[m]
+        positions = (it.row_end - 1) // g - it.row_start // g + 1
+        assert 1 <= positions <= min(qol[it.req], p.tile_q)
+        load[w] += 2 * positions + it.kv_len
     assert load == p.worker_cost
     # slots: exactly the chunks of split tiles, numbered 0.. in assignment order
     split = [m for m in order if len(p.tiles[p.items[m].tile].items) > 1]
