@@ -38,6 +38,10 @@ COMMON = [
 ]
 # Packed fp32 (v_pk_*_f32) code generation is switched off for every HIP source.
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The prefill kernel runs with the IEEE mode bit off: scores are never NaN (masked ones are
+# -inf), and with the bit on every maximum over matrix-core results needs an extra NaN-quieting
+# v_max_f32 per operand.
+EXTRA_FLAGS = {"attn_prefill_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def _hipcc():
@@ -51,7 +55,7 @@ def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [_hipcc()] + COMMON
     if src.endswith(".hip"):
-        cmd += HIP_FLAGS + ["-x", "hip"]
+        cmd += HIP_FLAGS + EXTRA_FLAGS.get(os.path.basename(src), []) + ["-x", "hip"]
     cmd += ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass warns that it does not know the packed-fp32 feature: harmless
