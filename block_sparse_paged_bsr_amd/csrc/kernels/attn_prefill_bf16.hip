@@ -12,19 +12,20 @@
 // g * h_kv + r mod g, eq. 3 of the review), so every staged KV tile serves all g query
 // heads of the group.
 //
-// LDS layout of one stage (64 tokens): K then V, each as 4 token groups (16 tokens) x
-// D/32 column groups (32 head-dim values) of 1 KB fragments, 64 lanes x 16 bytes:
+// LDS layout: four arrays, two K slots and two V slots, each one 64-token tile of K (or V)
+// as 4 token groups (16 tokens) x D/32 column groups (32 head-dim values) of 1 KB fragments,
+// 64 lanes x 16 bytes:
 //   K fragment (a, b): byte 16 L holds K[16a + L%16][32b + 8(L/16) .. +8]
 //   V fragment (a, b): byte 16 L holds V[16a + t][32b + 8c .. +8], c = L/16,
-//                      t = (L%16) xor 4(c%2)
-// Every DMA instruction reads 64 contiguous bytes of 16 token rows.  The swizzle of the
-// V fragments makes each ds_read_b64_tr_b16 (16 lanes x 8 bytes) hit the 32 LDS banks
+//                      t = (L%16) xor s(c), s(c) = 8(c%2) + 4(c/2)
+// Every DMA instruction reads 64 contiguous bytes of 16 token rows.  The V swizzle makes every
+// ds_read_b64_tr_b16 (32 lanes x 8 bytes per LDS cycle on gfx950's 64 banks) touch each bank
 // once, for both matrix shapes below; K reads are linear or one 256-byte row apart.
-// Two stages live in two separate LDS arrays: the DMA of tile i+1 into one overlaps the
-// products of tile i from the other, and LDS reads never wait for the other stage's DMA.
 //
-// Large query tiles (more than 32 packed rows) use v_mfma_f32_32x32x16_bf16 (on gfx950
-// it sustains about twice the rate of the 16x16x32 shape).  Per wave, a 32-row block:
+// Large query tiles (more than 64 packed rows) use v_mfma_f32_32x32x16_bf16 (on gfx950 it
+// sustains about twice the rate of the 16x16x32 shape), one 32-row block per wave, and a
+// software pipeline over the KV tiles: while the matrix cores compute the scores of tile i+1,
+// the vector ALUs run the softmax of tile i; then P.V of tile i runs.  Per wave:
 //   S^T[token][row] = sum_k K[token][k] Q[row][k]   (A = K, B = Q^T kept in registers)
 //     lane L holds, for row L%32, tokens 8(i/4) + 4(L/32) + i%4, i = 0..15, of a
 //     32-token block
@@ -35,14 +36,21 @@
 //   O^T[d][row] += sum_token V^T[d][token] P^T[token][row]: B = P^T is the score
 //     accumulator converted to bf16 in place (items 8k..8k+7 form one 16-token k-block),
 //     A = V^T from two transposing reads per k-block, with the same token order.
-// Small query tiles (at most 32 rows: decode-like and short requests, the composable
-// prefix level) use the 16x16x32 shape with 16-row blocks.
+// K and V have their own rings with a barrier each per tile, so each is fetched 1.5 tiles
+// ahead of its use; the waits name the exact number of younger loads that may still be in
+// flight.
+// Query tiles of 33-64 rows use the same 32x32 products on two waves per row block (each
+// takes half of every KV tile); tiles of at most 32 rows (decode-like and short requests,
+// the composable prefix level) use the 16x16x32 shape with 16-row blocks.  These smaller
+// shapes use a plain two-stage loop.
 //
 // Every wave computes all of its row blocks, including absent ones at the end of a
 // request (zero queries, never written), so the products carry no branches.  When a
 // tile has fewer row blocks than waves, waves also split the tile's tokens and their
 // states are combined at the end of the item with the merge of eq. 6 (§3.2 of the
 // review).
+#include <type_traits>
+
 #include "common.cuh"
 #include "launch.h"
 
@@ -54,6 +62,7 @@ constexpr int kTileKV = 64;  // tokens per staged KV tile
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleMargin = 8.f;  // log2 units
+constexpr int kPageWindow = 2048;      // page ids staged in LDS per workgroup
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -62,15 +71,33 @@ struct PF {
   static constexpr int KB = D / 32;           // 32-wide column groups per row
   static constexpr int FRAG = 1024;           // 64 lanes x 16 bytes
   static constexpr int TILE = 4 * KB * FRAG;  // K (or V) of 64 tokens
-  static constexpr int STAGE = 2 * TILE;      // K then V
   static constexpr int COMB16 = 16 * (D + 2) * 4;  // combine area of one 16-row wave
   static constexpr int COMB32 = 32 * (D + 2) * 4;  // combine area of one 32-row wave
-  static_assert(2 * COMB16 <= STAGE && COMB32 <= STAGE, "combine areas must fit in the stages");
+  static constexpr int SLOT = TILE > COMB32 ? TILE : COMB32;  // bytes of one LDS array
+  static_assert(2 * COMB16 <= SLOT, "two 16-row combine areas must fit in one array");
 };
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void* lds_ptr;
+// LDS-typed pointers: slot arithmetic stays in 32-bit LDS addresses and every access is a
+// ds_* instruction, also where a slot is chosen at run time
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) int32_t lds_i32;
+typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+
+// The workgroup's LDS: four SLOT-byte arrays (K and V of two 64-token tiles; the pipelined
+// path splits each into two 32-token slots) and the page-id window.
+template <int D>
+struct Slots {
+  lds_u8* base;
+  __device__ __forceinline__ lds_u8* k0() const { return base; }
+  __device__ __forceinline__ lds_u8* k1() const { return base + PF<D>::SLOT; }
+  __device__ __forceinline__ lds_u8* v0() const { return base + 2 * PF<D>::SLOT; }
+  __device__ __forceinline__ lds_u8* v1() const { return base + 3 * PF<D>::SLOT; }
+  __device__ __forceinline__ lds_i32* table() const { return reinterpret_cast<lds_i32*>(base + 4 * PF<D>::SLOT); }
+  static constexpr int BYTES = 4 * PF<D>::SLOT + 4 * kPageWindow;
+};
 
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   bf16x2 r;
@@ -107,7 +134,7 @@ __device__ __forceinline__ float pair16_sum(float x) {
   return __uint_as_float(a) + __uint_as_float(b);
 }
 
-__device__ __forceinline__ s16x4 tr_read(const unsigned char* p) {
+__device__ __forceinline__ s16x4 tr_read(const lds_u8* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(p));
 }
 
@@ -116,84 +143,220 @@ __device__ __forceinline__ bf16x8 cat(s16x4 lo, s16x4 hi) {
   return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
 }
 
+// row swizzle of the 16-byte column chunk c16 (0..3) inside a V fragment
+__device__ __forceinline__ int v_swz(int c16) { return 8 * (c16 & 1) + 4 * (c16 >> 1); }
+
 // byte offset, inside a V fragment, of the 8-byte chunk c (head-dim 4c .. 4c+3 of the
 // fragment's 32 columns) of token t (0..15)
 __device__ __forceinline__ int v_chunk(int t, int c) {
   const int c16 = c >> 1;
-  return 16 * (16 * c16 + (t ^ (4 * (c16 & 1)))) + 8 * (c & 1);
+  return 16 * (16 * c16 + (t ^ v_swz(c16))) + 8 * (c & 1);
 }
 
+// Plan records are the same for the whole workgroup: read them once and keep every field in
+// a scalar register, so everything derived from them is uniform (scalar branches, no
+// per-lane copies).
+template <typename T>
+__device__ __forceinline__ T uniform_load(const T* p) {
+  static_assert(sizeof(T) % 4 == 0, "records of 32-bit fields");
+  int32_t w[sizeof(T) / 4];
+  __builtin_memcpy(w, p, sizeof(T));
+#pragma unroll
+  for (unsigned i = 0; i < sizeof(T) / 4; ++i) w[i] = __builtin_amdgcn_readfirstlane(w[i]);
+  T v;
+  __builtin_memcpy(&v, w, sizeof(T));
+  return v;
+}
+
+// Token -> page lookups (eq. 7 of "FlashInfer: Making Attention Fit the Serving Workload").
+// A window of up to kPageWindow entries of the request's page list is staged in LDS, so the
+// lookups inside the tile loops are LDS reads and the only vector-memory loads in flight there
+// are the tile DMAs.  POW2: the page size is a power of two (shift and mask).
+template <bool POW2>
 struct Paging {
-  const int32_t* indices;
+  const int32_t* indices;  // the request's page list starts at indices + page_start
+  lds_i32* table;          // LDS window: table[j] = page id of request page base + j
   int32_t page_start, P, p_shift, Hk, hk, kv_end;
-  __device__ __forceinline__ int32_t page_of(int t) const {
+  int32_t base;  // first request page held in the window
+  __device__ __forceinline__ int page_no(int t) const {
     const int tc = min(t, kv_end - 1);
-    return indices[page_start + (p_shift >= 0 ? (tc >> p_shift) : tc / P)];
+    return POW2 ? (tc >> p_shift) : tc / P;
   }
+  __device__ __forceinline__ int32_t page_of(int t) const { return table[page_no(t) - base]; }
   // first element of token t's row for this KV head, t clamped to the chunk
   template <int D>
   __device__ __forceinline__ int64_t row(int t, int32_t page) const {
     const int tc = min(t, kv_end - 1);
-    const int off = p_shift >= 0 ? (tc & ((1 << p_shift) - 1)) : tc - (tc / P) * P;
+    const int off = POW2 ? (tc & (P - 1)) : tc - (tc / P) * P;
     return ((int64_t(page) * P + off) * Hk + hk) * D;
+  }
+  // (Re)fill the window so it holds the pages of tokens [lo, hi]; lo and hi are uniform and
+  // every thread of the workgroup calls this (it synchronises the workgroup when it refills).
+  __device__ __forceinline__ void cover(int lo, int hi) {
+    const int plo = page_no(lo), phi = page_no(hi);
+    if (plo >= base && phi < base + kPageWindow) return;
+    __syncthreads();  // nobody reads the old window any more
+    base = plo;
+    const int cnt = min(kPageWindow, page_no(kv_end - 1) - plo + 1);
+    for (int j = threadIdx.x; j < cnt; j += kThreads) table[j] = indices[page_start + plo + j];
+    __syncthreads();
   }
 };
 
 // tokens (within the wave's 16-token group) carried by this lane in K / V fragments
 __device__ __forceinline__ int k_dma_token(int lane) { return lane & 15; }
-__device__ __forceinline__ int v_dma_token(int lane) { return (lane & 15) ^ ((lane >> 2) & 4); }
+__device__ __forceinline__ int v_dma_token(int lane) { return (lane & 15) ^ v_swz(lane >> 4); }
 
-// Issue the LDS-DMA loads of one KV tile (tokens t0 .. t0+63) into `stage`.  Wave w
-// loads token group w: D/32 K fragments and D/32 V fragments.  pk / pv are the pages of
-// the tokens this lane carries (looked up one tile earlier).
-template <int D>
-__device__ __forceinline__ void issue_tile(unsigned char* stage, const Paging& pgn, int t0, int32_t pk,
-                                           int32_t pv, const uint16_t* K, const uint16_t* V) {
-  constexpr int KB = PF<D>::KB;
-  // the wave index is read as a scalar so the LDS destinations (M0) are formed on the SALU
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint16_t* kp = K + pgn.row<D>(t0 + w * 16 + k_dma_token(lane), pk) + 8 * (lane >> 4);
-  const uint16_t* vp = V + pgn.row<D>(t0 + w * 16 + v_dma_token(lane), pv) + 8 * (lane >> 4);
-#pragma unroll
-  for (int b = 0; b < KB; ++b) {
-    __builtin_amdgcn_global_load_lds(kp + b * 32, (lds_ptr)(stage + (w * KB + b) * PF<D>::FRAG), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vp + b * 32, (lds_ptr)(stage + PF<D>::TILE + (w * KB + b) * PF<D>::FRAG),
-                                     16, 0, 0);
+// pages of the tokens this lane carries in the K / V fragments of the tile starting at t0
+template <class PG>
+__device__ __forceinline__ int32_t k_page(const PG& pgn, int t0) {
+  return pgn.page_of(t0 + (threadIdx.x >> 6) * 16 + k_dma_token(threadIdx.x & 63));
+}
+template <class PG>
+__device__ __forceinline__ int32_t v_page(const PG& pgn, int t0) {
+  return pgn.page_of(t0 + (threadIdx.x >> 6) * 16 + v_dma_token(threadIdx.x & 63));
+}
+
+// KB LDS-DMA loads (global_load_lds_dwordx4) of one wave: load b reads 16 bytes per lane
+// from src + 64 b bytes and writes them lane-linearly to LDS fragment b (1 KB apart) starting
+// at lds.  The instruction offset (64 b) applies to the LDS address as well as the global one,
+// so M0 advances by 1024 - 64 bytes per load.  Written as one asm block so the compiler does not track these loads: every wait for
+// them is explicit (BSR_WAIT_VMCNT before the barrier that publishes a slot), and no read of
+// one slot waits for the loads still filling another.
+template <int KB>
+__device__ __forceinline__ void dma_fragments(const uint16_t* src, const lds_u8* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+  static_assert(KB == 1 || KB == 2 || KB == 4, "one, two or four fragments");
+  uint32_t saved;  // M0 is restored afterwards: the compiler treats it as reserved
+  if constexpr (KB == 1) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(m0)
+        : "memory");
+  } else if constexpr (KB == 2) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_add_u32 m0, m0, 0x3c0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off offset:64\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(m0)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_add_u32 m0, m0, 0x3c0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off offset:64\n\t"
+        "s_add_u32 m0, m0, 0x3c0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off offset:128\n\t"
+        "s_add_u32 m0, m0, 0x3c0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off offset:192\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(m0)
+        : "memory");
   }
 }
 
-__device__ __forceinline__ void tile_pages(const Paging& pgn, int t0, int32_t& pk, int32_t& pv) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  pk = pgn.page_of(t0 + w * 16 + k_dma_token(lane));
-  pv = pgn.page_of(t0 + w * 16 + v_dma_token(lane));
+// LDS-DMA loads of the K (V) half of the 64-token tile at t0 into one array: wave w loads
+// token group w, D/32 fragments; `page` comes from k_page (v_page) one step earlier
+template <int D, class PG>
+__device__ __forceinline__ void issue_k(lds_u8* slot, const PG& pgn, int t0, int32_t page,
+                                        const uint16_t* K) {
+  constexpr int KB = PF<D>::KB;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  dma_fragments<KB>(K + pgn.template row<D>(t0 + w * 16 + k_dma_token(lane), page) + 8 * (lane >> 4),
+                    slot + w * KB * PF<D>::FRAG);
+}
+template <int D, class PG>
+__device__ __forceinline__ void issue_v(lds_u8* slot, const PG& pgn, int t0, int32_t page,
+                                        const uint16_t* V) {
+  constexpr int KB = PF<D>::KB;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  dma_fragments<KB>(V + pgn.template row<D>(t0 + w * 16 + v_dma_token(lane), page) + 8 * (lane >> 4),
+                    slot + w * KB * PF<D>::FRAG);
 }
 
-// The double-buffered tile loop shared by both paths: compute(stage, t0) is called once
-// per 64-token tile while the next tile's DMA is in flight.
-template <int D, typename F>
-__device__ __forceinline__ void tile_loop(const Paging& pgn, int kv_start, int kv_end, unsigned char* lds0,
-                                          unsigned char* lds1, const uint16_t* K, const uint16_t* V, F&& compute) {
+// Empty volatile asm that reads and rewrites its operands: the values must exist at this
+// point of the program, so the code computing them cannot sink below it.
+__device__ __forceinline__ void pin(f32x16& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin(uint32_t (&v)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(v[j]));
+}
+
+// Instruction classes of the scheduling-group builtin, and an interleave of NM matrix
+// instructions with the LDS reads that feed them (AHEAD issued first, then PER after each
+// matrix instruction) and VALU vector-ALU instructions after each, so that independent vector
+// work issues while the matrix core is busy.
+constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgDsRead = 0x100;
+template <int NM, int AHEAD, int PER, int VALU>
+__device__ __forceinline__ void sched_mfma_interleave() {
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, AHEAD, 0);
+#pragma unroll
+  for (int j = 0; j < NM; ++j) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, PER, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgValu, VALU, 0);
+  }
+}
+
+// Wait until at most n vector-memory loads of this wave are in flight (loads complete in
+// order), leaving LDS and export counters alone.  n must be a compile-time constant.
+#define BSR_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// The plain double-buffered tile loop of the smaller shapes: compute(k_slot, v_slot, t0) is
+// called once per 64-token tile while the next tile's DMA is in flight.
+template <int D, class PG, typename F>
+__device__ __forceinline__ void tile_loop(PG& pgn, int kv_start, int kv_end, const Slots<D>& s, const uint16_t* K,
+                                          const uint16_t* V, F&& compute) {
   const int ntiles = (kv_end - kv_start + kTileKV - 1) / kTileKV;
-  int32_t pk, pv;
   __syncthreads();  // LDS free (previous item finished, including its combine)
-  tile_pages(pgn, kv_start, pk, pv);
-  issue_tile<D>(lds0, pgn, kv_start, pk, pv, K, V);
-  tile_pages(pgn, kv_start + kTileKV, pk, pv);
-  __syncthreads();  // waits for this wave's DMA, then for every wave's
+  pgn.base = -kPageWindow;  // nothing staged for this item yet
+  pgn.cover(kv_start, kv_start + 2 * kTileKV - 1);
+  int32_t pk = k_page(pgn, kv_start), pv = v_page(pgn, kv_start);
+  issue_k<D>(s.k0(), pgn, kv_start, pk, K);
+  issue_v<D>(s.v0(), pgn, kv_start, pv, V);
+  pk = k_page(pgn, kv_start + kTileKV);
+  pv = v_page(pgn, kv_start + kTileKV);
+  BSR_WAIT_VMCNT(0);  // this wave's DMA has landed
+  __syncthreads();    // ... and every wave's
   for (int ti = 0; ti < ntiles; ti += 2) {
     const int t0 = kv_start + ti * kTileKV;
+    pgn.cover(t0 + 2 * kTileKV, t0 + 4 * kTileKV - 1);
     if (ti + 1 < ntiles) {
-      issue_tile<D>(lds1, pgn, t0 + kTileKV, pk, pv, K, V);
-      tile_pages(pgn, t0 + 2 * kTileKV, pk, pv);
+      issue_k<D>(s.k1(), pgn, t0 + kTileKV, pk, K);
+      issue_v<D>(s.v1(), pgn, t0 + kTileKV, pv, V);
+      pk = k_page(pgn, t0 + 2 * kTileKV);
+      pv = v_page(pgn, t0 + 2 * kTileKV);
     }
-    compute(static_cast<const unsigned char*>(lds0), t0);
+    compute(static_cast<const lds_u8*>(s.k0()), static_cast<const lds_u8*>(s.v0()), t0);
+    BSR_WAIT_VMCNT(0);
     __syncthreads();
     if (ti + 1 < ntiles) {
       if (ti + 2 < ntiles) {
-        issue_tile<D>(lds0, pgn, t0 + 2 * kTileKV, pk, pv, K, V);
-        tile_pages(pgn, t0 + 3 * kTileKV, pk, pv);
+        issue_k<D>(s.k0(), pgn, t0 + 2 * kTileKV, pk, K);
+        issue_v<D>(s.v0(), pgn, t0 + 2 * kTileKV, pv, V);
+        pk = k_page(pgn, t0 + 3 * kTileKV);
+        pv = v_page(pgn, t0 + 3 * kTileKV);
       }
-      compute(static_cast<const unsigned char*>(lds1), t0 + kTileKV);
+      compute(static_cast<const lds_u8*>(s.k1()), static_cast<const lds_u8*>(s.v1()), t0 + kTileKV);
+      BSR_WAIT_VMCNT(0);
       __syncthreads();
     }
   }
@@ -213,27 +376,29 @@ __device__ __forceinline__ float raise_reference(float& m, float mx_scaled, bool
 }
 
 // ---------------------------------------------------------------------------------
-// Large query tiles: 32-row blocks on v_mfma_f32_32x32x16_bf16.
-// NT32: 32-token blocks of a tile per wave (2: the whole tile, 1: half, the other half
-// goes to a second wave sharing the row block).
+// Large query tiles: 32-row blocks on v_mfma_f32_32x32x16_bf16; every wave takes one
+// 32-token block per tile.
+// PIPE: more than 64 rows, one row block per wave, software-pipelined over 32-token tiles.
+// Otherwise (33-64 rows): two row blocks, each shared by two waves that take the two
+// 32-token halves of every 64-token tile of the plain loop.
 // ---------------------------------------------------------------------------------
-template <int D, int NT32>
+template <int D, bool PIPE, bool POW2>
 __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& item, const ReqRec& rq, int hk,
-                                               unsigned char* lds0, unsigned char* lds1) {
-  constexpr int KB = PF<D>::KB, FRAG = PF<D>::FRAG, TILE = PF<D>::TILE;
+                                               const Slots<D>& sl) {
+  constexpr int KB = PF<D>::KB, FRAG = PF<D>::FRAG;
   constexpr int KS16 = D / 16;  // 16-deep k-steps of the score product
-  constexpr int N_KS = 2 / NT32;
+  constexpr int N_KS = PIPE ? 1 : 2;
   constexpr int N_RG = kWaves / N_KS;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r32 = lane & 31, h = lane >> 5;
-  const int rg = wave % N_RG, ks = wave / N_RG;
+  const int rg = wave % N_RG, ks = wave / N_RG;  // row block; 32-token block within a tile
   const int nrows = item.row_end - item.row_start;
   const float c = a.sm_scale * kLog2e;
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
   const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
   const int kv_end = item.kv_end;
-  const Paging pgn{a.indices, rq.page_start, a.P, a.p_shift, a.Hk, hk, kv_end};
+  Paging<POW2> pgn{a.indices, sl.table(), rq.page_start, a.P, a.p_shift, a.Hk, hk, kv_end, -kPageWindow};
 
   // this lane's query row: block rg, row r32
   const int r = item.row_start + rg * 32 + r32;
@@ -254,7 +419,7 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
   int min_lim = kv_end;  // tiles ending before the smallest visible end need no mask
   if (a.causal) min_lim = min(kv_end, rq.kv_len - rq.q_len + item.row_start / a.g + 1);
 
-  float m = kNegInf, l = 0.f;
+  float m = kNegInf, l = 0.f, corr = 1.f;
   f32x16 oacc[KB];
 #pragma unroll
   for (int b = 0; b < KB; ++b)
@@ -269,81 +434,278 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
   const int v_lo = v_chunk(4 * (vG >> 1) + ve, 4 * (vG & 1) + vq);
   const int v_hi = v_chunk(4 * (vG >> 1) + ve + 8, 4 * (vG & 1) + vq);
 
-  auto compute = [&](const unsigned char* cur, int t0) {
-    f32x16 S[NT32];
+  // S^T of this wave's 32-token block of the tile staged at `kt`
+  auto qk = [&](const lds_u8* kt, f32x16& S) {
 #pragma unroll
-    for (int b = 0; b < NT32; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) S[b][i] = 0.f;
+    for (int i = 0; i < 16; ++i) S[i] = 0.f;
+    const lds_u8* kp = kt + (2 * ks + (r32 >> 4)) * KB * FRAG + k_pos;
 #pragma unroll
     for (int k = 0; k < KS16; ++k) {
+      const bf16x8 ka = *reinterpret_cast<lds_bf16x8*>(kp + (k >> 1) * FRAG + 512 * (k & 1));
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[k], S, 0, 0, 0);
+    }
+  };
+  // causal mask of the block whose tile starts at t0 (only where it reaches past the first
+  // row's limit)
+  auto mask = [&](f32x16& S, int t0) {
+    if (t0 + 32 * (ks + 1) > min_lim) {
 #pragma unroll
-      for (int b = 0; b < NT32; ++b) {
-        const int tb = ks * NT32 + b;  // 32-token block of the tile
-        const int grp = 2 * tb + (r32 >> 4);
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(cur + (grp * KB + (k >> 1)) * FRAG + k_pos + 512 * (k & 1));
-        S[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[k], S[b], 0, 0, 0);
+      for (int i = 0; i < 16; ++i) {
+        const int tok = t0 + 32 * ks + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (tok >= lim) S[i] = kNegInf;
       }
     }
-    if (t0 + kTileKV > min_lim) {
-#pragma unroll
-      for (int b = 0; b < NT32; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int tok = t0 + 32 * (ks * NT32 + b) + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (tok >= lim) S[b][i] = kNegInf;
-        }
-    }
+  };
+  // online softmax of one block's scores: update the reference m (raised only past the
+  // margin; corr is this row's rescale factor, 1 when it stays) and l, write P as bf16 pairs;
+  // returns whether any row of the wave raised its reference
+  auto softmax = [&](const f32x16& S, uint32_t (&pk)[8]) -> bool {
     float mx = kNegInf;
 #pragma unroll
-    for (int b = 0; b < NT32; ++b)
+    for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(S[i], S[i + 1]));
+    const float mxs = pair_max(mx) * c;
+    const bool raise = mxs > m + kRescaleMargin;
+    const bool any = __ballot(raise) != 0;
+    const float mnew = raise ? mxs : m;
+    corr = raise ? fast_exp2(m - mnew) : 1.f;  // m = -inf gives 0
+    m = mnew;
+    const float muse = m == kNegInf ? 0.f : m;
+    float lsum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(S[b][i], S[b][i + 1]));
-    mx = pair_max(mx);
-    bool any;
-    const float corr = raise_reference(m, mx * c, any);
+    for (int i = 0; i < 16; i += 2) {
+      const float p0 = fast_exp2(__builtin_fmaf(S[i], c, -muse));
+      const float p1 = fast_exp2(__builtin_fmaf(S[i + 1], c, -muse));
+      lsum += p0 + p1;
+      pk[i >> 1] = cvt_pk_bf16(p0, p1);
+    }
+    l = l * corr + lsum;
+    return any;
+  };
+  auto rescale = [&](bool any) {
     if (any) {
-      l *= corr;
 #pragma unroll
       for (int b = 0; b < KB; ++b) oacc[b] *= corr;
     }
-    const float muse = m == kNegInf ? 0.f : m;
-    uint32_t pk[NT32][8];
-    float lsum = 0.f;
+  };
+  // O^T += V^T P^T over this wave's block of the tile staged at `vt`, one 16-token k-block
+  // at a time
+  auto pv = [&](const lds_u8* vt, const uint32_t (&pk)[8]) {
 #pragma unroll
-    for (int b = 0; b < NT32; ++b)
+    for (int half = 0; half < 2; ++half) {
+      const bf16x8 pb = __builtin_bit_cast(
+          bf16x8, u32x4{pk[4 * half], pk[4 * half + 1], pk[4 * half + 2], pk[4 * half + 3]});
+      const lds_u8* vf = vt + (2 * ks + half) * KB * FRAG;
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(S[b][i], c, -muse));
-        const float p1 = fast_exp2(__builtin_fmaf(S[b][i + 1], c, -muse));
-        lsum += p0 + p1;
-        pk[b][i >> 1] = cvt_pk_bf16(p0, p1);
+      for (int cb = 0; cb < KB; ++cb) {
+        const bf16x8 va = cat(tr_read(vf + cb * FRAG + v_lo), tr_read(vf + cb * FRAG + v_hi));
+        oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[cb], 0, 0, 0);
       }
-    l += lsum;
-    // O^T += V^T P^T, one 16-token k-block kb at a time
+    }
+  };
+
+  // The two phases of a pipelined step, in a fixed instruction order (scheduling barriers
+  // between the groups keep the compiler from regrouping them):
+  // phase A: the KS16 score MFMAs of the next tile, each followed by the LDS read of the K
+  // fragment two k-steps ahead and a slice of this tile's softmax (first the row maximum and
+  // the reference update, then the exponentials, a few pairs per slice);
+  auto phase_a = [&](const lds_u8* kt, f32x16& Snext, const f32x16& Scur, uint32_t (&pk)[8]) -> bool {
+    const lds_u8* kp = kt + (2 * ks + (r32 >> 4)) * KB * FRAG + k_pos;
+    auto kread = [&](int k) { return *reinterpret_cast<lds_bf16x8*>(kp + (k >> 1) * FRAG + 512 * (k & 1)); };
+    bf16x8 kr[KS16];
+    kr[0] = kread(0);
+    kr[1] = kread(1);
+    float mx = kNegInf, muse = 0.f, lsum = 0.f;
+    bool any = false;
 #pragma unroll
-    for (int b = 0; b < NT32; ++b)
+    for (int g = 0; g < KS16; ++g) {
+      __builtin_amdgcn_sched_barrier(0);
+      Snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[g], qb[g], g == 0 ? f32x16{} : Snext, 0, 0, 0);
+      if (g + 2 < KS16) kr[g + 2] = kread(g + 2);
+      if (g == 0) {
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int grp = 2 * (ks * NT32 + b) + half;  // 16-token group of the tile
-        const bf16x8 pb = __builtin_bit_cast(
-            bf16x8, u32x4{pk[b][4 * half], pk[b][4 * half + 1], pk[b][4 * half + 2], pk[b][4 * half + 3]});
-        const unsigned char* vf = cur + TILE + grp * KB * FRAG;
+        for (int i = 0; i < 8; i += 2) mx = fmaxf(mx, fmaxf(Scur[i], Scur[i + 1]));
+      } else if (g == 1) {
 #pragma unroll
-        for (int cb = 0; cb < KB; ++cb) {
-          const bf16x8 va = cat(tr_read(vf + cb * FRAG + v_lo), tr_read(vf + cb * FRAG + v_hi));
-          oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[cb], 0, 0, 0);
+        for (int i = 8; i < 16; i += 2) mx = fmaxf(mx, fmaxf(Scur[i], Scur[i + 1]));
+        const float mxs = pair_max(mx) * c;
+        const bool raise = mxs > m + kRescaleMargin;
+        any = __ballot(raise) != 0;
+        const float mnew = raise ? mxs : m;
+        corr = raise ? fast_exp2(m - mnew) : 1.f;  // m = -inf gives 0
+        m = mnew;
+        muse = m == kNegInf ? 0.f : m;
+      } else {
+        // pairs whose slice is g: pair q goes to slice 2 + q (KS16 - 2) / 8
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (2 + q * (KS16 - 2) / 8 != g) continue;
+          const float p0 = fast_exp2(__builtin_fmaf(Scur[2 * q], c, -muse));
+          const float p1 = fast_exp2(__builtin_fmaf(Scur[2 * q + 1], c, -muse));
+          lsum += p0 + p1;
+          pk[q] = cvt_pk_bf16(p0, p1);
         }
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    l = l * corr + lsum;
+    return any;
   };
-  tile_loop<D>(pgn, item.kv_start, kv_end, lds0, lds1, K, V, compute);
+  // phase B: P.V of this tile, the two transposing reads of each MFMA issued two MFMAs ahead
+  auto phase_b = [&](const lds_u8* vt, const uint32_t (&pk)[8]) {
+    constexpr int NM = 2 * KB;
+    auto vread = [&](int m2) {  // operand of MFMA m2 = (k-block m2 / KB, column block m2 % KB)
+      const lds_u8* vf = vt + (2 * ks + m2 / KB) * KB * FRAG + (m2 % KB) * FRAG;
+      return cat(tr_read(vf + v_lo), tr_read(vf + v_hi));
+    };
+    bf16x8 va[NM];
+    va[0] = vread(0);
+    va[1] = vread(1);
+#pragma unroll
+    for (int m2 = 0; m2 < NM; ++m2) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int half = m2 / KB, cb = m2 % KB;
+      const bf16x8 pb = __builtin_bit_cast(
+          bf16x8, u32x4{pk[4 * half], pk[4 * half + 1], pk[4 * half + 2], pk[4 * half + 3]});
+      oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[m2], pb, oacc[cb], 0, 0, 0);
+      if (m2 + 2 < NM) va[m2 + 2] = vread(m2 + 2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if constexpr (!PIPE) {
+    tile_loop<D>(pgn, item.kv_start, kv_end, sl, K, V, [&](const lds_u8* kt, const lds_u8* vt, int t0) {
+      f32x16 S;
+      uint32_t pk[8];
+      qk(kt, S);
+      mask(S, t0);
+      rescale(softmax(S, pk));
+      pv(vt, pk);
+    });
+  } else {
+    // Software pipeline over 32-token tiles j (tokens T(j) .. T(j)+31), K(j) and V(j) in
+    // slot j % 4 of their 4-slot rings (8 KB each for D = 128).  Step j:
+    //   [A] wait for K(j+1), barrier, DMA V(j+3) into V(j-1)'s slot; scores of tile j+1 on
+    //       the matrix cores while the softmax of tile j runs on the vector ALUs;
+    //   [B] wait for V(j), barrier, DMA K(j+5) into K(j+1)'s slot; P.V of tile j; mask of
+    //       tile j+1.
+    // Each load is issued 3.5 steps before its use.  The DMA loads are the only vector-memory
+    // loads in flight (page ids come from the LDS window); per barrier every wave issues one
+    // batch of D/64 of them, so at each wait the batches younger than the one needed are the
+    // six issued at the previous six barriers (fewer near the end, where some are skipped).
+    constexpr int NF = KB / 2;            // K (or V) fragments each wave loads per tile
+    constexpr int HALF = 2 * KB * FRAG;   // bytes of K (or V) of one 32-token tile
+    const int kv0 = item.kv_start;
+    const int n = (kv_end - kv0 + 31) / 32;
+    auto T = [&](int j) { return kv0 + 32 * j; };
+    auto k_slot = [&](int j) { return sl.k0() + ((j >> 1) & 1) * PF<D>::SLOT + (j & 1) * HALF; };
+    auto v_slot = [&](int j) { return sl.v0() + ((j >> 1) & 1) * PF<D>::SLOT + (j & 1) * HALF; };
+    // wave w loads fragments w*NF .. w*NF+NF-1 (token group f / KB, column group f % KB)
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    const int f0 = wu * NF, tg = f0 / KB, cg = f0 % KB;
+    auto page_k = [&](int j) { return pgn.page_of(T(j) + 16 * tg + k_dma_token(lane)); };
+    auto page_v = [&](int j) { return pgn.page_of(T(j) + 16 * tg + v_dma_token(lane)); };
+    auto dma_k = [&](int j, int32_t page) {
+      dma_fragments<NF>(K + pgn.template row<D>(T(j) + 16 * tg + k_dma_token(lane), page) + 8 * (lane >> 4) + 32 * cg,
+                        k_slot(j) + f0 * FRAG);
+    };
+    auto dma_v = [&](int j, int32_t page) {
+      dma_fragments<NF>(V + pgn.template row<D>(T(j) + 16 * tg + v_dma_token(lane), page) + 8 * (lane >> 4) + 32 * cg,
+                        v_slot(j) + f0 * FRAG);
+    };
+    auto wait_batches = [&](int nb) {  // at most nb batches of NF loads in flight
+      switch (nb) {
+        case 6: BSR_WAIT_VMCNT(6 * NF); break;
+        case 5: BSR_WAIT_VMCNT(5 * NF); break;
+        case 4: BSR_WAIT_VMCNT(4 * NF); break;
+        case 3: BSR_WAIT_VMCNT(3 * NF); break;
+        case 2: BSR_WAIT_VMCNT(2 * NF); break;
+        case 1: BSR_WAIT_VMCNT(NF); break;
+        default: BSR_WAIT_VMCNT(0); break;
+      }
+    };
+    f32x16 Sa, Sb;
+    uint32_t pk[8];
+    __syncthreads();  // LDS free (previous item finished)
+    pgn.cover(T(0), T(6) - 1);
+    {
+      const int32_t k0 = page_k(0), k1 = page_k(1), k2 = page_k(2), k3 = page_k(3);
+      const int32_t v0 = page_v(0), v1 = page_v(1), v2 = page_v(2);
+      dma_k(0, k0);
+      if (n > 1) dma_k(1, k1);
+      if (n > 2) dma_k(2, k2);
+      if (n > 3) dma_k(3, k3);
+      dma_v(0, v0);
+      if (n > 1) dma_v(1, v1);
+      if (n > 2) dma_v(2, v2);
+    }
+    int32_t nk = page_k(4), nv = page_v(3);
+    BSR_WAIT_VMCNT(0);
+    __syncthreads();  // K(0..3), V(0..2) staged
+    qk(k_slot(0), Sa);
+    mask(Sa, T(0));
+    __syncthreads();  // every wave has read K(0)
+    {
+      const int32_t nk2 = page_k(5);
+      if (n > 4) dma_k(4, nk);
+      nk = nk2;
+    }
+    // FULL: every load of the step is issued (its tiles all exist), so the step is
+    // straight-line code with fixed wait counts
+    auto step = [&](auto full, int j, f32x16& Scur, f32x16& Snext) {
+      constexpr bool FULL = decltype(full)::value;
+      pgn.cover(T(j + 4), T(j + 7) - 1);  // this step's lookups: V(j+4), K(j+6)
+      // [A]
+      if (FULL) wait_batches(6);
+      else wait_batches(1 + (j + 2 < n) + (j + 1 < n) + (j + 3 < n) + (j + 2 < n) + (j + 4 < n));
+      __builtin_amdgcn_s_barrier();
+      {
+        const int32_t nv2 = page_v(j + 4);
+        if (FULL || j + 3 < n) dma_v(j + 3, nv);
+        nv = nv2;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // scores of the next tile on the matrix cores, softmax of this one in their shadow
+      // (past the last tile this reads a stale slot; the scores are then unused)
+      const bool any = phase_a(k_slot(j + 1), Snext, Scur, pk);
+      // keep both inside this phase: without these the compiler sinks P (and the scores)
+      // next to their first use after the rescale branch
+      pin(Snext);
+      pin(pk);
+      __builtin_amdgcn_sched_barrier(0);
+      // [B]
+      if (FULL) wait_batches(6);
+      else wait_batches((j + 2 < n) + (j + 1 < n) + (j + 3 < n) + (j + 2 < n) + (j + 4 < n) + (j + 3 < n));
+      __builtin_amdgcn_s_barrier();
+      {
+        const int32_t nk2 = page_k(j + 6);
+        if (FULL || j + 5 < n) dma_k(j + 5, nk);
+        nk = nk2;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      rescale(any);
+      phase_b(v_slot(j), pk);
+      if (FULL || j + 1 < n) mask(Snext, T(j + 1));
+    };
+    using Full = std::integral_constant<bool, true>;
+    using Tail = std::integral_constant<bool, false>;
+    int j = 0;
+    for (; j + 6 < n; j += 2) {
+      step(Full{}, j, Sa, Sb);
+      step(Full{}, j + 1, Sb, Sa);
+    }
+    for (; j < n; j += 2) {
+      step(Tail{}, j, Sa, Sb);
+      if (j + 1 >= n) break;
+      step(Tail{}, j + 1, Sb, Sa);
+    }
+  }
 
   l = pair_sum(l);  // the two halves of a row held different tokens
 
   if constexpr (N_KS > 1) {
     // combine the two waves that split each row block's tokens: the second one publishes
-    // its state, the first one folds it in
-    float* comb = reinterpret_cast<float*>(rg == 0 ? lds0 : lds1);
+    // its state, the first one folds it in (the loop ended with a barrier: LDS is free)
+    lds_f32* comb = reinterpret_cast<lds_f32*>(rg == 0 ? sl.v0() : sl.v1());
     if (ks == 1 && rb_on) {
 #pragma unroll
       for (int b = 0; b < KB; ++b)
@@ -404,10 +766,10 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
 // Small query tiles (<= 32 rows): 16-row blocks on v_mfma_f32_16x16x32_bf16.
 // NT: 16-token blocks of a tile per wave (2: two waves per row block, 1: four).
 // ---------------------------------------------------------------------------------
-template <int D, int NT>
+template <int D, int NT, bool POW2>
 __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& item, const ReqRec& rq, int hk,
-                                               unsigned char* lds0, unsigned char* lds1) {
-  constexpr int KB = PF<D>::KB, DB = D / 16, FRAG = PF<D>::FRAG, TILE = PF<D>::TILE;
+                                               const Slots<D>& sl) {
+  constexpr int KB = PF<D>::KB, DB = D / 16, FRAG = PF<D>::FRAG;
   constexpr int N_KS = 4 / NT;  // waves sharing a row block
   constexpr int N_RG = kWaves / N_KS;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -419,7 +781,7 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
   const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
   const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
   const int kv_end = item.kv_end;
-  const Paging pgn{a.indices, rq.page_start, a.P, a.p_shift, a.Hk, hk, kv_end};
+  Paging<POW2> pgn{a.indices, sl.table(), rq.page_start, a.P, a.p_shift, a.Hk, hk, kv_end, -kPageWindow};
 
   const int r = item.row_start + rg * 16 + n;
   const bool rb_on = rg * 16 < nrows;
@@ -449,7 +811,7 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
   const int vG = lane >> 4, ve = (lane >> 2) & 3, vq = lane & 3;
   const int v_even = v_chunk(4 * vG + ve, vq), v_odd = v_chunk(4 * vG + ve, 4 + vq);
 
-  auto compute = [&](const unsigned char* cur, int t0) {
+  auto compute = [&](const lds_u8* kt, const lds_u8* vt, int t0) {
     f32x4 S[NT];
 #pragma unroll
     for (int b = 0; b < NT; ++b) S[b] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -458,7 +820,7 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
       const int tb = ks * NT + b;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(cur + (tb * KB + kb) * FRAG + lane * 16);
+        const bf16x8 ka = *reinterpret_cast<lds_bf16x8*>(kt + (tb * KB + kb) * FRAG + lane * 16);
         S[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[kb], S[b], 0, 0, 0);
       }
     }
@@ -505,8 +867,8 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
         const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[b][0], pk[b][1], pk[b + 1][0], pk[b + 1][1]});
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int off = TILE + (db >> 1) * FRAG + ((db & 1) ? v_odd : v_even);
-          const bf16x8 vab = cat(tr_read(cur + tba * KB * FRAG + off), tr_read(cur + tbb * KB * FRAG + off));
+          const int off = (db >> 1) * FRAG + ((db & 1) ? v_odd : v_even);
+          const bf16x8 vab = cat(tr_read(vt + tba * KB * FRAG + off), tr_read(vt + tbb * KB * FRAG + off));
           oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vab, pb, oacc[db], 0, 0, 0);
         }
       }
@@ -515,12 +877,12 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
       const s16x4 pb = __builtin_bit_cast(s16x4, u32x2{pk[0][0], pk[0][1]});
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int off = TILE + (db >> 1) * FRAG + ((db & 1) ? v_odd : v_even);
-        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(tr_read(cur + tb * KB * FRAG + off), pb, oacc[db], 0, 0, 0);
+        const int off = (db >> 1) * FRAG + ((db & 1) ? v_odd : v_even);
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(tr_read(vt + tb * KB * FRAG + off), pb, oacc[db], 0, 0, 0);
       }
     }
   };
-  tile_loop<D>(pgn, item.kv_start, kv_end, lds0, lds1, K, V, compute);
+  tile_loop<D>(pgn, item.kv_start, kv_end, sl, K, V, compute);
 
   l = pair16_sum(l);
   l = pair_sum(l);
@@ -528,10 +890,10 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
   {
     // combine the waves that split this row block's tokens; waves 0-1 use the first
     // stage's array, waves 2-3 the second one's
-    auto comb_of = [&](int wv) -> float* {
-      return reinterpret_cast<float*>((wv < 2 ? lds0 : lds1) + (wv & 1) * PF<D>::COMB16);
+    auto comb_of = [&](int wv) -> lds_f32* {
+      return reinterpret_cast<lds_f32*>((wv < 2 ? sl.v0() : sl.v1()) + (wv & 1) * PF<D>::COMB16);
     };
-    float* mine = comb_of(wave);
+    lds_f32* mine = comb_of(wave);
     if (rb_on) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -551,7 +913,7 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
       float lt = 0.f, wgt[N_KS];
 #pragma unroll
       for (int o = 0; o < N_KS; ++o) {
-        const float* src = comb_of(rg + o * N_RG) + n * (D + 2);
+        const lds_f32* src = comb_of(rg + o * N_RG) + n * (D + 2);
         wgt[o] = fast_exp2(src[D] - muse);
         lt += wgt[o] * src[D + 1];
       }
@@ -594,41 +956,47 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
 
 }  // namespace
 
-template <int D>
+template <int D, bool POW2>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_bf16_kernel(RunArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds0[PF<D>::STAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char lds1[PF<D>::STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[Slots<D>::BYTES];
+  const Slots<D> sl{(lds_u8*)lds};
   // XCD-aware order: the dispatcher deals consecutive workgroups round-robin to the 8 XCDs,
   // so numbering them KV-head-minor puts every worker of one KV head on the same XCD (for
   // H_kv dividing 8), and the K/V tiles its query tiles share stay in that XCD's L2.
   const int bid = blockIdx.x + gridDim.x * blockIdx.y;
-  const int hk = bid % a.Hk, w = bid / a.Hk;
-  for (int it = a.qptr[w]; it < a.qptr[w + 1]; ++it) {
-    const ItemRec item = a.items[it];
-    const ReqRec rq = a.req[item.req];
+  // (the division runs on the vector ALU; the results are uniform, so read them back as scalars)
+  const int hk = __builtin_amdgcn_readfirstlane(bid % a.Hk), w = __builtin_amdgcn_readfirstlane(bid / a.Hk);
+  const int it_end = uniform_load(a.qptr + w + 1);
+  for (int it = uniform_load(a.qptr + w); it < it_end; ++it) {
+    const ItemRec item = uniform_load(a.items + it);
+    const ReqRec rq = uniform_load(a.req + item.req);
     const int rows = item.row_end - item.row_start;
-    if (rows > 64) prefill_item32<D, 2>(a, item, rq, hk, lds0, lds1);       // 3-4 blocks of 32 rows
-    else if (rows > 32) prefill_item32<D, 1>(a, item, rq, hk, lds0, lds1);  // 2 blocks, tokens split
-    else if (rows > 16) prefill_item16<D, 2>(a, item, rq, hk, lds0, lds1);  // 2 blocks of 16 rows
-    else prefill_item16<D, 1>(a, item, rq, hk, lds0, lds1);                 // 1 block, tokens split 4 ways
+    if (rows > 64) prefill_item32<D, true, POW2>(a, item, rq, hk, sl);        // 3-4 blocks of 32 rows, pipelined
+    else if (rows > 32) prefill_item32<D, false, POW2>(a, item, rq, hk, sl);  // 2 blocks, tokens split
+    else if (rows > 16) prefill_item16<D, 2, POW2>(a, item, rq, hk, sl);  // 2 blocks of 16 rows
+    else prefill_item16<D, 1, POW2>(a, item, rq, hk, sl);                 // 1 block, tokens split 4 ways
   }
 }
 
 bool prefill_bf16_supported(int d, int Tq) { return (d == 64 || d == 128) && Tq % 16 == 0 && Tq <= 128; }
 
 int prefill_bf16_blocks_per_cu(int d) {
+  // both page-size variants use the same resources; ask for the power-of-two one
   int nb = 1;
   hipError_t e = hipErrorInvalidValue;
-  if (d == 64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_prefill_bf16_kernel<64>, kThreads, 0);
-  if (d == 128) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_prefill_bf16_kernel<128>, kThreads, 0);
+  if (d == 64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_prefill_bf16_kernel<64, true>, kThreads, 0);
+  if (d == 128) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_prefill_bf16_kernel<128, true>, kThreads, 0);
   return (e == hipSuccess && nb > 0) ? nb : 1;
 }
 
 hipError_t launch_prefill_bf16(const RunArgs& a, hipStream_t s) {
   dim3 grid(a.C, a.Hk), block(kThreads);
-  if (a.d == 64) hipLaunchKernelGGL(attn_prefill_bf16_kernel<64>, grid, block, 0, s, a);
-  else if (a.d == 128) hipLaunchKernelGGL(attn_prefill_bf16_kernel<128>, grid, block, 0, s, a);
+  const bool pow2 = a.p_shift >= 0;
+  if (a.d == 64 && pow2) hipLaunchKernelGGL((attn_prefill_bf16_kernel<64, true>), grid, block, 0, s, a);
+  else if (a.d == 64) hipLaunchKernelGGL((attn_prefill_bf16_kernel<64, false>), grid, block, 0, s, a);
+  else if (a.d == 128 && pow2) hipLaunchKernelGGL((attn_prefill_bf16_kernel<128, true>), grid, block, 0, s, a);
+  else if (a.d == 128) hipLaunchKernelGGL((attn_prefill_bf16_kernel<128, false>), grid, block, 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
