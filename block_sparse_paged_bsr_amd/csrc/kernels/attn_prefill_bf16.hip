@@ -108,6 +108,13 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + the two bf16 values of a packed pair (v_dot2_f32_bf16 against (1, 1)): the row sum
+// adds the same rounded weights that P.V multiplies, one instruction per pair
+__device__ __forceinline__ float sum_pair(uint32_t pair, float acc) {
+  const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
+}
+
 // max / sum of the values held by lanes l and l ^ 32, through v_permlane32_swap (no LDS
 // round trip).  The swap exchanges the upper half of its first operand with the lower half of
 // its second, so with both operands x every lane ends up holding x[l] and x[l ^ 32].
@@ -188,7 +195,9 @@ struct Paging {
   __device__ __forceinline__ int64_t row(int t, int32_t page) const {
     const int tc = min(t, kv_end - 1);
     const int off = POW2 ? (tc & (P - 1)) : tc - (tc / P) * P;
-    return ((int64_t(page) * P + off) * Hk + hk) * D;
+    // page * (P Hk D) + (off Hk + hk) D as one unsigned 32x32 -> 64-bit multiply-add (page
+    // ids are non-negative; the planner keeps P Hk D below 2^31)
+    return int64_t(uint64_t(uint32_t(page)) * uint32_t(P * Hk * D) + uint32_t((off * Hk + hk) * D));
   }
   // (Re)fill the window so it holds the pages of tokens [lo, hi]; lo and hi are uniform and
   // every thread of the workgroup calls this (it synchronises the workgroup when it refills).
@@ -418,6 +427,7 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
   }
   int min_lim = kv_end;  // tiles ending before the smallest visible end need no mask
   if (a.causal) min_lim = min(kv_end, rq.kv_len - rq.q_len + item.row_start / a.g + 1);
+  min_lim = __builtin_amdgcn_readfirstlane(min_lim);  // uniform: the mask test is a scalar branch
 
   float m = kNegInf, l = 0.f, corr = 1.f;
   f32x16 oacc[KB];
@@ -475,8 +485,8 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
     for (int i = 0; i < 16; i += 2) {
       const float p0 = fast_exp2(__builtin_fmaf(S[i], c, -muse));
       const float p1 = fast_exp2(__builtin_fmaf(S[i + 1], c, -muse));
-      lsum += p0 + p1;
       pk[i >> 1] = cvt_pk_bf16(p0, p1);
+      lsum = sum_pair(pk[i >> 1], lsum);
     }
     l = l * corr + lsum;
     return any;
@@ -541,8 +551,8 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
           if (2 + q * (KS16 - 2) / 8 != g) continue;
           const float p0 = fast_exp2(__builtin_fmaf(Scur[2 * q], c, -muse));
           const float p1 = fast_exp2(__builtin_fmaf(Scur[2 * q + 1], c, -muse));
-          lsum += p0 + p1;
           pk[q] = cvt_pk_bf16(p0, p1);
+          lsum = sum_pair(pk[q], lsum);
         }
       }
     }
@@ -852,12 +862,10 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
     for (int b = 0; b < NT; ++b) {
       float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = fast_exp2(__builtin_fmaf(S[b][i], c, -muse));
-        lsum += p[i];
-      }
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(S[b][i], c, -muse));
       pk[b][0] = cvt_pk_bf16(p[0], p[1]);
       pk[b][1] = cvt_pk_bf16(p[2], p[3]);
+      lsum = sum_pair(pk[b][1], sum_pair(pk[b][0], lsum));
     }
     l += lsum;
     if constexpr (NT >= 2) {

@@ -45,6 +45,8 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
     return fail("num_qo_heads must be a multiple of num_kv_heads");
   if (desc->head_dim < 1) return fail("head_dim must be >= 1");
   if (desc->page_size < 1) return fail("page_size must be >= 1");
+  if (int64_t(desc->page_size) * desc->num_kv_heads * desc->head_dim >= (int64_t(1) << 31))
+    return fail("page_size * num_kv_heads * head_dim must be below 2^31 (elements of one page)");
   if (desc->num_workers < 0) return fail("num_workers must be >= 0");
   if (desc->tile_q < 0 || (desc->tile_q > 0 && desc->tile_q % 16 != 0) || desc->tile_q > 128)
     return fail("tile_q must be 0 or a multiple of 16 up to 128");

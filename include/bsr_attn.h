@@ -71,7 +71,8 @@ typedef struct bsr_plan_desc {
   int32_t num_qo_heads;         /* H_qo, a multiple of H_kv */
   int32_t num_kv_heads;         /* H_kv >= 1 */
   int32_t head_dim;             /* d */
-  int32_t page_size;            /* P >= 1 (tokens per page; 1 = vector sparse) */
+  int32_t page_size;            /* P >= 1 (tokens per page; 1 = vector sparse);
+                                   P * num_kv_heads * head_dim < 2^31 */
   int32_t causal;               /* 1: key k visible to query q iff k <= q + l_kv - l_qo */
   int32_t num_workers;          /* C: persistent workers; 0 => default for 256 CUs */
   int32_t tile_q;               /* packed query rows per tile; 0 => tile rule */
