@@ -62,6 +62,7 @@ constexpr int kTileKV = 64;  // tokens per staged KV tile
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kRescaleMargin = 8.f;  // log2 units
+constexpr float kMFloor = -1e30f;      // initial reference of the 32-row shapes (log2 units)
 constexpr int kPageWindow = 2048;      // page ids staged in LDS per workgroup
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -175,6 +176,11 @@ __device__ __forceinline__ T uniform_load(const T* p) {
   return v;
 }
 
+// Page-size classes the kernels are compiled for: any size (division), a power of two (shift
+// and mask), or a power of two that divides 32 (then a token's offset inside its page is the
+// same in every 32-token tile of an item, and its page number advances by 32 / P per tile).
+constexpr int kPageAny = 0, kPagePow2 = 1, kPageDiv32 = 2;
+
 // Token -> page lookups (eq. 7 of "FlashInfer: Making Attention Fit the Serving Workload").
 // A window of up to kPageWindow entries of the request's page list is staged in LDS, so the
 // lookups inside the tile loops are LDS reads and the only vector-memory loads in flight there
@@ -229,13 +235,16 @@ __device__ __forceinline__ int32_t v_page(const PG& pgn, int t0) {
 // KB LDS-DMA loads (global_load_lds_dwordx4) of one wave: load b reads 16 bytes per lane
 // from src + 64 b bytes and writes them lane-linearly to LDS fragment b (1 KB apart) starting
 // at lds.  The instruction offset (64 b) applies to the LDS address as well as the global one,
-// so M0 advances by 1024 - 64 bytes per load.  Written as one asm block so the compiler does not track these loads: every wait for
-// them is explicit (BSR_WAIT_VMCNT before the barrier that publishes a slot), and no read of
-// one slot waits for the loads still filling another.
+// so M0 holds lds + b (1024 - 64) for load b.  The M0 values are computed outside the asm and
+// set with s_mov_b32, which leaves SCC alone (the asm also declares SCC clobbered, so no
+// compare may live across it).  Written as one asm block so the compiler does not track these
+// loads: every wait for them is explicit (BSR_WAIT_VMCNT before the barrier that publishes a
+// slot), and no read of one slot waits for the loads still filling another.
 template <int KB>
 __device__ __forceinline__ void dma_fragments(const uint16_t* src, const lds_u8* lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
   static_assert(KB == 1 || KB == 2 || KB == 4, "one, two or four fragments");
+  constexpr uint32_t kStep = 1024 - 64;
   uint32_t saved;  // M0 is restored afterwards: the compiler treats it as reserved
   if constexpr (KB == 1) {
     asm volatile(
@@ -246,39 +255,39 @@ __device__ __forceinline__ void dma_fragments(const uint16_t* src, const lds_u8*
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
         : "v"(src), "s"(m0)
-        : "memory");
+        : "memory", "scc");
   } else if constexpr (KB == 2) {
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, off\n\t"
-        "s_add_u32 m0, m0, 0x3c0\n\t"
+        "s_mov_b32 m0, %3\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, off offset:64\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "v"(src), "s"(m0)
-        : "memory");
+        : "v"(src), "s"(m0), "s"(m0 + kStep)
+        : "memory", "scc");
   } else {
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, off\n\t"
-        "s_add_u32 m0, m0, 0x3c0\n\t"
+        "s_mov_b32 m0, %3\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, off offset:64\n\t"
-        "s_add_u32 m0, m0, 0x3c0\n\t"
+        "s_mov_b32 m0, %4\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, off offset:128\n\t"
-        "s_add_u32 m0, m0, 0x3c0\n\t"
+        "s_mov_b32 m0, %5\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %1, off offset:192\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "v"(src), "s"(m0)
-        : "memory");
+        : "v"(src), "s"(m0), "s"(m0 + kStep), "s"(m0 + 2 * kStep), "s"(m0 + 3 * kStep)
+        : "memory", "scc");
   }
 }
 
@@ -304,10 +313,7 @@ __device__ __forceinline__ void issue_v(lds_u8* slot, const PG& pgn, int t0, int
 // Empty volatile asm that reads and rewrites its operands: the values must exist at this
 // point of the program, so the code computing them cannot sink below it.
 __device__ __forceinline__ void pin(f32x16& v) { asm volatile("" : "+v"(v)); }
-__device__ __forceinline__ void pin(uint32_t (&v)[8]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(v[j]));
-}
+__device__ __forceinline__ void pin(u32x4 (&v)[2]) { asm volatile("" : "+v"(v[0]), "+v"(v[1])); }
 
 // Instruction classes of the scheduling-group builtin, and an interleave of NM matrix
 // instructions with the LDS reads that feed them (AHEAD issued first, then PER after each
@@ -391,7 +397,7 @@ __device__ __forceinline__ float raise_reference(float& m, float mx_scaled, bool
 // Otherwise (33-64 rows): two row blocks, each shared by two waves that take the two
 // 32-token halves of every 64-token tile of the plain loop.
 // ---------------------------------------------------------------------------------
-template <int D, bool PIPE, bool POW2>
+template <int D, bool PIPE, int PG>
 __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& item, const ReqRec& rq, int hk,
                                                const Slots<D>& sl) {
   constexpr int KB = PF<D>::KB, FRAG = PF<D>::FRAG;
@@ -400,7 +406,9 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
   constexpr int N_RG = kWaves / N_KS;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r32 = lane & 31, h = lane >> 5;
-  const int rg = wave % N_RG, ks = wave / N_RG;  // row block; 32-token block within a tile
+  constexpr bool POW2 = PG != kPageAny;
+  // row block; 32-token block within a tile (the pipelined shape has one row block per wave)
+  const int rg = PIPE ? wave : wave % N_RG, ks = PIPE ? 0 : wave / N_RG;
   const int nrows = item.row_end - item.row_start;
   const float c = a.sm_scale * kLog2e;
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
@@ -429,7 +437,10 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
   if (a.causal) min_lim = min(kv_end, rq.kv_len - rq.q_len + item.row_start / a.g + 1);
   min_lim = __builtin_amdgcn_readfirstlane(min_lim);  // uniform: the mask test is a scalar branch
 
-  float m = kNegInf, l = 0.f, corr = 1.f;
+  // Running reference in log2 units.  It starts at a finite floor far below any score, so the
+  // exponent S c - m is -inf for masked scores and finite otherwise, with no special case;
+  // a row that saw no visible key keeps l = 0 and is written as the empty state.
+  float m = kMFloor, l = 0.f, corr = 1.f;
   f32x16 oacc[KB];
 #pragma unroll
   for (int b = 0; b < KB; ++b)
@@ -476,19 +487,21 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
     const float mxs = pair_max(mx) * c;
     const bool raise = mxs > m + kRescaleMargin;
     const bool any = __ballot(raise) != 0;
-    const float mnew = raise ? mxs : m;
-    corr = raise ? fast_exp2(m - mnew) : 1.f;  // m = -inf gives 0
-    m = mnew;
-    const float muse = m == kNegInf ? 0.f : m;
+    if (any) {
+      const float mnew = raise ? mxs : m;
+      corr = fast_exp2(m - mnew);  // 1 where the reference stays
+      m = mnew;
+      l *= corr;
+    }
     float lsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
-      const float p0 = fast_exp2(__builtin_fmaf(S[i], c, -muse));
-      const float p1 = fast_exp2(__builtin_fmaf(S[i + 1], c, -muse));
+      const float p0 = fast_exp2(__builtin_fmaf(S[i], c, -m));
+      const float p1 = fast_exp2(__builtin_fmaf(S[i + 1], c, -m));
       pk[i >> 1] = cvt_pk_bf16(p0, p1);
       lsum = sum_pair(pk[i >> 1], lsum);
     }
-    l = l * corr + lsum;
+    l += lsum;
     return any;
   };
   auto rescale = [&](bool any) {
@@ -513,75 +526,6 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
     }
   };
 
-  // The two phases of a pipelined step, in a fixed instruction order (scheduling barriers
-  // between the groups keep the compiler from regrouping them):
-  // phase A: the KS16 score MFMAs of the next tile, each followed by the LDS read of the K
-  // fragment two k-steps ahead and a slice of this tile's softmax (first the row maximum and
-  // the reference update, then the exponentials, a few pairs per slice);
-  auto phase_a = [&](const lds_u8* kt, f32x16& Snext, const f32x16& Scur, uint32_t (&pk)[8]) -> bool {
-    const lds_u8* kp = kt + (2 * ks + (r32 >> 4)) * KB * FRAG + k_pos;
-    auto kread = [&](int k) { return *reinterpret_cast<lds_bf16x8*>(kp + (k >> 1) * FRAG + 512 * (k & 1)); };
-    bf16x8 kr[KS16];
-    kr[0] = kread(0);
-    kr[1] = kread(1);
-    float mx = kNegInf, muse = 0.f, lsum = 0.f;
-    bool any = false;
-#pragma unroll
-    for (int g = 0; g < KS16; ++g) {
-      __builtin_amdgcn_sched_barrier(0);
-      Snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[g], qb[g], g == 0 ? f32x16{} : Snext, 0, 0, 0);
-      if (g + 2 < KS16) kr[g + 2] = kread(g + 2);
-      if (g == 0) {
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) mx = fmaxf(mx, fmaxf(Scur[i], Scur[i + 1]));
-      } else if (g == 1) {
-#pragma unroll
-        for (int i = 8; i < 16; i += 2) mx = fmaxf(mx, fmaxf(Scur[i], Scur[i + 1]));
-        const float mxs = pair_max(mx) * c;
-        const bool raise = mxs > m + kRescaleMargin;
-        any = __ballot(raise) != 0;
-        const float mnew = raise ? mxs : m;
-        corr = raise ? fast_exp2(m - mnew) : 1.f;  // m = -inf gives 0
-        m = mnew;
-        muse = m == kNegInf ? 0.f : m;
-      } else {
-        // pairs whose slice is g: pair q goes to slice 2 + q (KS16 - 2) / 8
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          if (2 + q * (KS16 - 2) / 8 != g) continue;
-          const float p0 = fast_exp2(__builtin_fmaf(Scur[2 * q], c, -muse));
-          const float p1 = fast_exp2(__builtin_fmaf(Scur[2 * q + 1], c, -muse));
-          pk[q] = cvt_pk_bf16(p0, p1);
-          lsum = sum_pair(pk[q], lsum);
-        }
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    l = l * corr + lsum;
-    return any;
-  };
-  // phase B: P.V of this tile, the two transposing reads of each MFMA issued two MFMAs ahead
-  auto phase_b = [&](const lds_u8* vt, const uint32_t (&pk)[8]) {
-    constexpr int NM = 2 * KB;
-    auto vread = [&](int m2) {  // operand of MFMA m2 = (k-block m2 / KB, column block m2 % KB)
-      const lds_u8* vf = vt + (2 * ks + m2 / KB) * KB * FRAG + (m2 % KB) * FRAG;
-      return cat(tr_read(vf + v_lo), tr_read(vf + v_hi));
-    };
-    bf16x8 va[NM];
-    va[0] = vread(0);
-    va[1] = vread(1);
-#pragma unroll
-    for (int m2 = 0; m2 < NM; ++m2) {
-      __builtin_amdgcn_sched_barrier(0);
-      const int half = m2 / KB, cb = m2 % KB;
-      const bf16x8 pb = __builtin_bit_cast(
-          bf16x8, u32x4{pk[4 * half], pk[4 * half + 1], pk[4 * half + 2], pk[4 * half + 3]});
-      oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[m2], pb, oacc[cb], 0, 0, 0);
-      if (m2 + 2 < NM) va[m2 + 2] = vread(m2 + 2);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
   if constexpr (!PIPE) {
     tile_loop<D>(pgn, item.kv_start, kv_end, sl, K, V, [&](const lds_u8* kt, const lds_u8* vt, int t0) {
       f32x16 S;
@@ -592,18 +536,20 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
       pv(vt, pk);
     });
   } else {
-    // Software pipeline over 32-token tiles j (tokens T(j) .. T(j)+31), K(j) and V(j) in
-    // slot j % 4 of their 4-slot rings (8 KB each for D = 128).  Step j:
-    //   [A] wait for K(j+1), barrier, DMA V(j+3) into V(j-1)'s slot; scores of tile j+1 on
-    //       the matrix cores while the softmax of tile j runs on the vector ALUs;
-    //   [B] wait for V(j), barrier, DMA K(j+5) into K(j+1)'s slot; P.V of tile j; mask of
-    //       tile j+1.
-    // Each load is issued 3.5 steps before its use.  The DMA loads are the only vector-memory
-    // loads in flight (page ids come from the LDS window); per barrier every wave issues one
-    // batch of D/64 of them, so at each wait the batches younger than the one needed are the
-    // six issued at the previous six barriers (fewer near the end, where some are skipped).
-    constexpr int NF = KB / 2;            // K (or V) fragments each wave loads per tile
-    constexpr int HALF = 2 * KB * FRAG;   // bytes of K (or V) of one 32-token tile
+    // Software pipeline over 32-token tiles j (tokens T(j) .. T(j)+31); K(j) and V(j) sit in
+    // slot j % 4 of their 4-slot rings (8 KB each for D = 128).  Step j, after one barrier:
+    //   - DMA K(j+4) into K(j)'s slot and V(j+2) into V(j-2)'s slot (both read in step j-1);
+    //   - one interleaved stream of matrix instructions: the scores of tile j+1
+    //     (S(j+1) = K(j+1) Q^T, a chain of D/16 products) alternating with P.V of tile j-1
+    //     (independent accumulators), while the vector ALUs run the online softmax of tile j
+    //     (scores computed in step j-1) and produce P(j);
+    //   - if the reference maximum was raised, rescale O (which now holds P.V up to j-1).
+    // Every load is issued three steps before its use; each step issues one batch of D/64
+    // loads of K and one of V per wave, so at the wait the batches younger than the ones
+    // needed are those of the previous two steps (fewer where loads past the end were skipped).
+    constexpr int NF = KB / 2;           // K (or V) fragments each wave loads per tile
+    constexpr int HALF = 2 * KB * FRAG;  // bytes of K (or V) of one 32-token tile
+    constexpr int AH = 2;                // operand reads issued ahead of their matrix instruction
     const int kv0 = item.kv_start;
     const int n = (kv_end - kv0 + 31) / 32;
     auto T = [&](int j) { return kv0 + 32 * j; };
@@ -622,10 +568,35 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
       dma_fragments<NF>(V + pgn.template row<D>(T(j) + 16 * tg + v_dma_token(lane), page) + 8 * (lane >> 4) + 32 * cg,
                         v_slot(j) + f0 * FRAG);
     };
+    // Fast steps (P divides 32) touch only full tiles (no clamping), and a lane's token keeps
+    // its offset inside the page from tile to tile: its row address is the page id times the
+    // page's bytes plus a per-item constant (one 32 x 32 -> 64-bit multiply-add), and its
+    // page-table entry advances by 32 / P entries per tile.
+    uint64_t k_add = 0, v_add = 0;
+    int32_t k_pn = 0, v_pn = 0, pstep = 0;
+    uint32_t page_bytes = 0;
+    if constexpr (PG == kPageDiv32) {
+      const int kx = kv0 + 16 * tg + k_dma_token(lane), vx = kv0 + 16 * tg + v_dma_token(lane);
+      const int col = 8 * (lane >> 4) + 32 * cg;
+      k_add = reinterpret_cast<uint64_t>(K) + 2u * uint32_t(((kx & (a.P - 1)) * a.Hk + hk) * D + col);
+      v_add = reinterpret_cast<uint64_t>(V) + 2u * uint32_t(((vx & (a.P - 1)) * a.Hk + hk) * D + col);
+      k_pn = kx >> a.p_shift;
+      v_pn = vx >> a.p_shift;
+      pstep = 32 >> a.p_shift;
+      page_bytes = uint32_t(a.P * a.Hk * D) * 2u;
+    }
+    auto page_k_fast = [&](int j) { return pgn.table[k_pn + j * pstep - pgn.base]; };
+    auto page_v_fast = [&](int j) { return pgn.table[v_pn + j * pstep - pgn.base]; };
+    auto dma_k_fast = [&](int j, int32_t page) {
+      const uint64_t addr = uint64_t(uint32_t(page)) * page_bytes + k_add;
+      dma_fragments<NF>(reinterpret_cast<const uint16_t*>(addr), k_slot(j) + f0 * FRAG);
+    };
+    auto dma_v_fast = [&](int j, int32_t page) {
+      const uint64_t addr = uint64_t(uint32_t(page)) * page_bytes + v_add;
+      dma_fragments<NF>(reinterpret_cast<const uint16_t*>(addr), v_slot(j) + f0 * FRAG);
+    };
     auto wait_batches = [&](int nb) {  // at most nb batches of NF loads in flight
       switch (nb) {
-        case 6: BSR_WAIT_VMCNT(6 * NF); break;
-        case 5: BSR_WAIT_VMCNT(5 * NF); break;
         case 4: BSR_WAIT_VMCNT(4 * NF); break;
         case 3: BSR_WAIT_VMCNT(3 * NF); break;
         case 2: BSR_WAIT_VMCNT(2 * NF); break;
@@ -633,80 +604,145 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
         default: BSR_WAIT_VMCNT(0); break;
       }
     };
+
+    // One step's matrix and vector work in a fixed instruction order (scheduling barriers
+    // between the groups keep the compiler from regrouping them): for g = 0 .. D/16 - 1,
+    // P.V product g of tile j-1, score product g of tile j+1, the operand reads AH products
+    // ahead, and slice g of the softmax of tile j (first the row maximum and the reference
+    // update, then the exponentials, a few pairs per slice).  Returns whether any row of the
+    // wave raised its reference (then corr holds each row's factor and l is already rescaled).
+    auto fused = [&](const lds_u8* kt, const lds_u8* vt, f32x16& Snext, const f32x16& Scur, const u32x4 (&pprev)[2],
+                     u32x4 (&pcur)[2]) -> bool {
+      constexpr bool QK = true, PV = true, SM = true;
+      const lds_u8* kp = kt + (r32 >> 4) * KB * FRAG + k_pos;
+      auto kread = [&](int k) { return *reinterpret_cast<lds_bf16x8*>(kp + (k >> 1) * FRAG + 512 * (k & 1)); };
+      // operand of P.V product m2 = (16-token half m2 / KB, column block m2 % KB)
+      auto vread = [&](int m2) {
+        const lds_u8* vf = vt + (m2 / KB) * KB * FRAG + (m2 % KB) * FRAG;
+        return cat(tr_read(vf + v_lo), tr_read(vf + v_hi));
+      };
+      bf16x8 kr[KS16], va[KS16];
+#pragma unroll
+      for (int k = 0; k < AH; ++k) {
+        if (PV) va[k] = vread(k);
+        if (QK) kr[k] = kread(k);
+      }
+      float mx = 0.f, lsum = 0.f;
+      bool any = false;
+#pragma unroll
+      for (int g = 0; g < KS16; ++g) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (PV) {
+          const int half = g / KB, cb = g % KB;
+          oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[g], __builtin_bit_cast(bf16x8, pprev[half]), oacc[cb],
+                                                             0, 0, 0);
+        }
+        if (QK) Snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[g], qb[g], g == 0 ? f32x16{} : Snext, 0, 0, 0);
+        if (g + AH < KS16) {
+          if (PV) va[g + AH] = vread(g + AH);
+          if (QK) kr[g + AH] = kread(g + AH);
+        }
+        if (!SM) continue;
+        if (g == 0) {
+          // row maximum as a tree of three-input maxima
+          mx = fmaxf(Scur[0], fmaxf(Scur[1], Scur[2]));
+#pragma unroll
+          for (int i = 3; i < 7; i += 2) mx = fmaxf(mx, fmaxf(Scur[i], Scur[i + 1]));
+        } else if (g == 1) {
+#pragma unroll
+          for (int i = 7; i < 15; i += 2) mx = fmaxf(mx, fmaxf(Scur[i], Scur[i + 1]));
+          mx = fmaxf(mx, Scur[15]);
+          const float mxs = pair_max(mx) * c;
+          const bool raise = mxs > m + kRescaleMargin;
+          any = __ballot(raise) != 0;
+          if (any) {  // rare after the first tiles: a scalar branch around the update
+            const float mnew = raise ? mxs : m;
+            corr = fast_exp2(m - mnew);  // 1 where the reference stays
+            m = mnew;
+            l *= corr;
+          }
+        } else {
+          // pairs whose slice is g: pair q goes to slice 2 + q (KS16 - 2) / 8
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            if (2 + q * (KS16 - 2) / 8 != g) continue;
+            const float p0 = fast_exp2(__builtin_fmaf(Scur[2 * q], c, -m));
+            const float p1 = fast_exp2(__builtin_fmaf(Scur[2 * q + 1], c, -m));
+            pcur[q >> 2][q & 3] = cvt_pk_bf16(p0, p1);
+            lsum = sum_pair(pcur[q >> 2][q & 3], lsum);
+          }
+        }
+      }
+      // keep P and the scores inside this stream: without these the compiler sinks them next
+      // to their first use, after the rescale branch
+      pin(pcur);
+      pin(Snext);
+      __builtin_amdgcn_sched_barrier(0);
+      l += lsum;
+      return any;
+    };
+
     f32x16 Sa, Sb;
-    uint32_t pk[8];
+    u32x4 pa[2], pb[2];
     __syncthreads();  // LDS free (previous item finished)
+    pgn.base = -kPageWindow;  // nothing staged for this item yet
     pgn.cover(T(0), T(6) - 1);
     {
       const int32_t k0 = page_k(0), k1 = page_k(1), k2 = page_k(2), k3 = page_k(3);
-      const int32_t v0 = page_v(0), v1 = page_v(1), v2 = page_v(2);
+      const int32_t v0 = page_v(0), v1 = page_v(1);
       dma_k(0, k0);
       if (n > 1) dma_k(1, k1);
       if (n > 2) dma_k(2, k2);
       if (n > 3) dma_k(3, k3);
       dma_v(0, v0);
       if (n > 1) dma_v(1, v1);
-      if (n > 2) dma_v(2, v2);
     }
-    int32_t nk = page_k(4), nv = page_v(3);
+    int32_t nk = page_k(4), nv = page_v(2);  // for step 0's loads
     BSR_WAIT_VMCNT(0);
-    __syncthreads();  // K(0..3), V(0..2) staged
+    __syncthreads();  // K(0..3), V(0..1) staged
     qk(k_slot(0), Sa);
     mask(Sa, T(0));
-    __syncthreads();  // every wave has read K(0)
-    {
-      const int32_t nk2 = page_k(5);
-      if (n > 4) dma_k(4, nk);
-      nk = nk2;
-    }
-    // FULL: every load of the step is issued (its tiles all exist), so the step is
-    // straight-line code with fixed wait counts
-    auto step = [&](auto full, int j, f32x16& Scur, f32x16& Snext) {
-      constexpr bool FULL = decltype(full)::value;
-      pgn.cover(T(j + 4), T(j + 7) - 1);  // this step's lookups: V(j+4), K(j+6)
-      // [A]
-      if (FULL) wait_batches(6);
-      else wait_batches(1 + (j + 2 < n) + (j + 1 < n) + (j + 3 < n) + (j + 2 < n) + (j + 4 < n));
+
+    // Steps 0 .. n all run the same stream.  In step 0 the P.V product uses P(-1) = 0 over
+    // the staged V(0) (rows of real tokens, so it adds exact zeros).  Step n-1 computes the
+    // scores of the nonexistent tile n from a stale slot and the mask sets every one of them
+    // to -inf (all its tokens lie past the end), so step n's softmax leaves the state as it
+    // is while its P.V product adds the last tile.
+    // Fast steps need tiles up to j + 5 full (and exist only for P dividing 32).
+    const int n_full = PG == kPageDiv32 ? (kv_end - kv0) / 32 : 0;
+    // step j with S(j) in Scur and P(j-1) in pprev; writes S(j+1) to Snext and P(j) to pcur
+    auto step = [&](int j, f32x16& Scur, f32x16& Snext, const u32x4 (&pprev)[2], u32x4 (&pcur)[2]) {
+      const bool fast = PG == kPageDiv32 && j >= 1 && j + 5 < n_full;
+      pgn.cover(T(j + 3), T(j + 6) - 1);  // this step's lookups: K(j+5), V(j+3)
+      if (fast) wait_batches(4);
+      else wait_batches((j + 2 < n) + (j < n) + (j + 3 < n) + (j + 1 < n));
       __builtin_amdgcn_s_barrier();
-      {
-        const int32_t nv2 = page_v(j + 4);
-        if (FULL || j + 3 < n) dma_v(j + 3, nv);
+      if (fast) {
+        const int32_t nk2 = page_k_fast(j + 5), nv2 = page_v_fast(j + 3);
+        dma_k_fast(j + 4, nk);
+        dma_v_fast(j + 2, nv);
+        nk = nk2;
+        nv = nv2;
+      } else {
+        const int32_t nk2 = page_k(j + 5), nv2 = page_v(j + 3);
+        if (j + 4 < n) dma_k(j + 4, nk);
+        if (j + 2 < n) dma_v(j + 2, nv);
+        nk = nk2;
         nv = nv2;
       }
       __builtin_amdgcn_sched_barrier(0);
-      // scores of the next tile on the matrix cores, softmax of this one in their shadow
-      // (past the last tile this reads a stale slot; the scores are then unused)
-      const bool any = phase_a(k_slot(j + 1), Snext, Scur, pk);
-      // keep both inside this phase: without these the compiler sinks P (and the scores)
-      // next to their first use after the rescale branch
-      pin(Snext);
-      pin(pk);
-      __builtin_amdgcn_sched_barrier(0);
-      // [B]
-      if (FULL) wait_batches(6);
-      else wait_batches((j + 2 < n) + (j + 1 < n) + (j + 3 < n) + (j + 2 < n) + (j + 4 < n) + (j + 3 < n));
-      __builtin_amdgcn_s_barrier();
-      {
-        const int32_t nk2 = page_k(j + 6);
-        if (FULL || j + 5 < n) dma_k(j + 5, nk);
-        nk = nk2;
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      const bool any = fused(k_slot(j + 1), v_slot(j == 0 ? 0 : j - 1), Snext, Scur, pprev, pcur);
       rescale(any);
-      phase_b(v_slot(j), pk);
-      if (FULL || j + 1 < n) mask(Snext, T(j + 1));
+      mask(Snext, T(j + 1));
     };
-    using Full = std::integral_constant<bool, true>;
-    using Tail = std::integral_constant<bool, false>;
-    int j = 0;
-    for (; j + 6 < n; j += 2) {
-      step(Full{}, j, Sa, Sb);
-      step(Full{}, j + 1, Sb, Sa);
-    }
-    for (; j < n; j += 2) {
-      step(Tail{}, j, Sa, Sb);
-      if (j + 1 >= n) break;
-      step(Tail{}, j + 1, Sb, Sa);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) pb[i] = u32x4{0u, 0u, 0u, 0u};  // P(-1)
+    // two steps per iteration so that the register roles alternate without copies
+    for (int j = 0;; j += 2) {
+      step(j, Sa, Sb, pb, pa);
+      if (j + 1 > n) break;
+      step(j + 1, Sb, Sa, pa, pb);
+      if (j + 2 > n) break;
     }
   }
 
@@ -964,9 +1000,10 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
 
 }  // namespace
 
-template <int D, bool POW2>
+template <int D, int PG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_bf16_kernel(RunArgs a) {
+  constexpr bool POW2 = PG != kPageAny;
   __shared__ __attribute__((aligned(16))) unsigned char lds[Slots<D>::BYTES];
   const Slots<D> sl{(lds_u8*)lds};
   // XCD-aware order: the dispatcher deals consecutive workgroups round-robin to the 8 XCDs,
@@ -980,8 +1017,8 @@ void attn_prefill_bf16_kernel(RunArgs a) {
     const ItemRec item = uniform_load(a.items + it);
     const ReqRec rq = uniform_load(a.req + item.req);
     const int rows = item.row_end - item.row_start;
-    if (rows > 64) prefill_item32<D, true, POW2>(a, item, rq, hk, sl);        // 3-4 blocks of 32 rows, pipelined
-    else if (rows > 32) prefill_item32<D, false, POW2>(a, item, rq, hk, sl);  // 2 blocks, tokens split
+    if (rows > 64) prefill_item32<D, true, PG>(a, item, rq, hk, sl);        // 3-4 blocks of 32 rows, pipelined
+    else if (rows > 32) prefill_item32<D, false, PG>(a, item, rq, hk, sl);  // 2 blocks, tokens split
     else if (rows > 16) prefill_item16<D, 2, POW2>(a, item, rq, hk, sl);  // 2 blocks of 16 rows
     else prefill_item16<D, 1, POW2>(a, item, rq, hk, sl);                 // 1 block, tokens split 4 ways
   }
@@ -990,21 +1027,25 @@ void attn_prefill_bf16_kernel(RunArgs a) {
 bool prefill_bf16_supported(int d, int Tq) { return (d == 64 || d == 128) && Tq % 16 == 0 && Tq <= 128; }
 
 int prefill_bf16_blocks_per_cu(int d) {
-  // both page-size variants use the same resources; ask for the power-of-two one
+  // every page-size variant uses the same resources; ask for one of them
   int nb = 1;
   hipError_t e = hipErrorInvalidValue;
-  if (d == 64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_prefill_bf16_kernel<64, true>, kThreads, 0);
-  if (d == 128) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_prefill_bf16_kernel<128, true>, kThreads, 0);
+  if (d == 64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_prefill_bf16_kernel<64, kPageDiv32>, kThreads, 0);
+  if (d == 128) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_prefill_bf16_kernel<128, kPageDiv32>, kThreads, 0);
   return (e == hipSuccess && nb > 0) ? nb : 1;
+}
+
+template <int D>
+static void launch_d(const RunArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  if (a.p_shift >= 0 && a.P <= 32) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPageDiv32>), grid, block, 0, s, a);
+  else if (a.p_shift >= 0) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPagePow2>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPageAny>), grid, block, 0, s, a);
 }
 
 hipError_t launch_prefill_bf16(const RunArgs& a, hipStream_t s) {
   dim3 grid(a.C, a.Hk), block(kThreads);
-  const bool pow2 = a.p_shift >= 0;
-  if (a.d == 64 && pow2) hipLaunchKernelGGL((attn_prefill_bf16_kernel<64, true>), grid, block, 0, s, a);
-  else if (a.d == 64) hipLaunchKernelGGL((attn_prefill_bf16_kernel<64, false>), grid, block, 0, s, a);
-  else if (a.d == 128 && pow2) hipLaunchKernelGGL((attn_prefill_bf16_kernel<128, true>), grid, block, 0, s, a);
-  else if (a.d == 128) hipLaunchKernelGGL((attn_prefill_bf16_kernel<128, false>), grid, block, 0, s, a);
+  if (a.d == 64) launch_d<64>(a, grid, block, s);
+  else if (a.d == 128) launch_d<128>(a, grid, block, s);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
