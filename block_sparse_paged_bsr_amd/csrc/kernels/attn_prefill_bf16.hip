@@ -605,6 +605,9 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
       }
     };
 
+    const float inv_c = 1.f / c;
+    float thr = __builtin_fmaf(m, inv_c, kRescaleMargin * inv_c);  // raw-score threshold of a raise
+
     // One step's matrix and vector work in a fixed instruction order (scheduling barriers
     // between the groups keep the compiler from regrouping them): for g = 0 .. D/16 - 1,
     // P.V product g of tile j-1, score product g of tile j+1, the operand reads AH products
@@ -627,7 +630,7 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
         if (PV) va[k] = vread(k);
         if (QK) kr[k] = kread(k);
       }
-      float mx = 0.f, lsum = 0.f;
+      float mx = 0.f, mx5[5], lsum = 0.f;
       bool any = false;
 #pragma unroll
       for (int g = 0; g < KS16; ++g) {
@@ -644,21 +647,20 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
         }
         if (!SM) continue;
         if (g == 0) {
-          // row maximum as a tree of three-input maxima
-          mx = fmaxf(Scur[0], fmaxf(Scur[1], Scur[2]));
+          // row maximum as a balanced tree of three-input maxima: five independent ones here
 #pragma unroll
-          for (int i = 3; i < 7; i += 2) mx = fmaxf(mx, fmaxf(Scur[i], Scur[i + 1]));
+          for (int i = 0; i < 5; ++i) mx5[i] = fmaxf(Scur[3 * i], fmaxf(Scur[3 * i + 1], Scur[3 * i + 2]));
         } else if (g == 1) {
-#pragma unroll
-          for (int i = 7; i < 15; i += 2) mx = fmaxf(mx, fmaxf(Scur[i], Scur[i + 1]));
-          mx = fmaxf(mx, Scur[15]);
-          const float mxs = pair_max(mx) * c;
-          const bool raise = mxs > m + kRescaleMargin;
+          mx = fmaxf(fmaxf(mx5[0], fmaxf(mx5[1], mx5[2])), fmaxf(mx5[3], fmaxf(mx5[4], Scur[15])));
+          // the reference is raised when a raw score exceeds thr = (m + margin) / c
+          const float pmx = pair_max(mx);
+          const bool raise = pmx > thr;
           any = __ballot(raise) != 0;
           if (any) {  // rare after the first tiles: a scalar branch around the update
-            const float mnew = raise ? mxs : m;
+            const float mnew = raise ? pmx * c : m;
             corr = fast_exp2(m - mnew);  // 1 where the reference stays
             m = mnew;
+            thr = __builtin_fmaf(m, inv_c, kRescaleMargin * inv_c);
             l *= corr;
           }
         } else {
