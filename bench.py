@@ -159,8 +159,9 @@ def bench_prefill(args):
     from block_sparse_paged_bsr_amd import inputs
 
     b = inputs.ragged_prefill_bf16(seed=0, poison=False)
-    r = run_case(b, "prefill", max(5, args.steps // 5), 2, causal=True)
-    attn_ms, _, merge_ms, _ = kernel_times(r["step"], 5)
+    # ~1 ms per call: enough warm-up calls for the clocks to settle, then a few tens timed
+    r = run_case(b, "prefill", max(10, args.steps // 2), 10, causal=True)
+    attn_ms, _, merge_ms, _ = kernel_times(r["step"], 10)
     fl = prefill_flops(b.kv_lens)
     return {"ms": r["ms"], "tflops": fl / (r["ms"] * 1e-3) / 1e12, "flops": fl, "attn_kernel_ms": attn_ms,
             "merge_kernel_ms": merge_ms, "num_workers": r["num_workers"], "batch": b}

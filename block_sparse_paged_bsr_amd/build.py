@@ -41,7 +41,10 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", 
 # The prefill kernel runs with the IEEE mode bit off: scores are never NaN (masked ones are
 # -inf), and with the bit on every maximum over matrix-core results needs an extra NaN-quieting
 # v_max_f32 per operand.
-EXTRA_FLAGS = {"attn_prefill_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+# The MFMA accumulators that the vector ALUs read (scores) stay in VGPRs; the 128-row shape
+# places its output accumulators in AGPRs itself (inline asm), so the compiler's heuristic
+# never moves scores into AGPRs and back.
+EXTRA_FLAGS = {"attn_prefill_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc():

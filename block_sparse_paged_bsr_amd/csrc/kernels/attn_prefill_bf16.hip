@@ -61,6 +61,7 @@ namespace {
 constexpr int kTileKV = 64;  // tokens per staged KV tile
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kThreads2 = 128;  // workgroup of the 128-row shape: two waves of 512 VGPRs
 constexpr float kRescaleMargin = 8.f;  // log2 units
 constexpr float kMFloor = -1e30f;      // initial reference of the 32-row shapes (log2 units)
 constexpr int kPageWindow = 2048;      // page ids staged in LDS per workgroup
@@ -206,14 +207,16 @@ struct Paging {
     return int64_t(uint64_t(uint32_t(page)) * uint32_t(P * Hk * D) + uint32_t((off * Hk + hk) * D));
   }
   // (Re)fill the window so it holds the pages of tokens [lo, hi]; lo and hi are uniform and
-  // every thread of the workgroup calls this (it synchronises the workgroup when it refills).
+  // every thread of the workgroup (NTH of them) calls this (it synchronises the workgroup
+  // when it refills).
+  template <int NTH = kThreads>
   __device__ __forceinline__ void cover(int lo, int hi) {
     const int plo = page_no(lo), phi = page_no(hi);
     if (plo >= base && phi < base + kPageWindow) return;
     __syncthreads();  // nobody reads the old window any more
     base = plo;
     const int cnt = min(kPageWindow, page_no(kv_end - 1) - plo + 1);
-    for (int j = threadIdx.x; j < cnt; j += kThreads) table[j] = indices[page_start + plo + j];
+    for (int j = threadIdx.x; j < cnt; j += NTH) table[j] = indices[page_start + plo + j];
     __syncthreads();
   }
 };
@@ -309,6 +312,17 @@ __device__ __forceinline__ void issue_v(lds_u8* slot, const PG& pgn, int t0, int
   dma_fragments<KB>(V + pgn.template row<D>(t0 + w * 16 + v_dma_token(lane), page) + 8 * (lane >> 4),
                     slot + w * KB * PF<D>::FRAG);
 }
+
+// O^T += V^T P^T on the matrix cores with the accumulator held in AGPRs (the 128-row shape
+// keeps its 128 accumulator registers there and everything the vector ALUs touch in VGPRs).
+// The compiler does not see inside the asm, so reads of the accumulator by other
+// instructions wait for the product explicitly (acc_settle).
+__device__ __forceinline__ void mfma_acc_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last accumulator product and any other access to the accumulators
+// (at least the latency of a 16-pass product).
+__device__ __forceinline__ void acc_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 // Empty volatile asm that reads and rewrites its operands: the values must exist at this
 // point of the program, so the code computing them cannot sink below it.
@@ -1000,6 +1014,344 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Query tiles of up to 128 rows on two waves of 512 VGPRs (one wave per SIMD, two
+// workgroups per CU).  Wave w holds row blocks 2w and 2w+1 (32 rows each), so every K
+// fragment and every V operand read from LDS feeds two matrix instructions, and each
+// staged 32-token KV tile serves all 128 rows.  The step structure is the software
+// pipeline of the 4-wave shape: after one barrier per step, the scores of tile j+1
+// (S(j+1) = K(j+1) Q^T) and P.V of tile j-1 run on the matrix cores while the vector ALUs
+// run the online softmax of tile j, for both row blocks.  Absent rows (past the end of a
+// short tile) carry zero queries and are never written.
+// ---------------------------------------------------------------------------------
+template <int D, int PG>
+__device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec& item, const ReqRec& rq, int hk,
+                                                const Slots<D>& sl) {
+  constexpr int KB = PF<D>::KB, FRAG = PF<D>::FRAG;
+  constexpr int KS16 = D / 16;  // 16-deep k-steps of the score product
+  constexpr bool POW2 = PG != kPageAny;
+  constexpr int NF = KB;               // fragments of K (or V) each wave loads per tile
+  constexpr int HALF = 2 * KB * FRAG;  // bytes of K (or V) of one 32-token tile
+  constexpr int AH = 2;                // operand reads issued ahead of their matrix instructions
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r32 = lane & 31, h = lane >> 5;
+  const float c = a.sm_scale * kLog2e;
+  const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
+  const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
+  const int kv_end = item.kv_end;
+  Paging<POW2> pgn{a.indices, sl.table(), rq.page_start, a.P, a.p_shift, a.Hk, hk, kv_end, -kPageWindow};
+
+  // this lane's query rows: row r32 of blocks 2 wave and 2 wave + 1
+  int row_pos[2], row_hq[2], lim[2];
+  bool row_ok[2];
+  bf16x8 qb[2][KS16];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int r = item.row_start + 64 * wave + 32 * b + r32;
+    row_ok[b] = r < item.row_end;
+    row_pos[b] = r / a.g;
+    row_hq[b] = hk * a.g + r % a.g;
+    lim[b] = (a.causal && row_ok[b]) ? min(kv_end, rq.kv_len - rq.q_len + row_pos[b] + 1) : kv_end;
+    const uint16_t* qp = Q + (int64_t(rq.q_start + row_pos[b]) * a.Hq + row_hq[b]) * D + 8 * h;
+#pragma unroll
+    for (int k = 0; k < KS16; ++k) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row_ok[b]) v = *reinterpret_cast<const u32x4*>(qp + 16 * k);
+      qb[b][k] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  int min_lim = kv_end;  // tiles ending before the smallest visible end need no mask
+  if (a.causal) min_lim = min(kv_end, rq.kv_len - rq.q_len + item.row_start / a.g + 1);
+  min_lim = __builtin_amdgcn_readfirstlane(min_lim);
+
+  // running references (log2 units, from a finite floor), sums and rescale factors per block
+  float m[2] = {kMFloor, kMFloor}, l[2] = {0.f, 0.f}, corr[2] = {1.f, 1.f};
+  const float inv_c = 1.f / c;
+  float thr[2];  // raw-score threshold of a raise: (m + margin) / c
+#pragma unroll
+  for (int b = 0; b < 2; ++b) thr[b] = __builtin_fmaf(m[b], inv_c, kRescaleMargin * inv_c);
+  f32x16 oacc[2][KB];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int cb = 0; cb < KB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[b][cb][i] = 0.f;
+
+  // K fragment position of this lane (token r32 of the 32-token tile, half h); V transposing
+  // read: lane 16G + 4e + q addresses token 4(G >> 1) + e (and + 8), chunk 4(G & 1) + q
+  const int k_pos = 16 * ((r32 & 15) + 16 * h);
+  const int vG = lane >> 4, ve = (lane >> 2) & 3, vq = lane & 3;
+  const int v_lo = v_chunk(4 * (vG >> 1) + ve, 4 * (vG & 1) + vq);
+  const int v_hi = v_chunk(4 * (vG >> 1) + ve + 8, 4 * (vG & 1) + vq);
+
+  const int kv0 = item.kv_start;
+  const int n = (kv_end - kv0 + 31) / 32;
+  auto T = [&](int j) { return kv0 + 32 * j; };
+  auto k_slot = [&](int j) { return sl.k0() + ((j >> 1) & 1) * PF<D>::SLOT + (j & 1) * HALF; };
+  auto v_slot = [&](int j) { return sl.v0() + ((j >> 1) & 1) * PF<D>::SLOT + (j & 1) * HALF; };
+
+  // scores of both blocks for the tile staged at `kt` (prologue only)
+  auto qk = [&](const lds_u8* kt, f32x16 (&S)[2]) {
+    const lds_u8* kp = kt + (r32 >> 4) * KB * FRAG + k_pos;
+#pragma unroll
+    for (int k = 0; k < KS16; ++k) {
+      const bf16x8 ka = *reinterpret_cast<lds_bf16x8*>(kp + (k >> 1) * FRAG + 512 * (k & 1));
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        S[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[b][k], k == 0 ? f32x16{} : S[b], 0, 0, 0);
+    }
+  };
+  // causal mask of the tile starting at t0 (only where it reaches past the first row's limit)
+  auto mask = [&](f32x16 (&S)[2], int t0) {
+    if (t0 + 32 > min_lim) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int tok = t0 + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (tok >= lim[b]) S[b][i] = kNegInf;
+        }
+    }
+  };
+
+  // wave w loads token group w (16 tokens) of every 32-token tile, all KB column groups
+  auto page_k = [&](int j) { return pgn.page_of(T(j) + 16 * wave + k_dma_token(lane)); };
+  auto page_v = [&](int j) { return pgn.page_of(T(j) + 16 * wave + v_dma_token(lane)); };
+  auto dma_k = [&](int j, int32_t page) {
+    dma_fragments<NF>(K + pgn.template row<D>(T(j) + 16 * wave + k_dma_token(lane), page) + 8 * (lane >> 4),
+                      k_slot(j) + wave * KB * FRAG);
+  };
+  auto dma_v = [&](int j, int32_t page) {
+    dma_fragments<NF>(V + pgn.template row<D>(T(j) + 16 * wave + v_dma_token(lane), page) + 8 * (lane >> 4),
+                      v_slot(j) + wave * KB * FRAG);
+  };
+  // fast steps (P divides 32): fixed in-page offsets, page-table entries advance by 32 / P
+  uint64_t k_add = 0, v_add = 0;
+  int32_t k_pn = 0, v_pn = 0, pstep = 0;
+  uint32_t page_bytes = 0;
+  if constexpr (PG == kPageDiv32) {
+    const int kx = kv0 + 16 * wave + k_dma_token(lane), vx = kv0 + 16 * wave + v_dma_token(lane);
+    const int col = 8 * (lane >> 4);
+    k_add = reinterpret_cast<uint64_t>(K) + 2u * uint32_t(((kx & (a.P - 1)) * a.Hk + hk) * D + col);
+    v_add = reinterpret_cast<uint64_t>(V) + 2u * uint32_t(((vx & (a.P - 1)) * a.Hk + hk) * D + col);
+    k_pn = kx >> a.p_shift;
+    v_pn = vx >> a.p_shift;
+    pstep = 32 >> a.p_shift;
+    page_bytes = uint32_t(a.P * a.Hk * D) * 2u;
+  }
+  auto page_k_fast = [&](int j) { return pgn.table[k_pn + j * pstep - pgn.base]; };
+  auto page_v_fast = [&](int j) { return pgn.table[v_pn + j * pstep - pgn.base]; };
+  auto dma_k_fast = [&](int j, int32_t page) {
+    const uint64_t addr = uint64_t(uint32_t(page)) * page_bytes + k_add;
+    dma_fragments<NF>(reinterpret_cast<const uint16_t*>(addr), k_slot(j) + wave * KB * FRAG);
+  };
+  auto dma_v_fast = [&](int j, int32_t page) {
+    const uint64_t addr = uint64_t(uint32_t(page)) * page_bytes + v_add;
+    dma_fragments<NF>(reinterpret_cast<const uint16_t*>(addr), v_slot(j) + wave * KB * FRAG);
+  };
+  auto wait_batches = [&](int nb) {  // at most nb batches of NF loads in flight
+    switch (nb) {
+      case 4: BSR_WAIT_VMCNT(4 * NF); break;
+      case 3: BSR_WAIT_VMCNT(3 * NF); break;
+      case 2: BSR_WAIT_VMCNT(2 * NF); break;
+      case 1: BSR_WAIT_VMCNT(NF); break;
+      default: BSR_WAIT_VMCNT(0); break;
+    }
+  };
+
+  // One step's stream: 4 D/16 slots s = 4g + m, each one matrix instruction followed by one
+  // chunk of vector work, in a fixed order (scheduling barriers between the slots keep the
+  // compiler from regrouping them; a single wave per SIMD issues in order, so a matrix
+  // instruction is followed by about as much vector work as it takes to execute).
+  //   m = 0, 1: P.V product g of block m (V operand g of tile j-1, P(j-1) of block m);
+  //   m = 2, 3: score product g of block m - 2 (K fragment g of tile j+1).
+  // Vector chunks (softmax of tile j): slots 0, 1 the leaves of each block's maximum tree,
+  // 4, 5 the rest of the tree and the cross-lane maximum, 6 the reference update of both
+  // blocks (selects, no branch), then 16 units of two exponentials (pair q of block b) spread
+  // over slots 7 .. 4 D/16 - 1.  Operand reads are issued AH k-steps ahead.
+  auto fused = [&](const lds_u8* kt, const lds_u8* vt, f32x16 (&Snext)[2], const f32x16 (&Scur)[2],
+                   const u32x4 (&pprev)[2][2], u32x4 (&pcur)[2][2]) -> bool {
+    constexpr int NS = 4 * KS16;
+    const lds_u8* kp = kt + (r32 >> 4) * KB * FRAG + k_pos;
+    auto kread = [&](int k) { return *reinterpret_cast<lds_bf16x8*>(kp + (k >> 1) * FRAG + 512 * (k & 1)); };
+    auto vread = [&](int m2) {
+      const lds_u8* vf = vt + (m2 / KB) * KB * FRAG + (m2 % KB) * FRAG;
+      return cat(tr_read(vf + v_lo), tr_read(vf + v_hi));
+    };
+    bf16x8 kr[KS16], va[KS16];
+#pragma unroll
+    for (int k = 0; k < AH; ++k) {
+      va[k] = vread(k);
+      kr[k] = kread(k);
+    }
+    float mx5[2][5], pmx[2], lsum[2] = {0.f, 0.f};
+    bool raise[2] = {false, false}, any = false;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int g = s >> 2, mm = s & 3;
+      __builtin_amdgcn_sched_barrier(0);
+      if (mm == 0 && g + AH < KS16) {  // operands of k-step g + AH
+        va[g + AH] = vread(g + AH);
+        kr[g + AH] = kread(g + AH);
+      }
+      if (mm < 2) {
+        mfma_acc_agpr(oacc[mm][g % KB], va[g], __builtin_bit_cast(bf16x8, pprev[mm][g / KB]));
+      } else {
+        const int b = mm - 2;
+        Snext[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[g], qb[b][g], g == 0 ? f32x16{} : Snext[b], 0, 0, 0);
+      }
+      if (s < 2) {
+        // leaves of block s's maximum tree: five independent three-input maxima
+#pragma unroll
+        for (int i = 0; i < 5; ++i)
+          mx5[s][i] = fmaxf(Scur[s][3 * i], fmaxf(Scur[s][3 * i + 1], Scur[s][3 * i + 2]));
+      } else if (s == 4 || s == 5) {
+        const int b = s - 4;
+        const float mx = fmaxf(fmaxf(mx5[b][0], fmaxf(mx5[b][1], mx5[b][2])),
+                               fmaxf(mx5[b][3], fmaxf(mx5[b][4], Scur[b][15])));
+        pmx[b] = pair_max(mx);
+        raise[b] = pmx[b] > thr[b];
+      } else if (s == 6) {
+        // the reference moves only where a raw score passed (m + margin) / c
+        any = __ballot(raise[0] || raise[1]) != 0;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const float mnew = raise[b] ? pmx[b] * c : m[b];
+          corr[b] = fast_exp2(m[b] - mnew);  // 1 where the reference stays
+          m[b] = mnew;
+          thr[b] = __builtin_fmaf(m[b], inv_c, kRescaleMargin * inv_c);
+          l[b] *= corr[b];
+        }
+      } else if (s >= 7) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if (7 + u * (NS - 7) / 16 != s) continue;
+          const int b = u & 1, q = u >> 1;
+          const float p0 = fast_exp2(__builtin_fmaf(Scur[b][2 * q], c, -m[b]));
+          const float p1 = fast_exp2(__builtin_fmaf(Scur[b][2 * q + 1], c, -m[b]));
+          pcur[b][q >> 2][q & 3] = cvt_pk_bf16(p0, p1);
+          lsum[b] = sum_pair(pcur[b][q >> 2][q & 3], lsum[b]);
+        }
+      }
+    }
+    // keep P and the scores inside this stream: without these the compiler sinks them next
+    // to their first use
+    pin(pcur[0]);
+    pin(pcur[1]);
+    pin(Snext[0]);
+    pin(Snext[1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) l[b] += lsum[b];
+    return any;
+  };
+  auto rescale = [&](bool any) {
+    if (any) {
+      acc_settle();
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int cb = 0; cb < KB; ++cb) oacc[b][cb] *= corr[b];
+      acc_settle();
+    }
+  };
+
+  f32x16 Sa[2], Sb[2];
+  u32x4 pa[2][2], pb[2][2];
+  __syncthreads();  // LDS free (previous item finished)
+  pgn.template cover<kThreads2>(T(0), T(6) - 1);
+  {
+    const int32_t k0 = page_k(0), k1 = page_k(1), k2 = page_k(2), k3 = page_k(3);
+    const int32_t v0 = page_v(0), v1 = page_v(1);
+    dma_k(0, k0);
+    if (n > 1) dma_k(1, k1);
+    if (n > 2) dma_k(2, k2);
+    if (n > 3) dma_k(3, k3);
+    dma_v(0, v0);
+    if (n > 1) dma_v(1, v1);
+  }
+  int32_t nk = page_k(4), nv = page_v(2);  // for step 0's loads
+  BSR_WAIT_VMCNT(0);
+  __syncthreads();  // K(0..3), V(0..1) staged
+  qk(k_slot(0), Sa);
+  mask(Sa, T(0));
+
+  // Steps 0 .. n as in prefill_item32: step 0's P.V uses P(-1) = 0 over V(0); the scores of
+  // the nonexistent tile n are all masked, so step n only adds P.V of the last tile.
+  const int n_full = PG == kPageDiv32 ? (kv_end - kv0) / 32 : 0;
+  auto step = [&](int j, f32x16 (&Scur)[2], f32x16 (&Snext)[2], const u32x4 (&pprev)[2][2], u32x4 (&pcur)[2][2]) {
+    const bool fast = PG == kPageDiv32 && j >= 1 && j + 5 < n_full;
+    pgn.template cover<kThreads2>(T(j + 3), T(j + 6) - 1);  // this step's lookups: K(j+5), V(j+3)
+    if (fast) wait_batches(4);
+    else wait_batches((j + 2 < n) + (j < n) + (j + 3 < n) + (j + 1 < n));
+    __builtin_amdgcn_s_barrier();
+    if (fast) {
+      const int32_t nk2 = page_k_fast(j + 5), nv2 = page_v_fast(j + 3);
+      dma_k_fast(j + 4, nk);
+      dma_v_fast(j + 2, nv);
+      nk = nk2;
+      nv = nv2;
+    } else {
+      const int32_t nk2 = page_k(j + 5), nv2 = page_v(j + 3);
+      if (j + 4 < n) dma_k(j + 4, nk);
+      if (j + 2 < n) dma_v(j + 2, nv);
+      nk = nk2;
+      nv = nv2;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const bool any = fused(k_slot(j + 1), v_slot(j == 0 ? 0 : j - 1), Snext, Scur, pprev, pcur);
+    rescale(any);
+    mask(Snext, T(j + 1));
+  };
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) pb[b][i] = u32x4{0u, 0u, 0u, 0u};  // P(-1)
+  for (int j = 0;; j += 2) {
+    step(j, Sa, Sb, pb, pa);
+    if (j + 1 > n) break;
+    step(j + 1, Sb, Sa, pa, pb);
+    if (j + 2 > n) break;
+  }
+
+  // ---- epilogue: final output or partial state, per block ----
+  acc_settle();
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const float lb = pair_sum(l[b]);  // the two halves of a row held different tokens
+    if (!row_ok[b]) continue;
+    const bool empty = !(lb > 0.f);
+    const float inv = empty ? 0.f : 1.f / lb;
+    const float lse = empty ? kNegInf : (m[b] + log2f(lb)) * kLn2;
+    const int r = item.row_start + 64 * wave + 32 * b + r32;
+    if (item.slot < 0) {
+      const int64_t orow = int64_t(rq.q_start + row_pos[b]) * a.Hq + row_hq[b];
+      uint16_t* op = static_cast<uint16_t*>(a.o) + orow * D + 4 * h;
+#pragma unroll
+      for (int cb = 0; cb < KB; ++cb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<u32x2*>(op + 32 * cb + 8 * q4) =
+              u32x2{cvt_pk_bf16(oacc[b][cb][4 * q4] * inv, oacc[b][cb][4 * q4 + 1] * inv),
+                    cvt_pk_bf16(oacc[b][cb][4 * q4 + 2] * inv, oacc[b][cb][4 * q4 + 3] * inv)};
+      if (h == 0) a.lse[orow] = lse;
+    } else {
+      const int64_t prow = (int64_t(item.slot) * a.Hk + hk) * a.Tq + (r - item.row_start);
+      float* pp = a.part_o + prow * D + 4 * h;
+#pragma unroll
+      for (int cb = 0; cb < KB; ++cb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(pp + 32 * cb + 8 * q4) =
+              f32x4{oacc[b][cb][4 * q4], oacc[b][cb][4 * q4 + 1], oacc[b][cb][4 * q4 + 2], oacc[b][cb][4 * q4 + 3]} *
+              inv;
+      if (h == 0) a.part_lse[prow] = lse;
+    }
+  }
+}
+
 }  // namespace
 
 template <int D, int PG>
@@ -1026,6 +1378,22 @@ void attn_prefill_bf16_kernel(RunArgs a) {
   }
 }
 
+// The 128-row shape: every item of a plan whose query tile is 128 rows.
+template <int D, int PG>
+__global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_prefill128_bf16_kernel(RunArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[Slots<D>::BYTES];
+  const Slots<D> sl{(lds_u8*)lds};
+  const int bid = blockIdx.x + gridDim.x * blockIdx.y;  // KV-head-minor: see attn_prefill_bf16_kernel
+  const int hk = __builtin_amdgcn_readfirstlane(bid % a.Hk), w = __builtin_amdgcn_readfirstlane(bid / a.Hk);
+  const int it_end = uniform_load(a.qptr + w + 1);
+  for (int it = uniform_load(a.qptr + w); it < it_end; ++it) {
+    const ItemRec item = uniform_load(a.items + it);
+    const ReqRec rq = uniform_load(a.req + item.req);
+    prefill_item128<D, PG>(a, item, rq, hk, sl);
+  }
+}
+
 bool prefill_bf16_supported(int d, int Tq) { return (d == 64 || d == 128) && Tq % 16 == 0 && Tq <= 128; }
 
 int prefill_bf16_blocks_per_cu(int d) {
@@ -1038,16 +1406,25 @@ int prefill_bf16_blocks_per_cu(int d) {
 }
 
 template <int D>
-static void launch_d(const RunArgs& a, dim3 grid, dim3 block, hipStream_t s) {
-  if (a.p_shift >= 0 && a.P <= 32) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPageDiv32>), grid, block, 0, s, a);
-  else if (a.p_shift >= 0) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPagePow2>), grid, block, 0, s, a);
+static void launch_d(const RunArgs& a, dim3 grid, hipStream_t s) {
+  const bool div32 = a.p_shift >= 0 && a.P <= 32, pow2 = a.p_shift >= 0;
+  if (a.Tq == 128) {  // 128-row tiles: two waves of two row blocks each
+    const dim3 block(kThreads2);
+    if (div32) hipLaunchKernelGGL((attn_prefill128_bf16_kernel<D, kPageDiv32>), grid, block, 0, s, a);
+    else if (pow2) hipLaunchKernelGGL((attn_prefill128_bf16_kernel<D, kPagePow2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_prefill128_bf16_kernel<D, kPageAny>), grid, block, 0, s, a);
+    return;
+  }
+  const dim3 block(kThreads);
+  if (div32) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPageDiv32>), grid, block, 0, s, a);
+  else if (pow2) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPagePow2>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPageAny>), grid, block, 0, s, a);
 }
 
 hipError_t launch_prefill_bf16(const RunArgs& a, hipStream_t s) {
-  dim3 grid(a.C, a.Hk), block(kThreads);
-  if (a.d == 64) launch_d<64>(a, grid, block, s);
-  else if (a.d == 128) launch_d<128>(a, grid, block, s);
+  dim3 grid(a.C, a.Hk);
+  if (a.d == 64) launch_d<64>(a, grid, s);
+  else if (a.d == 128) launch_d<128>(a, grid, s);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
