@@ -141,6 +141,28 @@ def run_case(b, kind, steps, warmup, rotate=1, causal=False):
     return res
 
 
+def graph_replay_ms(step, steps, warmup, variants=3):
+    """Per-step time when each step is a captured HIP graph replayed (one graph per KV pool
+    of the rotation): the plan-once, replay-per-step loop of a serving engine."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(variants):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(variants):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return time_calls(lambda s: graphs[s % variants].replay(), steps, warmup)
+
+
 def bench_decode(args):
     from block_sparse_paged_bsr_amd import inputs
 
@@ -148,9 +170,10 @@ def bench_decode(args):
     r = run_case(b, "decode", args.steps, args.warmup, rotate=3)
     med, mn, p90 = per_call_ms(r["step"], 50 if not args.quick else 10)
     attn_ms, n_attn, merge_ms, n_merge = kernel_times(r["step"], 50 if not args.quick else 10)
+    graph_ms = graph_replay_ms(r["step"], args.steps, args.warmup)
     nbytes = decode_bytes(b.kv_lens, b.batch, len(b.kv_indices))
     r.update({"gbs": nbytes / (r["ms"] * 1e-3) / 1e9, "bytes": nbytes, "median_ms": med, "min_ms": mn,
-              "p90_ms": p90, "attn_kernel_ms": attn_ms, "merge_kernel_ms": merge_ms,
+              "p90_ms": p90, "attn_kernel_ms": attn_ms, "merge_kernel_ms": merge_ms, "graph_ms": graph_ms,
               "tokens": int(b.kv_lens.sum()), "batch": b})
     return r
 
@@ -340,7 +363,8 @@ def main():
         return
     dec = bench_decode(args)
     log(f"decode: {dec['ms']*1e3:.1f} us/step, {dec['gbs']:.0f} GB/s; attn kernel "
-        f"{dec['attn_kernel_ms']*1e3:.1f} us, merge {dec['merge_kernel_ms']*1e3:.1f} us")
+        f"{dec['attn_kernel_ms']*1e3:.1f} us, merge {dec['merge_kernel_ms']*1e3:.1f} us; "
+        f"graph replay {dec['graph_ms']*1e3:.1f} us/step")
     out = {
         "metric": METRIC,
         "value": round(dec["gbs"], 2),
@@ -364,6 +388,8 @@ def main():
             "p90_us": round(dec["p90_ms"] * 1e3, 2),
             "pct_hbm_peak": round(100 * dec["gbs"] / HBM_PEAK_GBS, 2),
             "kv_pool_rotation": 3,
+            "graph_replay_us": round(dec["graph_ms"] * 1e3, 2),
+            "graph_replay_gbs": round(dec["bytes"] / (dec["graph_ms"] * 1e-3) / 1e9, 1),
         },
     }
     ach = dec["bytes"] / (dec["attn_kernel_ms"] * 1e-3) / 1e9
