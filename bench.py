@@ -257,6 +257,8 @@ def bench_composable(args):
 
     ms_c = time_calls(composed, args.steps, args.warmup)
     ms_s = time_calls(single, args.steps, args.warmup)
+    ms_cg = graph_replay_ms(composed, args.steps, args.warmup)
+    ms_sg = graph_replay_ms(single, args.steps, args.warmup)
     per = H_KV * D * 2 * 2
     qol = 2 * R * H_QO * D * 2 + R * H_QO * 4
     comp_bytes = b.groups * b.prefix_len * per + int(b.suffix_lens.sum()) * per + qol
@@ -265,7 +267,9 @@ def bench_composable(args):
             "speedup": round(ms_s / ms_c, 3), "composable_bytes": comp_bytes, "single_level_bytes": single_bytes,
             "composable_gbs_counted": round(comp_bytes / (ms_c * 1e-3) / 1e9, 1),
             "single_level_gbs": round(single_bytes / (ms_s * 1e-3) / 1e9, 1),
-            "traffic_ratio_eq15": round(single_bytes / comp_bytes, 3)}
+            "traffic_ratio_eq15": round(single_bytes / comp_bytes, 3),
+            "composable_graph_us": round(ms_cg * 1e3, 2), "single_level_graph_us": round(ms_sg * 1e3, 2),
+            "graph_speedup": round(ms_sg / ms_cg, 3)}
 
 
 def cpu_baseline(dec):
@@ -331,13 +335,78 @@ def copy_calibration():
     log(f"copy calibration: 3 x {n} bytes")
 
 
+def bench_cascade(args):
+    """Three BSR views (a prompt shared by all 64 requests, 16 group prefixes of 4, private
+    suffixes) merged left to right, vs the single-level view over the same pages."""
+    import torch
+    from block_sparse_paged_bsr_amd import api, inputs
+
+    b = inputs.cascade_decode(seed=0, poison=False)
+    q, k, v = b.torch_values("cuda")
+    C1 = api.query_num_workers("prefill", H_QO, H_KV, D)
+    C2 = api.query_num_workers("decode", H_QO, H_KV, D)
+    plans = []
+    for qo, ip, ix, la in b.levels:
+        mk = lambda C: api.Plan(ip, ix, la, num_pages=b.num_pages, num_qo_heads=H_QO, num_kv_heads=H_KV,
+                                head_dim=D, page_size=b.page_size, qo_indptr=qo, causal=False, num_workers=C)
+        # a level with little work (one prompt shared by every request) would be cut into
+        # chunks of a few tokens at the full worker count: plan it for chunks of >= 256 tokens
+        W = int(mk(C1).export()["total_work"])
+        plans.append((mk(max(1, min(C1, (W + 255) // 256))), api.run_prefill))
+    ip, ix, la = b.suffix
+    plans.append((api.Plan(ip, ix, la, num_pages=b.num_pages, num_qo_heads=H_QO, num_kv_heads=H_KV, head_dim=D,
+                           page_size=b.page_size, num_workers=C2), api.run_decode))
+    pf = api.Plan(*b.full, num_pages=b.num_pages, num_qo_heads=H_QO, num_kv_heads=H_KV, head_dim=D,
+                  page_size=b.page_size, num_workers=C2)
+    wss = [api.alloc_workspace(p) for p, _ in plans]
+    for (p, _), w in zip(plans, wss):
+        p.upload(w)
+    wf = api.alloc_workspace(pf)
+    pf.upload(wf)
+    R = q.shape[0]
+    outs = [(torch.empty_like(q), torch.empty(R, H_QO, dtype=torch.float32, device="cuda")) for _ in plans]
+    o = torch.empty_like(q)
+    l = torch.empty(R, H_QO, dtype=torch.float32, device="cuda")
+    pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(2)]
+
+    def cascade(s):
+        kk, vv = pools[s % 3]
+        for ((p, fn), w, (oo, ll)) in zip(plans, wss, outs):
+            fn(p, w, q, kk, vv, o=oo, lse=ll, sm_scale=SM)
+        api.merge_state(outs[0][0], outs[0][1], outs[1][0], outs[1][1], o_out=o, lse_out=l)
+        for oo, ll in outs[2:]:
+            api.merge_state(o, l, oo, ll, o_out=o, lse_out=l)
+
+    def single(s):
+        kk, vv = pools[s % 3]
+        api.run_decode(pf, wf, q, kk, vv, o=o, lse=l, sm_scale=SM)
+
+    ms_c = time_calls(cascade, args.steps, args.warmup)
+    ms_s = time_calls(single, args.steps, args.warmup)
+    # the cascade is several launches per step: replayed as one captured graph per KV pool
+    # it is not bound by the host's per-call cost
+    ms_cg = graph_replay_ms(cascade, args.steps, args.warmup)
+    ms_sg = graph_replay_ms(single, args.steps, args.warmup)
+    per = H_KV * D * 2 * 2
+    qol = 2 * R * H_QO * D * 2 + R * H_QO * 4
+    shared = sum(g_ * n_ for g_, n_ in zip(b.groups, b.prefix_lens))
+    casc_bytes = shared * per + int(b.suffix_lens.sum()) * per + qol
+    single_bytes = int((sum(b.prefix_lens) + b.suffix_lens).sum()) * per + qol
+    return {"cascade_us": round(ms_c * 1e3, 2), "single_level_us": round(ms_s * 1e3, 2),
+            "speedup": round(ms_s / ms_c, 3), "levels": len(plans),
+            "cascade_graph_us": round(ms_cg * 1e3, 2), "single_level_graph_us": round(ms_sg * 1e3, 2),
+            "graph_speedup": round(ms_sg / ms_cg, 3),
+            "cascade_bytes": casc_bytes, "single_level_bytes": single_bytes,
+            "single_level_gbs": round(single_bytes / (ms_s * 1e-3) / 1e9, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="decode only, no CPU baseline")
-    ap.add_argument("--only", choices=["decode", "prefill", "vector", "composable"], default=None)
+    ap.add_argument("--only", choices=["decode", "prefill", "vector", "composable", "cascade"], default=None)
     ap.add_argument("--copy-calib", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -360,6 +429,9 @@ def main():
         return
     if args.only == "composable":
         log(json.dumps(bench_composable(args)))
+        return
+    if args.only == "cascade":
+        log(json.dumps(bench_cascade(args)))
         return
     dec = bench_decode(args)
     log(f"decode: {dec['ms']*1e3:.1f} us/step, {dec['gbs']:.0f} GB/s; attn kernel "
@@ -417,6 +489,10 @@ def main():
         cp = bench_composable(args)
         log(f"composable: {cp}")
         out["composable"] = cp
+        torch.cuda.empty_cache()
+        cc = bench_cascade(args)
+        log(f"cascade: {cc}")
+        out["cascade"] = cc
         out["cpu_baseline"] = cpu_baseline(dec)
     print(json.dumps(out), flush=True)
 

@@ -455,3 +455,113 @@ def shared_prefix_decode(
         l2_last_page_len=l2_last, full_kv_indptr=full_indptr, full_kv_indices=full_idx,
         full_last_page_len=full_last, suffix_lens=suf, dtype=dtype,
     )
+
+
+@dataclass
+class CascadeBatch:
+    """L shared-prefix levels plus private suffixes: L + 1 BSR views over one KV pool.
+
+    Level ``i`` < L groups the R decode requests into ``groups[i]`` block rows of
+    R / groups[i] consecutive requests that share ``prefix_lens[i]`` tokens; a request's
+    context is level 0's prefix, then level 1's, ..., then its own suffix.
+    """
+
+    groups: tuple
+    prefix_lens: tuple
+    page_size: int
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+    q_f32: np.ndarray  # [R, H_qo, d]
+    k_f32: np.ndarray  # [num_pages, P, H_kv, d]
+    v_f32: np.ndarray
+    num_pages: int
+    levels: list  # per shared level: (qo_indptr, kv_indptr, kv_indices, last_page_len)
+    suffix: tuple  # (kv_indptr, kv_indices, last_page_len), one request per query
+    full: tuple  # single-level view: every request over all of its pages
+    suffix_lens: np.ndarray
+    dtype: str = "bf16"
+
+    @property
+    def requests(self):
+        return int(self.q_f32.shape[0])
+
+    def torch_values(self, device="cpu"):
+        import torch
+
+        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        return tuple(
+            torch.from_numpy(a).to(tdt).to(device) for a in (self.q_f32, self.k_f32, self.v_f32)
+        )
+
+
+def cascade_decode(
+    seed: int = 0,
+    requests: int = 64,
+    groups=(1, 16),
+    prefix_lens=(1024, 2048),
+    suffix_lo: int = 128,
+    suffix_hi: int = 1024,
+    page_size: int = 16,
+    num_qo_heads: int = 32,
+    num_kv_heads: int = 8,
+    head_dim: int = 128,
+    poison: bool = True,
+    dtype: str = "bf16",
+) -> CascadeBatch:
+    """Decode batch with a multi-level shared-prefix tree (the multi-level cascade of
+    "FlashInfer 原理", §⑤ and §F2): by default one 1024-token prompt shared by all 64
+    requests, 16 groups of 4 sharing a further 2048 tokens, and private suffixes
+    U[128, 1024].  Prefixes occupy full pages; all pages come from one random
+    permutation of the pool."""
+    assert len(groups) == len(prefix_lens)
+    rng = np.random.default_rng(seed)
+    R = requests
+    for g_, n_ in zip(groups, prefix_lens):
+        assert R % g_ == 0 and n_ % page_size == 0
+    suf = rng.integers(suffix_lo, suffix_hi, size=R, endpoint=True).astype(np.int32)
+    lvl_pages = [g_ * (n_ // page_size) for g_, n_ in zip(groups, prefix_lens)]
+    suf_pages = (suf + page_size - 1) // page_size
+    pool = sum(lvl_pages) + int(suf_pages.sum())
+    perm = rng.permutation(pool).astype(np.int64)
+    q = _round(rng.standard_normal((R, num_qo_heads, head_dim), dtype=np.float32), dtype)
+    fill = np.nan if poison else 0.0
+    k = np.full((pool, page_size, num_kv_heads, head_dim), fill, dtype=np.float32)
+    v = np.full_like(k, fill)
+    kf = k.reshape(-1, num_kv_heads, head_dim)
+    vf = v.reshape(-1, num_kv_heads, head_dim)
+
+    def fill_tokens(ids, n):
+        slots = (ids[:, None] * page_size + np.arange(page_size)[None, :]).reshape(-1)[:n]
+        kf[slots] = _round(rng.standard_normal((n, num_kv_heads, head_dim), dtype=np.float32), dtype)
+        vf[slots] = _round(rng.standard_normal((n, num_kv_heads, head_dim), dtype=np.float32), dtype)
+
+    off = 0
+    levels, level_ids = [], []
+    for g_, n_ in zip(groups, prefix_lens):
+        npg = n_ // page_size
+        ids = perm[off : off + g_ * npg].reshape(g_, npg)
+        off += g_ * npg
+        for gi in range(g_):
+            fill_tokens(ids[gi], n_)
+        qo = np.arange(0, R + 1, R // g_, dtype=np.int32)
+        ip, ix, la = page_table_from_lengths(np.full(g_, n_), page_size, ids.reshape(-1))
+        levels.append((qo, ip, ix, la))
+        level_ids.append(ids)
+    suf_lists = []
+    for r in range(R):
+        ids = perm[off : off + suf_pages[r]]
+        off += suf_pages[r]
+        suf_lists.append(ids)
+        fill_tokens(ids, int(suf[r]))
+    suffix = page_table_from_lengths(suf, page_size, np.concatenate(suf_lists))
+    full_ids = np.concatenate([
+        np.concatenate([level_ids[li][r // (R // g_)] for li, g_ in enumerate(groups)] + [suf_lists[r]])
+        for r in range(R)])
+    full = page_table_from_lengths(sum(prefix_lens) + suf.astype(np.int64), page_size, full_ids)
+    return CascadeBatch(
+        groups=tuple(groups), prefix_lens=tuple(prefix_lens), page_size=page_size,
+        num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+        q_f32=q, k_f32=k, v_f32=v, num_pages=pool, levels=levels, suffix=suffix, full=full,
+        suffix_lens=suf, dtype=dtype,
+    )

@@ -253,3 +253,29 @@ def composable_attention(
     )
     o, s = merge_state(o1, s1, o2, s2)
     return o, s, (o1, s1), (o2, s2)
+
+
+# ---------------------------------------------------------------------------
+# Multi-level cascade: shared-prefix levels plus private suffixes
+# ---------------------------------------------------------------------------
+
+
+def cascade_attention(q, k_cache, v_cache, levels, suffix, page_size, num_qo_heads, num_kv_heads, sm_scale):
+    """Attention over L + 1 BSR views of one KV pool folded left with the merge.
+
+    ``levels``: per shared level, (qo_indptr, kv_indptr, kv_indices, last_page_len) whose
+    block rows are groups of decode queries reading the same prefix pages (non-causal).
+    ``suffix``: (kv_indptr, kv_indices, last_page_len), one query per request.  The
+    multi-level cascade of "FlashInfer 原理" (§⑤: shared prefixes at several levels,
+    recombined with merge_state); the fold order is level 0, 1, ..., suffix.
+    Returns the folded (O, LSE) and the list of per-view states.
+    """
+    states = []
+    for qo, ip, ix, la in levels:
+        states.append(batch_attention(q, k_cache, v_cache, ip, ix, la, page_size, num_qo_heads,
+                                      num_kv_heads, sm_scale, qo_indptr=qo, causal=False))
+    ip, ix, la = suffix
+    states.append(batch_attention(q, k_cache, v_cache, ip, ix, la, page_size, num_qo_heads,
+                                  num_kv_heads, sm_scale, qo_indptr=None, causal=False))
+    o, s = fold_states(states)
+    return o, s, states

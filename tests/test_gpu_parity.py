@@ -231,3 +231,40 @@ def test_composable_shared_prefix():
     compare(o1.float().cpu().numpy(), l1.cpu().numpy(), ro1, rl1, "bf16", "composable level 1")
     compare(o2.float().cpu().numpy(), l2.cpu().numpy(), ro2, rl2, "bf16", "composable level 2")
     compare(o.float().cpu().numpy(), l.cpu().numpy(), ro, rl, "bf16", "composable merged")
+
+
+def test_cascade_three_levels():
+    """Multi-level cascade: a prompt shared by all 64 requests, group prefixes (16 x 4) and
+    private suffixes, as three BSR views merged left to right with merge_state."""
+    import torch
+    from block_sparse_paged_bsr_amd import api
+
+    b = I.cascade_decode(seed=0)
+    log(f"[cascade] groups={b.groups} prefixes={b.prefix_lens} suffix={b.suffix_lens.min()}..{b.suffix_lens.max()}")
+    q, k, v = b.torch_values("cuda")
+    sm = 1.0 / math.sqrt(b.head_dim)
+    C1 = api.query_num_workers("prefill", 32, 8, 128)
+    C2 = api.query_num_workers("decode", 32, 8, 128)
+    states = []
+    for qo, ip, ix, la in b.levels:
+        p = api.Plan(ip, ix, la, num_pages=b.num_pages, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                     page_size=b.page_size, qo_indptr=qo, causal=False, num_workers=C1)
+        w = api.alloc_workspace(p)
+        p.upload(w)
+        states.append(api.run_prefill(p, w, q, k, v, sm_scale=sm))
+    ip, ix, la = b.suffix
+    p = api.Plan(ip, ix, la, num_pages=b.num_pages, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                 page_size=b.page_size, num_workers=C2)
+    w = api.alloc_workspace(p)
+    p.upload(w)
+    states.append(api.run_decode(p, w, q, k, v, sm_scale=sm))
+    o, l = states[0]
+    for o2, l2 in states[1:]:
+        o, l = api.merge_state(o, l, o2, l2)
+    torch.cuda.synchronize()
+    ro, rl, rstates = A.cascade_attention(b.q_f32, b.k_f32, b.v_f32, b.levels, b.suffix, b.page_size, 32, 8, sm)
+    for i, ((og, lg), (orf, lrf)) in enumerate(zip(states, rstates)):
+        compare(og.float().cpu().numpy(), lg.cpu().numpy(), orf, lrf, "bf16", f"cascade view {i}")
+    compare(o.float().cpu().numpy(), l.cpu().numpy(), ro, rl, "bf16", "cascade merged")
+    uo, ul = A.batch_attention(b.q_f32, b.k_f32, b.v_f32, *b.full, b.page_size, 32, 8, sm)
+    compare(o.float().cpu().numpy(), l.cpu().numpy(), uo, ul, "bf16", "cascade vs union")

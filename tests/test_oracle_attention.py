@@ -200,3 +200,19 @@ def test_composable_equals_union():
     of, lf = A.batch_attention(b.q_f32, b.k_f32, b.v_f32, b.full_kv_indptr, b.full_kv_indices,
                                b.full_last_page_len, 4, 8, 2, 0.25)
     assert np.allclose(o, of, atol=1e-13, rtol=0) and np.allclose(l, lf, atol=1e-13, rtol=0)
+
+
+def test_cascade_three_levels_equals_union():
+    """Level 0 (one prompt for all) (+) level 1 (group prefixes) (+) private suffixes equals
+    single-level attention over the concatenated pages of each request (the union check)."""
+    b = I.cascade_decode(seed=1, requests=8, groups=(1, 4), prefix_lens=(12, 8), suffix_lo=0,
+                         suffix_hi=9, page_size=4, num_qo_heads=8, num_kv_heads=2, head_dim=16,
+                         dtype="f32")
+    o, l, states = A.cascade_attention(b.q_f32, b.k_f32, b.v_f32, b.levels, b.suffix, 4, 8, 2, 0.25)
+    assert len(states) == 3
+    of, lf = A.batch_attention(b.q_f32, b.k_f32, b.v_f32, *b.full, 4, 8, 2, 0.25)
+    assert np.allclose(o, of, atol=1e-13, rtol=0) and np.allclose(l, lf, atol=1e-13, rtol=0)
+    # an empty suffix leaves the prefix levels' state unchanged (the merge's identity)
+    empty = np.nonzero(b.suffix_lens == 0)[0]
+    for r in empty:
+        assert np.all(np.isneginf(states[2][1][r]))
