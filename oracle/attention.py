@@ -21,6 +21,11 @@ Definitions followed, by page:
   request with l_qo queries and l_kv keys may see key k iff k <= q + l_kv - l_qo
   (review §4.1; the sliding-window predicate in "FlashInfer 原理" §⑧ carries the same
   kv_len - qo_len offset).
+* Variants ("FlashInfer 原理" §⑧; review §5, eq. 8): a sliding window of
+  ``window_left`` keys lets query q see key k only if k >= q + l_kv - l_qo -
+  window_left (the lower half of the §⑧ predicate; the causal flag supplies the upper
+  half); a logits soft cap c > 0 replaces every score s = sm_scale q.k by c tanh(s / c)
+  before the mask decides which scores take part.
 
 Nothing here tiles, fuses or reorders: the score matrix of every (request, head) is
 materialised and each row goes through softmax on its own.
@@ -66,17 +71,20 @@ def physical_rows(kv_indptr, kv_indices, last_page_len, page_size, i):
 # ---------------------------------------------------------------------------
 
 
-def attention_one_head(q, k, v, sm_scale, allowed=None):
+def attention_one_head(q, k, v, sm_scale, allowed=None, soft_cap=0.0):
     """O and LSE of one head: materialise S, softmax each row.
 
     q: [Lq, d], k: [Lk, d], v: [Lk, dv]; allowed: bool [Lq, Lk] or None (all allowed).
-    A row with no allowed key is the empty state: O = 0, LSE = -inf.
+    soft_cap > 0 transforms the scores to soft_cap * tanh(S / soft_cap) (eq. 8) before
+    masking.  A row with no allowed key is the empty state: O = 0, LSE = -inf.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     Lq, Lk = q.shape[0], k.shape[0]
     S = float(sm_scale) * (q @ k.T) if Lk > 0 else np.zeros((Lq, 0))
+    if soft_cap > 0:
+        S = float(soft_cap) * np.tanh(S / float(soft_cap))
     if allowed is not None:
         S = np.where(allowed, S, NEG_INF)
     O = np.zeros((Lq, v.shape[1]), dtype=np.float64)
@@ -102,6 +110,14 @@ def causal_allowed(l_qo, l_kv):
     return kpos <= qpos + (l_kv - l_qo)
 
 
+def window_allowed(l_qo, l_kv, window_left):
+    """Sliding-window predicate ("FlashInfer 原理" §⑧): key k visible to query q iff
+    k + l_qo + window_left >= l_kv + q, i.e. k >= q + l_kv - l_qo - window_left."""
+    qpos = np.arange(l_qo)[:, None]
+    kpos = np.arange(l_kv)[None, :]
+    return kpos + l_qo + window_left >= l_kv + qpos
+
+
 # ---------------------------------------------------------------------------
 # Batched attention over a BSR / paged KV cache
 # ---------------------------------------------------------------------------
@@ -122,6 +138,8 @@ def batch_attention(
     causal=False,
     requests=None,
     query_subset=None,
+    window_left=-1,
+    soft_cap=0.0,
 ):
     """Attention of every (query, head) of a ragged batch over its own paged KV.
 
@@ -131,7 +149,8 @@ def batch_attention(
     float64; only rows of ``requests`` (default all) are filled, the rest stay NaN.
     ``query_subset`` maps a request to the query positions (0-based within the
     request) to evaluate; each query row is independent of the others, so a subset
-    is the same definition on fewer rows.
+    is the same definition on fewer rows.  ``window_left`` >= 0 adds the sliding-window
+    mask and ``soft_cap`` > 0 the score soft cap (module docstring).
     """
     assert num_qo_heads % num_kv_heads == 0
     g = num_qo_heads // num_kv_heads
@@ -154,13 +173,18 @@ def batch_attention(
         sel = np.arange(l_qo)
         if query_subset is not None and i in query_subset:
             sel = np.asarray(query_subset[i], dtype=np.int64)
-        allowed = causal_allowed(l_qo, l_kv)[sel] if causal else None
+        allowed = causal_allowed(l_qo, l_kv) if causal else None
+        if window_left >= 0:
+            win = window_allowed(l_qo, l_kv, window_left)
+            allowed = win if allowed is None else (allowed & win)
+        if allowed is not None:
+            allowed = allowed[sel]
         K_i = k_flat[rows].astype(np.float64)  # [l_kv, H_kv, d]
         V_i = v_flat[rows].astype(np.float64)
         for h in range(num_qo_heads):
             hk = h // g
             o, s = attention_one_head(
-                q[q0 + sel, h].astype(np.float64), K_i[:, hk], V_i[:, hk], sm_scale, allowed
+                q[q0 + sel, h].astype(np.float64), K_i[:, hk], V_i[:, hk], sm_scale, allowed, soft_cap
             )
             O[q0 + sel, h] = o
             lse[q0 + sel, h] = s

@@ -23,7 +23,9 @@ the query-tile set is {16, 32, 64, 128} (a tile is a multiple of the 16-row matr
 instruction; 128 when the average exceeds 64); the per-item cost charges the query
 positions of the item's own tile (one for a decode request, at most T_q / g for a
 prefill tile) plus its chunk length; chunks are counted in tokens and may start inside a page; a causal
-tile's visible KV range ends at the tile's last query position; ties in the heap go
+tile's visible KV range ends at the tile's last query position, and with a sliding window of
+w keys it starts at the window's start for the tile's first query position (the total work
+then sums the tiles' windowed ranges instead of eq. 10's full lengths); ties in the heap go
 to the lower worker id; a tile with exactly one chunk writes its final output, the
 chunks of split tiles get partial slots 0, 1, 2, ... in assignment order, and each
 split tile's reduction list orders its slots by KV start.
@@ -46,7 +48,8 @@ class Tile:
     req: int
     row_start: int  # packed rows [row_start, row_end) of the request
     row_end: int
-    vis: int  # visible KV length of the tile
+    vis: int  # end of the tile's visible KV range
+    lo: int = 0  # start of the tile's visible KV range (> 0 only with a sliding window)
     items: List[int] = field(default_factory=list)  # creation-order item ids
 
 
@@ -105,8 +108,12 @@ def make_plan(
     alpha=2,
     beta=1,
     causal=False,
+    window_left=-1,
 ):
-    """Build the partition for requests with the given query and KV lengths."""
+    """Build the partition for requests with the given query and KV lengths.
+
+    ``window_left`` >= 0: sliding window; the visible range of a tile starts at
+    max(0, l_kv - l_qo + first_pos - window_left) (its first row's window start)."""
     kv_lens = [int(x) for x in kv_lens]
     B = len(kv_lens)
     qo_lens = [1] * B if qo_lens is None else [int(x) for x in qo_lens]
@@ -128,17 +135,23 @@ def make_plan(
                 vis = max(0, min(kv_lens[i], kv_lens[i] - qo_lens[i] + last_pos + 1))
             else:
                 vis = kv_lens[i]
-            tiles.append(Tile(i, r0, r1, vis))
+            lo = 0
+            if window_left >= 0:
+                lo = min(vis, max(0, kv_lens[i] - qo_lens[i] + r0 // g - window_left))
+            tiles.append(Tile(i, r0, r1, vis, lo))
 
-    # total work (eq. 10) and the chunk limit
-    W = sum(ceil_div(pq[i], T) * kv_lens[i] for i in range(B))
+    # total work (eq. 10; with a window, the tiles' windowed ranges) and the chunk limit
+    if window_left >= 0:
+        W = sum(t.vis - t.lo for t in tiles)
+    else:
+        W = sum(ceil_div(pq[i], T) * kv_lens[i] for i in range(B))
     L = max(1, ceil_div(W, num_workers)) if (B > 0 and W > 0) else 0
 
     # work items: chunks of each tile's visible range, in creation order
     items: List[Item] = []
     if L > 0:
         for t_id, t in enumerate(tiles):
-            s = 0
+            s = t.lo
             while s < t.vis:
                 n = min(L, t.vis - s)
                 t.items.append(len(items))
