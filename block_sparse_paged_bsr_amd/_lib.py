@@ -46,6 +46,8 @@ class PlanDesc(C.Structure):
         ("tile_q", C.c_int32),
         ("alpha", C.c_int32),
         ("beta", C.c_int32),
+        ("window_left", C.c_int32),
+        ("logits_soft_cap", C.c_float),
     ]
 
 
@@ -74,6 +76,9 @@ class PlanView(C.Structure):
         ("merge_tiles", i32p),
         ("merge_ptr", i32p),
         ("merge_slots", i32p),
+        ("window_left", C.c_int32),
+        ("logits_soft_cap", C.c_float),
+        ("tile_lo", i32p),
     ]
 
 

@@ -58,6 +58,8 @@ class Plan:
         tile_q: int = 0,
         alpha: int = 2,
         beta: int = 1,
+        window_left: int = -1,
+        logits_soft_cap: float = 0.0,
     ):
         kv_indptr, p_ip = _i32(kv_indptr)
         kv_indices, p_ix = _i32(kv_indices)
@@ -82,6 +84,8 @@ class Plan:
             tile_q=int(tile_q),
             alpha=int(alpha),
             beta=int(beta),
+            window_left=int(window_left),
+            logits_soft_cap=float(logits_soft_cap),
         )
         h = C.c_void_p()
         check(lib().bsr_plan_create(C.byref(d), C.byref(h)))
@@ -148,6 +152,9 @@ class Plan:
             "merge_tiles": arr(v.merge_tiles, nm),
             "merge_ptr": merge_ptr,
             "merge_slots": arr(v.merge_slots, int(merge_ptr[-1]) if nm else 0),
+            "tile_lo": arr(v.tile_lo, v.num_tiles),
+            "window_left": v.window_left,
+            "logits_soft_cap": v.logits_soft_cap,
         }
 
 

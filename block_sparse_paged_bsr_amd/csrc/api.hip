@@ -109,6 +109,8 @@ RunArgs make_args(const bsr_plan* p, const void* ws) {
   a.causal = p->causal;
   a.num_merge = int32_t(p->merge_tiles.size());
   a.p_shift = p_shift_of(p->P);
+  a.window_left = p->window_left;
+  a.soft_cap = p->soft_cap;
   return a;
 }
 
@@ -270,6 +272,9 @@ int bsr_plan_export(const bsr_plan* p, bsr_plan_view* v) {
   v->merge_tiles = p->merge_tiles.data();
   v->merge_ptr = p->merge_ptr.data();
   v->merge_slots = p->merge_slots.data();
+  v->window_left = p->window_left;
+  v->logits_soft_cap = p->soft_cap;
+  v->tile_lo = p->tile_lo.data();
   return BSR_OK;
 }
 

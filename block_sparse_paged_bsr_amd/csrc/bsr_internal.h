@@ -62,6 +62,8 @@ struct bsr_plan {
   // description
   int32_t B = 0, Hq = 0, Hk = 0, d = 0, P = 1, causal = 0, C = 1, g = 1, Tq = 16;
   int32_t alpha = 2, beta = 1, num_pages = 0;
+  int32_t window_left = -1;  // sliding window: keys to the left of the diagonal, -1 = none
+  float soft_cap = 0.f;      // logits soft cap, 0 = none
   bool decode = true;  // qo_indptr == NULL
   std::vector<int32_t> qo_indptr, kv_indptr, kv_indices, last_page_len;
   std::vector<int32_t> qo_len, kv_len;
@@ -70,6 +72,7 @@ struct bsr_plan {
   // partition
   int64_t W = 0, L = 0;
   std::vector<int32_t> tiles;        // [num_tiles][5]
+  std::vector<int32_t> tile_lo;      // [num_tiles]: first visible key of each tile
   std::vector<int32_t> items;        // [num_items][8], creation order
   std::vector<int32_t> queue_ptr;    // [C+1]
   std::vector<int32_t> queue_items;  // [num_items]

@@ -22,12 +22,15 @@
 //           staged in a wave-private LDS tile and read back with the transposing
 //           LDS read of gfx950 (ds_read_b64_tr_b16, A operand).
 // A work item writes the final (O, LSE) or a partial state folded by the merge pass.
+// CAP: logits soft cap (eq. 8 of the review), each scaled score s becomes c tanh(s / c).  A
+// sliding window needs nothing here: all rows of a decode item share one query position, so
+// the planned chunks already start at the window.
 #include "common.cuh"
 #include "launch.h"
 
 namespace bsr {
 
-template <int D>
+template <int D, bool CAP>
 __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
   constexpr int KB = D / 32;  // k-blocks of the score product
   constexpr int DB = D / 16;  // d-blocks of the output product
@@ -37,7 +40,8 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
   const int w = blockIdx.x, hk = blockIdx.y;
   const int lane = threadIdx.x, n = lane & 15, j = lane >> 4;
   const int g = a.g;
-  const float c = a.sm_scale * kLog2e;
+  const float c = CAP ? a.sm_scale / a.soft_cap : a.sm_scale * kLog2e;
+  const float cap_l2 = a.soft_cap * kLog2e;
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
   const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
   const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
@@ -114,7 +118,8 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
       float mt = kNegInf;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s[i] = (t0 + 4 * j + i) < kv_end ? S[i] * c : kNegInf;
+        const float si = CAP ? cap_l2 * fast_tanh(S[i] * c) : S[i] * c;
+        s[i] = (t0 + 4 * j + i) < kv_end ? si : kNegInf;
         mt = fmaxf(mt, s[i]);
       }
       mt = fmaxf(mt, shfl_xor(mt, 16));
@@ -188,15 +193,18 @@ int decode_bf16_waves_per_kv_head(int) { return 1; }
 int decode_bf16_blocks_per_cu(int d, int) {
   int nb = 1;
   hipError_t e = hipErrorInvalidValue;
-  if (d == 64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<64>, 64, 0);
-  if (d == 128) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<128>, 64, 0);
+  if (d == 64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<64, false>, 64, 0);
+  if (d == 128) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<128, false>, 64, 0);
   return (e == hipSuccess && nb > 0) ? nb : 1;
 }
 
 hipError_t launch_decode_bf16(const RunArgs& a, hipStream_t s) {
   dim3 grid(a.C, a.Hk), block(64);
-  if (a.d == 64) hipLaunchKernelGGL(attn_decode_bf16_kernel<64>, grid, block, 0, s, a);
-  else if (a.d == 128) hipLaunchKernelGGL(attn_decode_bf16_kernel<128>, grid, block, 0, s, a);
+  const bool cap = a.soft_cap > 0.f;
+  if (a.d == 64 && cap) hipLaunchKernelGGL((attn_decode_bf16_kernel<64, true>), grid, block, 0, s, a);
+  else if (a.d == 64) hipLaunchKernelGGL((attn_decode_bf16_kernel<64, false>), grid, block, 0, s, a);
+  else if (a.d == 128 && cap) hipLaunchKernelGGL((attn_decode_bf16_kernel<128, true>), grid, block, 0, s, a);
+  else if (a.d == 128) hipLaunchKernelGGL((attn_decode_bf16_kernel<128, false>), grid, block, 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

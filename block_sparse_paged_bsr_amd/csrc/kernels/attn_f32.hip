@@ -8,6 +8,9 @@
 // "FlashInfer: Engineering a Customizable, Block-Sparse Attention Engine for LLM
 // Inference Serving" (§II.2) and writes either the final (O, LSE) or a partial
 // state for the merge pass.
+// Variants ("FlashInfer 原理" §⑧; eq. 8 of the review): a sliding window raises the first
+// visible key of each row, and a logits soft cap c replaces each scaled score s by
+// c tanh(s / c) before the softmax.
 #include "common.cuh"
 #include "launch.h"
 
@@ -17,7 +20,11 @@ template <int D>
 __global__ __launch_bounds__(64) void attn_f32_kernel(RunArgs a) {
   constexpr int EPL = (D + 63) / 64;  // elements per lane
   const int w = blockIdx.x, hk = blockIdx.y, lane = threadIdx.x;
-  const float c = a.sm_scale * kLog2e;  // scores kept in log2 units
+  // scores kept in log2 units; with a soft cap the dot product is taken with q sm_scale / c
+  // and the score is c log2(e) tanh(.)
+  const bool capped = a.soft_cap > 0.f;
+  const float c = capped ? a.sm_scale / a.soft_cap : a.sm_scale * kLog2e;
+  const float cap_l2 = a.soft_cap * kLog2e;
   const float* __restrict__ Q = static_cast<const float*>(a.q);
   const float* __restrict__ K = static_cast<const float*>(a.k);
   const float* __restrict__ V = static_cast<const float*>(a.v);
@@ -39,8 +46,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(RunArgs a) {
       }
       int kend = item.kv_end;
       if (a.causal) kend = min(kend, rq.kv_len - rq.q_len + pos + 1);
+      int kbeg = item.kv_start;
+      if (a.window_left >= 0) kbeg = max(kbeg, rq.kv_len - rq.q_len + pos - a.window_left);
       float m = kNegInf, l = 0.f;
-      for (int t = item.kv_start; t < kend; ++t) {
+      for (int t = kbeg; t < kend; ++t) {
         const int64_t base = (page_row(a.indices, rq.page_start, t, a.P, a.p_shift) * a.Hk + hk) * D;
         float s = 0.f;
 #pragma unroll
@@ -49,6 +58,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(RunArgs a) {
           if (idx < D) s += qv[e] * K[base + idx];
         }
         s = wave_sum(s);
+        if (capped) s = cap_l2 * tanhf(s);
         const float mn = fmaxf(m, s);
         const float corr = exp2f(m - mn);
         const float p = exp2f(s - mn);

@@ -49,6 +49,12 @@
 // tile has fewer row blocks than waves, waves also split the tile's tokens and their
 // states are combined at the end of the item with the merge of eq. 6 (§3.2 of the
 // review).
+//
+// Variants ("FlashInfer 原理" §⑧; eq. 8 of the review) run in a separate instantiation of the
+// 4-wave kernel (VAR), for every tile size: the soft cap turns each score s into
+// (c / sm_scale) tanh(sm_scale s / c) before the mask (the softmax then multiplies by
+// sm_scale log2(e) as usual), and a sliding window adds a per-row lower bound to the mask.
+#include <climits>
 #include <type_traits>
 
 #include "common.cuh"
@@ -411,7 +417,27 @@ __device__ __forceinline__ float raise_reference(float& m, float mx_scaled, bool
 // Otherwise (33-64 rows): two row blocks, each shared by two waves that take the two
 // 32-token halves of every 64-token tile of the plain loop.
 // ---------------------------------------------------------------------------------
-template <int D, bool PIPE, int PG>
+// Per-row state of the variants: the first key the sliding window shows this row (INT_MIN
+// without a window), the largest such key over the item's rows (uniform; KV blocks that
+// start before it need the lower-bound test) and the soft cap as S -> k1 tanh(k2 S).
+struct VarRow {
+  int lo = INT_MIN, max_lo = INT_MIN;
+  float k1 = 0.f, k2 = 0.f;
+  __device__ __forceinline__ VarRow(const RunArgs& a, const ItemRec& item, const ReqRec& rq, int row_pos) {
+    if (a.window_left >= 0) {
+      const int base = rq.kv_len - rq.q_len - a.window_left;
+      lo = base + row_pos;
+      max_lo = __builtin_amdgcn_readfirstlane(base + (item.row_end - 1) / a.g);
+    }
+    if (a.soft_cap > 0.f) {
+      k1 = a.soft_cap / a.sm_scale;
+      k2 = a.sm_scale / a.soft_cap;
+    }
+  }
+  __device__ __forceinline__ float cap(float s) const { return k1 * fast_tanh(k2 * s); }
+};
+
+template <int D, bool PIPE, int PG, bool VAR>
 __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& item, const ReqRec& rq, int hk,
                                                const Slots<D>& sl) {
   constexpr int KB = PF<D>::KB, FRAG = PF<D>::FRAG;
@@ -437,6 +463,7 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
   const bool row_ok = r < item.row_end;
   const int row_pos = r / a.g, row_hq = hk * a.g + r % a.g;
   const int lim = (a.causal && row_ok) ? min(kv_end, rq.kv_len - rq.q_len + row_pos + 1) : kv_end;
+  const VarRow var(a, item, rq, row_pos);
   bf16x8 qb[KS16];
   {
     const uint16_t* qp = Q + (int64_t(rq.q_start + row_pos) * a.Hq + row_hq) * D + 8 * h;
@@ -483,7 +510,19 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
   // causal mask of the block whose tile starts at t0 (only where it reaches past the first
   // row's limit)
   auto mask = [&](f32x16& S, int t0) {
-    if (t0 + 32 * (ks + 1) > min_lim) {
+    if constexpr (VAR) {
+      if (var.k1 > 0.f) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[i] = var.cap(S[i]);
+      }
+      if (t0 + 32 * (ks + 1) > min_lim || t0 + 32 * ks < var.max_lo) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int tok = t0 + 32 * ks + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (tok >= lim || tok < var.lo) S[i] = kNegInf;
+        }
+      }
+    } else if (t0 + 32 * (ks + 1) > min_lim) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int tok = t0 + 32 * ks + 8 * (i >> 2) + 4 * h + (i & 3);
@@ -828,7 +867,7 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
 // Small query tiles (<= 32 rows): 16-row blocks on v_mfma_f32_16x16x32_bf16.
 // NT: 16-token blocks of a tile per wave (2: two waves per row block, 1: four).
 // ---------------------------------------------------------------------------------
-template <int D, int NT, bool POW2>
+template <int D, int NT, bool POW2, bool VAR>
 __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& item, const ReqRec& rq, int hk,
                                                const Slots<D>& sl) {
   constexpr int KB = PF<D>::KB, DB = D / 16, FRAG = PF<D>::FRAG;
@@ -850,6 +889,7 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
   const bool row_ok = r < item.row_end;
   const int row_pos = r / a.g, row_hq = hk * a.g + r % a.g;
   const int lim = (a.causal && row_ok) ? min(kv_end, rq.kv_len - rq.q_len + row_pos + 1) : kv_end;
+  const VarRow var(a, item, rq, row_pos);
   bf16x8 qb[KB];
   {
     const uint16_t* qp = Q + (int64_t(rq.q_start + row_pos) * a.Hq + row_hq) * D + j * 8;
@@ -886,7 +926,23 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
         S[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[kb], S[b], 0, 0, 0);
       }
     }
-    if (t0 + kTileKV > min_lim) {
+    if constexpr (VAR) {
+      if (var.k1 > 0.f) {
+#pragma unroll
+        for (int b = 0; b < NT; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[b][i] = var.cap(S[b][i]);
+      }
+      if (t0 + kTileKV > min_lim || t0 < var.max_lo) {
+#pragma unroll
+        for (int b = 0; b < NT; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = t0 + (ks * NT + b) * 16 + 4 * j + i;
+            if (tok >= lim || tok < var.lo) S[b][i] = kNegInf;
+          }
+      }
+    } else if (t0 + kTileKV > min_lim) {
 #pragma unroll
       for (int b = 0; b < NT; ++b)
 #pragma unroll
@@ -1354,7 +1410,7 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
 
 }  // namespace
 
-template <int D, int PG>
+template <int D, int PG, bool VAR>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_bf16_kernel(RunArgs a) {
   constexpr bool POW2 = PG != kPageAny;
@@ -1371,10 +1427,10 @@ void attn_prefill_bf16_kernel(RunArgs a) {
     const ItemRec item = uniform_load(a.items + it);
     const ReqRec rq = uniform_load(a.req + item.req);
     const int rows = item.row_end - item.row_start;
-    if (rows > 64) prefill_item32<D, true, PG>(a, item, rq, hk, sl);        // 3-4 blocks of 32 rows, pipelined
-    else if (rows > 32) prefill_item32<D, false, PG>(a, item, rq, hk, sl);  // 2 blocks, tokens split
-    else if (rows > 16) prefill_item16<D, 2, POW2>(a, item, rq, hk, sl);  // 2 blocks of 16 rows
-    else prefill_item16<D, 1, POW2>(a, item, rq, hk, sl);                 // 1 block, tokens split 4 ways
+    if (rows > 64) prefill_item32<D, true, PG, VAR>(a, item, rq, hk, sl);        // 3-4 blocks of 32 rows, pipelined
+    else if (rows > 32) prefill_item32<D, false, PG, VAR>(a, item, rq, hk, sl);  // 2 blocks, tokens split
+    else if (rows > 16) prefill_item16<D, 2, POW2, VAR>(a, item, rq, hk, sl);  // 2 blocks of 16 rows
+    else prefill_item16<D, 1, POW2, VAR>(a, item, rq, hk, sl);                 // 1 block, tokens split 4 ways
   }
 }
 
@@ -1400,25 +1456,31 @@ int prefill_bf16_blocks_per_cu(int d) {
   // every page-size variant uses the same resources; ask for one of them
   int nb = 1;
   hipError_t e = hipErrorInvalidValue;
-  if (d == 64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_prefill_bf16_kernel<64, kPageDiv32>, kThreads, 0);
-  if (d == 128) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_prefill_bf16_kernel<128, kPageDiv32>, kThreads, 0);
+  if (d == 64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_prefill_bf16_kernel<64, kPageDiv32, false>, kThreads, 0);
+  if (d == 128) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_prefill_bf16_kernel<128, kPageDiv32, false>, kThreads, 0);
   return (e == hipSuccess && nb > 0) ? nb : 1;
 }
 
 template <int D>
 static void launch_d(const RunArgs& a, dim3 grid, hipStream_t s) {
   const bool div32 = a.p_shift >= 0 && a.P <= 32, pow2 = a.p_shift >= 0;
-  if (a.Tq == 128) {  // 128-row tiles: two waves of two row blocks each
-    const dim3 block(kThreads2);
-    if (div32) hipLaunchKernelGGL((attn_prefill128_bf16_kernel<D, kPageDiv32>), grid, block, 0, s, a);
-    else if (pow2) hipLaunchKernelGGL((attn_prefill128_bf16_kernel<D, kPagePow2>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_prefill128_bf16_kernel<D, kPageAny>), grid, block, 0, s, a);
+  const dim3 block(kThreads);
+  if (a.window_left >= 0 || a.soft_cap > 0.f) {  // variants: the 4-wave shapes, any tile size
+    if (div32) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPageDiv32, true>), grid, block, 0, s, a);
+    else if (pow2) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPagePow2, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPageAny, true>), grid, block, 0, s, a);
     return;
   }
-  const dim3 block(kThreads);
-  if (div32) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPageDiv32>), grid, block, 0, s, a);
-  else if (pow2) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPagePow2>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPageAny>), grid, block, 0, s, a);
+  if (a.Tq == 128) {  // 128-row tiles: two waves of two row blocks each
+    const dim3 block2(kThreads2);
+    if (div32) hipLaunchKernelGGL((attn_prefill128_bf16_kernel<D, kPageDiv32>), grid, block2, 0, s, a);
+    else if (pow2) hipLaunchKernelGGL((attn_prefill128_bf16_kernel<D, kPagePow2>), grid, block2, 0, s, a);
+    else hipLaunchKernelGGL((attn_prefill128_bf16_kernel<D, kPageAny>), grid, block2, 0, s, a);
+    return;
+  }
+  if (div32) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPageDiv32, false>), grid, block, 0, s, a);
+  else if (pow2) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPagePow2, false>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPageAny, false>), grid, block, 0, s, a);
 }
 
 hipError_t launch_prefill_bf16(const RunArgs& a, hipStream_t s) {

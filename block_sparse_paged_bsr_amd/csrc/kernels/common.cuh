@@ -37,6 +37,8 @@ struct RunArgs {
   int32_t B, Hq, Hk, g, d, P, Tq, C, causal, num_merge;
   int32_t p_shift;  // log2(page_size) when the page size is a power of two, else -1
   float sm_scale;
+  int32_t window_left;  // sliding window (keys left of the diagonal), -1 = none
+  float soft_cap;       // logits soft cap c (score -> c tanh(score / c)), 0 = none
 };
 
 // ---- bf16 <-> fp32 ----
@@ -52,6 +54,13 @@ __device__ __forceinline__ uint32_t f2bf_bits(float f) {
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f2bf_bits(lo) | (f2bf_bits(hi) << 16);
+}
+
+// tanh(x) = sign(x) (1 - e) / (1 + e) with e = exp(-2 |x|) in (0, 1]: one hardware exp2 and
+// one reciprocal, no overflow for any |x|, absolute error a few 1e-7 (used by the soft cap)
+__device__ __forceinline__ float fast_tanh(float x) {
+  const float e = __builtin_amdgcn_exp2f(-2.f * kLog2e * __builtin_fabsf(x));
+  return __builtin_copysignf((1.f - e) * __builtin_amdgcn_rcpf(1.f + e), x);
 }
 
 // ---- paging: physical token row of logical token t of a request (eq. 7) ----

@@ -52,6 +52,9 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
     return fail("tile_q must be 0 or a multiple of 16 up to 128");
   if (desc->alpha < 0 || desc->beta < 0) return fail("alpha and beta must be >= 0");
   if (desc->num_pages < 0) return fail("num_pages must be >= 0");
+  if (desc->window_left < -1) return fail("window_left must be -1 (no window) or >= 0");
+  if (!(desc->logits_soft_cap >= 0.f) || desc->logits_soft_cap == __builtin_huge_valf())
+    return fail("logits_soft_cap must be 0 (off) or positive and finite");
   if (B > 0 && (!desc->kv_indptr || !desc->last_page_len))
     return fail("kv_indptr and last_page_len are required");
 
@@ -70,6 +73,8 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
     p->beta = 1;
   }
   p->num_pages = desc->num_pages;
+  p->window_left = desc->window_left;
+  p->soft_cap = desc->logits_soft_cap;
   p->decode = desc->qo_indptr == nullptr;
 
   // ---- copy and validate the BSR arrays ----
@@ -147,7 +152,12 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
   const int32_t Tq = p->Tq;
 
   // ---- query tiles and their visible KV ranges ----
+  // A tile sees keys [lo, vis): vis ends at the causal limit of its last query position;
+  // with a sliding window of w keys to the left, lo is the window start of its first
+  // query position ("FlashInfer 原理" §⑧: key k is visible to query q of a request iff
+  // k + l_qo + w >= l_kv + q), clipped to [0, vis].
   p->tiles.clear();
+  p->tile_lo.clear();
   for (int32_t i = 0; i < B; ++i) {
     const int64_t nt = ceil_div(pq[i], Tq);
     for (int64_t j = 0; j < nt; ++j) {
@@ -157,14 +167,24 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
       if (p->causal)
         vis = std::max<int64_t>(0, std::min<int64_t>(p->kv_len[i],
                                                      int64_t(p->kv_len[i]) - p->qo_len[i] + last_pos + 1));
+      int64_t lo = 0;
+      if (p->window_left >= 0)
+        lo = std::min<int64_t>(vis, std::max<int64_t>(0, int64_t(p->kv_len[i]) - p->qo_len[i] + r0 / p->g -
+                                                             p->window_left));
       p->tiles.insert(p->tiles.end(), {i, int32_t(r0), int32_t(r1), int32_t(vis), 0});
+      p->tile_lo.push_back(int32_t(lo));
     }
   }
   const int32_t num_tiles = int32_t(p->tiles.size() / 5);
 
-  // ---- total work (eq. 10) and chunk limit ----
+  // ---- total work (eq. 10; with a window, the sum of the tiles' windowed ranges) and
+  // chunk limit ----
   int64_t W = 0;
-  for (int32_t i = 0; i < B; ++i) W += ceil_div(pq[i], Tq) * p->kv_len[i];
+  if (p->window_left >= 0) {
+    for (int32_t t = 0; t < num_tiles; ++t) W += p->tiles[5 * t + 3] - p->tile_lo[t];
+  } else {
+    for (int32_t i = 0; i < B; ++i) W += ceil_div(pq[i], Tq) * p->kv_len[i];
+  }
   p->W = W;
   p->L = (B > 0 && W > 0) ? std::max<int64_t>(1, ceil_div(W, p->C)) : 0;
 
@@ -177,7 +197,7 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
   if (p->L > 0) {
     for (int32_t t = 0; t < num_tiles; ++t) {
       const int32_t* tr = &p->tiles[5 * t];
-      for (int64_t s = 0; s < tr[3]; s += p->L) {
+      for (int64_t s = p->tile_lo[t]; s < tr[3]; s += p->L) {
         const int32_t n = int32_t(std::min<int64_t>(p->L, tr[3] - s));
         tile_items[t].push_back(int32_t(items.size()));
         items.push_back({tr[0], t, tr[1], tr[2], int32_t(s), n, -1, -1});

@@ -78,6 +78,17 @@ typedef struct bsr_plan_desc {
   int32_t tile_q;               /* packed query rows per tile; 0 => tile rule */
   int32_t alpha, beta;          /* item cost = alpha * (query positions of its tile) +
                                    beta * chunk_len; both 0 => (2, 1) */
+  int32_t window_left;          /* sliding window: -1 = none (note: a zero-filled
+                                   description asks for a window of 0, which keeps only
+                                   the diagonal key); w >= 0 => key k is visible to query q
+                                   only if k + l_qo + w >= l_kv + q, i.e. the w keys left of
+                                   q's aligned position and that position itself
+                                   ("FlashInfer 原理" §⑧, the mask of the window variant).
+                                   Combines with causal, which supplies the upper bound. */
+  float logits_soft_cap;        /* 0 = none; c > 0 => every score s = sm_scale * q.k is
+                                   replaced by c * tanh(s / c) before masking and softmax
+                                   ("FlashInfer: Making Attention Fit the Serving Workload"
+                                   §5, eq. 8).  Must be finite. */
 } bsr_plan_desc;
 
 /*
@@ -89,6 +100,8 @@ typedef struct bsr_plan_desc {
  *   T_q = tile_q or the smallest of {16, 32, 64, 128} >= ceil(sum pq_i / B);
  *   W = sum_i ceil(pq_i / T_q) * l_kv(i);  chunk limit L = max(1, ceil(W / C));
  *   each query tile's visible KV range is cut into chunks of at most L tokens;
+ *   with a sliding window a tile's range starts at the window start of its first query
+ *   position, and W is the sum of the tiles' windowed range lengths instead;
  *   chunks are stably sorted by length, descending, and each goes to the worker of
  *   least accumulated cost (ties: lower worker id); an item costs alpha times the query
  *   positions of its tile (1 in decode) plus beta times its chunk length (eq. 11).  A tile with one chunk writes its
@@ -132,6 +145,7 @@ int bsr_plan_upload(bsr_plan* plan, void* dev_ws, size_t ws_bytes, void* stream)
  *   merge_tiles[num_merge]: tiles written by the merge pass (split or empty), creation
  *                           order; merge_ptr[num_merge+1], merge_slots[]: their slots
  *                           in fold order (ascending kv_start)
+ *   tile_lo[num_tiles]    = first visible key of each tile (> 0 only with a window)
  */
 typedef struct bsr_plan_view {
   int32_t batch, num_qo_heads, num_kv_heads, head_dim, page_size, causal;
@@ -148,6 +162,9 @@ typedef struct bsr_plan_view {
   const int32_t* merge_tiles;
   const int32_t* merge_ptr;
   const int32_t* merge_slots;
+  int32_t window_left;
+  float logits_soft_cap;
+  const int32_t* tile_lo;
 } bsr_plan_view;
 
 int bsr_plan_export(const bsr_plan* plan, bsr_plan_view* view);

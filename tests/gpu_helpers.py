@@ -15,13 +15,13 @@ def log(msg):
     sys.stdout.flush()
 
 
-def make_plan(b, num_workers=64, tile_q=0, causal=None, qo_indptr="auto"):
+def make_plan(b, num_workers=64, tile_q=0, causal=None, qo_indptr="auto", window_left=-1, soft_cap=0.0):
     qo = b.qo_indptr if qo_indptr == "auto" else qo_indptr
     return api.Plan(
         b.kv_indptr, b.kv_indices, b.last_page_len, num_pages=b.num_pages,
         num_qo_heads=b.num_qo_heads, num_kv_heads=b.num_kv_heads, head_dim=b.head_dim,
         page_size=b.page_size, qo_indptr=qo, causal=b.causal if causal is None else causal,
-        num_workers=num_workers, tile_q=tile_q,
+        num_workers=num_workers, tile_q=tile_q, window_left=window_left, logits_soft_cap=soft_cap,
     )
 
 
@@ -37,11 +37,12 @@ def run_gpu(b, p, decode=None, tensors=None):
     return o.float().cpu().numpy(), lse.cpu().numpy(), ws
 
 
-def oracle(b, requests=None, query_subset=None, causal=None):
+def oracle(b, requests=None, query_subset=None, causal=None, window_left=-1, soft_cap=0.0):
     return A.batch_attention(
         b.q_f32, b.k_f32, b.v_f32, b.kv_indptr, b.kv_indices, b.last_page_len, b.page_size,
         b.num_qo_heads, b.num_kv_heads, 1.0 / math.sqrt(b.head_dim), qo_indptr=b.qo_indptr,
         causal=b.causal if causal is None else causal, requests=requests, query_subset=query_subset,
+        window_left=window_left, soft_cap=soft_cap,
     )
 
 

@@ -53,6 +53,7 @@ def _oracle_as_export(p):
         "num_slots": p.num_slots, "group_size": p.group_size, "tiles": tiles, "items": items,
         "queue_ptr": qptr, "queue_items": qitems, "worker_cost": np.array(p.worker_cost, dtype=np.int64),
         "merge_tiles": np.array(p.merge_tiles, dtype=np.int32), "merge_ptr": mptr, "merge_slots": mslots,
+        "tile_lo": np.array([t.lo for t in p.tiles], dtype=np.int32),
     }
 
 
@@ -66,13 +67,13 @@ def _assert_same(lib_plan, oracle_plan):
             assert a[k] == v, k
 
 
-def _lib_plan(kv_lens, qo_lens, Hq, Hk, C_, P=16, tq=0, causal=False, alpha=2, beta=1, d=128):
+def _lib_plan(kv_lens, qo_lens, Hq, Hk, C_, P=16, tq=0, causal=False, alpha=2, beta=1, d=128, window_left=-1):
     kv_lens = np.asarray(kv_lens, dtype=np.int64)
     ip, ix, last = I.page_table_from_lengths(kv_lens, P, np.arange(int(((kv_lens + P - 1) // P).sum())))
     qo = None if qo_lens is None else np.concatenate([[0], np.cumsum(qo_lens)])
     return api.Plan(ip, ix, last, num_pages=max(len(ix), 1), num_qo_heads=Hq, num_kv_heads=Hk,
                     head_dim=d, page_size=P, qo_indptr=qo, causal=causal, num_workers=C_,
-                    tile_q=tq, alpha=alpha, beta=beta)
+                    tile_q=tq, alpha=alpha, beta=beta, window_left=window_left)
 
 
 @pytest.mark.parametrize("alpha,beta", [(0, 1), (2, 1)])
@@ -101,6 +102,42 @@ def test_random_plans_bit_exact(seed):
     lp = _lib_plan(kv, qo, Hk * g, Hk, C_, P=P, tq=tq, causal=causal, alpha=alpha, beta=beta)
     op = PL.make_plan(kv, qo, Hk * g, Hk, C_, tile_q=tq, causal=causal, alpha=alpha, beta=beta)
     _assert_same(lp, op)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_window_plans_bit_exact(seed):
+    """Sliding-window plans ("FlashInfer 原理" §⑧): tiles start at their first row's window,
+    the total work sums the windowed ranges, chunks start at each tile's first visible key."""
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 12))
+    kv = rng.integers(0, 3000, size=B)
+    qo = None if rng.random() < 0.3 else rng.integers(1, 300, size=B)
+    if qo is not None:
+        kv = np.maximum(kv, qo)  # queries are the last positions of their request
+    Hk = int(rng.choice([1, 2, 8]))
+    g = int(rng.choice([1, 4, 8]))
+    C_ = int(rng.integers(1, 300))
+    tq = int(rng.choice([0, 16, 64, 128]))
+    causal = bool(rng.random() < 0.7) and qo is not None
+    w = int(rng.choice([0, 1, 31, 127, 1000, 5000]))
+    P = int(rng.choice([1, 16]))
+    lp = _lib_plan(kv, qo, Hk * g, Hk, C_, P=P, tq=tq, causal=causal, window_left=w)
+    op = PL.make_plan(kv, qo, Hk * g, Hk, C_, tile_q=tq, causal=causal, window_left=w)
+    _assert_same(lp, op)
+    e = lp.export()
+    assert e["window_left"] == w and e["logits_soft_cap"] == 0.0
+    assert e["total_work"] == int((e["tiles"][:, 3] - e["tile_lo"]).sum())
+
+
+def test_soft_cap_leaves_the_plan_unchanged():
+    lens = I.decode_lengths(2)[:40]
+    a = _lib_plan(lens, None, 32, 8, 64).export()
+    b = api.Plan(*I.page_table_from_lengths(np.asarray(lens), 16, np.arange(int(((np.asarray(lens) + 15) // 16).sum()))),
+                 num_pages=int(((np.asarray(lens) + 15) // 16).sum()), num_qo_heads=32, num_kv_heads=8,
+                 head_dim=128, page_size=16, num_workers=64, logits_soft_cap=30.0).export()
+    assert b["logits_soft_cap"] == 30.0
+    for k in ("tiles", "items", "queue_items", "merge_slots", "tile_lo"):
+        assert np.array_equal(a[k], b[k]), k
 
 
 def test_workload_plans_bit_exact():
@@ -141,11 +178,15 @@ def _desc_errors():
         dict(tile_q=24),
         dict(qo_indptr=[0, 2, 1]),
         dict(qo_indptr=[1, 2, 3]),
+        dict(window_left=-2),
+        dict(logits_soft_cap=-1.0),
+        dict(logits_soft_cap=float("nan")),
+        dict(logits_soft_cap=float("inf")),
     ]
     return good, cases
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(16))
 def test_invalid_descriptions(i):
     good, cases = _desc_errors()
     kw = dict(good)
