@@ -104,23 +104,23 @@ def kernel_times(fn, n):
             t["merge_ms"] / max(t["merge_launches"], 1), t["merge_launches"])
 
 
-def make_plan(b, kind, causal=False):
+def make_plan(b, kind, causal=False, **variant):
     from block_sparse_paged_bsr_amd import api
 
     C = api.query_num_workers(kind, H_QO, H_KV, D)
     return api.Plan(b.kv_indptr, b.kv_indices, b.last_page_len, num_pages=b.num_pages,
                     num_qo_heads=H_QO, num_kv_heads=H_KV, head_dim=D, page_size=b.page_size,
-                    qo_indptr=b.qo_indptr, causal=causal, num_workers=C)
+                    qo_indptr=b.qo_indptr, causal=causal, num_workers=C, **variant)
 
 
-def run_case(b, kind, steps, warmup, rotate=1, causal=False):
+def run_case(b, kind, steps, warmup, rotate=1, causal=False, **variant):
     """Plan once, upload, then time steps of run_decode / run_prefill."""
     import torch
     from block_sparse_paged_bsr_amd import api
 
     q, k, v = b.torch_values("cuda")
     t0 = time.perf_counter()
-    p = make_plan(b, kind, causal)
+    p = make_plan(b, kind, causal, **variant)
     plan_us = (time.perf_counter() - t0) * 1e6
     ws = api.alloc_workspace(p)
     p.upload(ws)
@@ -188,6 +188,48 @@ def bench_prefill(args):
     fl = prefill_flops(b.kv_lens)
     return {"ms": r["ms"], "tflops": fl / (r["ms"] * 1e-3) / 1e12, "flops": fl, "attn_kernel_ms": attn_ms,
             "merge_kernel_ms": merge_ms, "num_workers": r["num_workers"], "batch": b}
+
+
+def windowed_prefill_flops(lens, w):
+    """Flops over the visible pairs of causal prefill with a window of w keys to the left:
+    query position p (0-based, q_len = kv_len) sees min(p + 1, w + 1) keys."""
+    tot = 0.0
+    for l in lens:
+        l = int(l)
+        full = min(l, w + 1)  # positions 0 .. full-1 see p + 1 keys
+        tot += full * (full + 1) / 2 + (l - full) * (w + 1)
+    return 4.0 * D * H_QO * tot
+
+
+def bench_variants(args):
+    """The attention variants on the headline workloads: logits soft cap 50 and a 4096-key
+    sliding window on batch-64 decode; soft cap 50, a 1024-key window, and both, on the
+    ragged causal prefill.  Rates count only the visible KV (window) or pairs."""
+    from block_sparse_paged_bsr_amd import inputs
+
+    out = {}
+    b = inputs.batched_decode_bf16(seed=0, poison=False)
+    nnz = len(b.kv_indices)
+    for name, var, lens in (("decode_soft_cap50", dict(logits_soft_cap=50.0), b.kv_lens),
+                            ("decode_window4096", dict(window_left=4095), np.minimum(b.kv_lens, 4096))):
+        r = run_case(b, "decode", args.steps, args.warmup, rotate=3, **var)
+        attn_ms, _, merge_ms, _ = kernel_times(r["step"], 20)
+        nbytes = decode_bytes(lens, b.batch, nnz if "window" not in name else int(np.sum((lens + 15) // 16)))
+        out[name] = {"us": round(r["ms"] * 1e3, 2), "gbs": round(nbytes / (r["ms"] * 1e-3) / 1e9, 1),
+                     "attn_kernel_us": round(attn_ms * 1e3, 2), "merge_kernel_us": round(merge_ms * 1e3, 2),
+                     "bytes": nbytes}
+        del r
+    pb = inputs.ragged_prefill_bf16(seed=0, poison=False)
+    for name, var, fl in (("prefill_soft_cap50", dict(logits_soft_cap=50.0), prefill_flops(pb.kv_lens)),
+                          ("prefill_window1024", dict(window_left=1024), windowed_prefill_flops(pb.kv_lens, 1024)),
+                          ("prefill_window1024_soft_cap50", dict(window_left=1024, logits_soft_cap=50.0),
+                           windowed_prefill_flops(pb.kv_lens, 1024))):
+        r = run_case(pb, "prefill", max(10, args.steps // 2), 10, causal=True, **var)
+        attn_ms, _, merge_ms, _ = kernel_times(r["step"], 10)
+        out[name] = {"ms": round(r["ms"], 4), "tflops": round(fl / (r["ms"] * 1e-3) / 1e12, 1),
+                     "attn_kernel_ms": round(attn_ms, 4), "merge_kernel_ms": round(merge_ms, 4), "flops": fl}
+        del r
+    return out
 
 
 def bench_vector_sparse(args):
@@ -406,7 +448,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="decode only, no CPU baseline")
-    ap.add_argument("--only", choices=["decode", "prefill", "vector", "composable", "cascade"], default=None)
+    ap.add_argument("--only", choices=["decode", "prefill", "vector", "composable", "cascade", "variants"],
+                    default=None)
     ap.add_argument("--copy-calib", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -432,6 +475,9 @@ def main():
         return
     if args.only == "cascade":
         log(json.dumps(bench_cascade(args)))
+        return
+    if args.only == "variants":
+        log(json.dumps(bench_variants(args)))
         return
     dec = bench_decode(args)
     log(f"decode: {dec['ms']*1e3:.1f} us/step, {dec['gbs']:.0f} GB/s; attn kernel "
@@ -467,7 +513,7 @@ def main():
     ach = dec["bytes"] / (dec["attn_kernel_ms"] * 1e-3) / 1e9
     out["roofline"] = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                       "kernel": "attn_decode_bf16_kernel<128>",
+                       "kernel": "attn_decode_bf16_kernel<128, false>",
                        "kernel_avg_us": round(dec["attn_kernel_ms"] * 1e3, 2),
                        "merge_avg_us": round(dec["merge_kernel_ms"] * 1e3, 2)}
     if not args.quick:
@@ -493,6 +539,10 @@ def main():
         cc = bench_cascade(args)
         log(f"cascade: {cc}")
         out["cascade"] = cc
+        torch.cuda.empty_cache()
+        va = bench_variants(args)
+        log(f"variants: {va}")
+        out["variants"] = va
         out["cpu_baseline"] = cpu_baseline(dec)
     print(json.dumps(out), flush=True)
 

@@ -50,8 +50,8 @@
 // states are combined at the end of the item with the merge of eq. 6 (§3.2 of the
 // review).
 //
-// Variants ("FlashInfer 原理" §⑧; eq. 8 of the review) run in a separate instantiation of the
-// 4-wave kernel (VAR), for every tile size: the soft cap turns each score s into
+// Variants ("FlashInfer 原理" §⑧; eq. 8 of the review) run in separate instantiations (VAR): the
+// sliding window in both kernels, the soft cap in the 4-wave one.  The soft cap turns each score s into
 // (c / sm_scale) tanh(sm_scale s / c) before the mask (the softmax then multiplies by
 // sm_scale log2(e) as usual), and a sliding window adds a per-row lower bound to the mask.
 #include <climits>
@@ -1080,7 +1080,7 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
 // run the online softmax of tile j, for both row blocks.  Absent rows (past the end of a
 // short tile) carry zero queries and are never written.
 // ---------------------------------------------------------------------------------
-template <int D, int PG>
+template <int D, int PG, bool VAR>
 __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec& item, const ReqRec& rq, int hk,
                                                 const Slots<D>& sl) {
   constexpr int KB = PF<D>::KB, FRAG = PF<D>::FRAG;
@@ -1120,6 +1120,7 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
   int min_lim = kv_end;  // tiles ending before the smallest visible end need no mask
   if (a.causal) min_lim = min(kv_end, rq.kv_len - rq.q_len + item.row_start / a.g + 1);
   min_lim = __builtin_amdgcn_readfirstlane(min_lim);
+  const VarRow var[2] = {VarRow(a, item, rq, row_pos[0]), VarRow(a, item, rq, row_pos[1])};
 
   // running references (log2 units, from a finite floor), sums and rescale factors per block
   float m[2] = {kMFloor, kMFloor}, l[2] = {0.f, 0.f}, corr[2] = {1.f, 1.f};
@@ -1160,8 +1161,19 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
     }
   };
   // causal mask of the tile starting at t0 (only where it reaches past the first row's limit)
+  // (with VAR also below the sliding window's first key; soft-capped plans never come here)
   auto mask = [&](f32x16 (&S)[2], int t0) {
-    if (t0 + 32 > min_lim) {
+    if constexpr (VAR) {
+      if (t0 + 32 > min_lim || t0 < var[0].max_lo) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int tok = t0 + 8 * (i >> 2) + 4 * h + (i & 3);
+            if (tok >= lim[b] || tok < var[b].lo) S[b][i] = kNegInf;
+          }
+      }
+    } else if (t0 + 32 > min_lim) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -1435,7 +1447,7 @@ void attn_prefill_bf16_kernel(RunArgs a) {
 }
 
 // The 128-row shape: every item of a plan whose query tile is 128 rows.
-template <int D, int PG>
+template <int D, int PG, bool VAR>
 __global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_prefill128_bf16_kernel(RunArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[Slots<D>::BYTES];
@@ -1446,7 +1458,7 @@ void attn_prefill128_bf16_kernel(RunArgs a) {
   for (int it = uniform_load(a.qptr + w); it < it_end; ++it) {
     const ItemRec item = uniform_load(a.items + it);
     const ReqRec rq = uniform_load(a.req + item.req);
-    prefill_item128<D, PG>(a, item, rq, hk, sl);
+    prefill_item128<D, PG, VAR>(a, item, rq, hk, sl);
   }
 }
 
@@ -1461,26 +1473,31 @@ int prefill_bf16_blocks_per_cu(int d) {
   return (e == hipSuccess && nb > 0) ? nb : 1;
 }
 
+// VAR: the variant instantiations (sliding window, soft cap).  Soft-capped plans use the 4-wave
+// shapes for every tile size: their two waves per SIMD overlap the extra exponential and
+// reciprocal of each capped score with the other wave's matrix work, where the single wave per
+// SIMD of the 128-row shape runs them in series (measured 573 against 542 TFLOP/s on the ragged
+// causal prefill with a cap of 50).
+template <int D, bool VAR>
+static void launch_pg(const RunArgs& a, dim3 grid, hipStream_t s, bool div32, bool pow2) {
+  if (a.Tq == 128 && !(VAR && a.soft_cap > 0.f)) {  // 128-row tiles: two waves of two row blocks each
+    const dim3 block(kThreads2);
+    if (div32) hipLaunchKernelGGL((attn_prefill128_bf16_kernel<D, kPageDiv32, VAR>), grid, block, 0, s, a);
+    else if (pow2) hipLaunchKernelGGL((attn_prefill128_bf16_kernel<D, kPagePow2, VAR>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_prefill128_bf16_kernel<D, kPageAny, VAR>), grid, block, 0, s, a);
+    return;
+  }
+  const dim3 block(kThreads);
+  if (div32) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPageDiv32, VAR>), grid, block, 0, s, a);
+  else if (pow2) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPagePow2, VAR>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPageAny, VAR>), grid, block, 0, s, a);
+}
+
 template <int D>
 static void launch_d(const RunArgs& a, dim3 grid, hipStream_t s) {
   const bool div32 = a.p_shift >= 0 && a.P <= 32, pow2 = a.p_shift >= 0;
-  const dim3 block(kThreads);
-  if (a.window_left >= 0 || a.soft_cap > 0.f) {  // variants: the 4-wave shapes, any tile size
-    if (div32) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPageDiv32, true>), grid, block, 0, s, a);
-    else if (pow2) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPagePow2, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPageAny, true>), grid, block, 0, s, a);
-    return;
-  }
-  if (a.Tq == 128) {  // 128-row tiles: two waves of two row blocks each
-    const dim3 block2(kThreads2);
-    if (div32) hipLaunchKernelGGL((attn_prefill128_bf16_kernel<D, kPageDiv32>), grid, block2, 0, s, a);
-    else if (pow2) hipLaunchKernelGGL((attn_prefill128_bf16_kernel<D, kPagePow2>), grid, block2, 0, s, a);
-    else hipLaunchKernelGGL((attn_prefill128_bf16_kernel<D, kPageAny>), grid, block2, 0, s, a);
-    return;
-  }
-  if (div32) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPageDiv32, false>), grid, block, 0, s, a);
-  else if (pow2) hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPagePow2, false>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((attn_prefill_bf16_kernel<D, kPageAny, false>), grid, block, 0, s, a);
+  if (a.window_left >= 0 || a.soft_cap > 0.f) launch_pg<D, true>(a, grid, s, div32, pow2);
+  else launch_pg<D, false>(a, grid, s, div32, pow2);
 }
 
 hipError_t launch_prefill_bf16(const RunArgs& a, hipStream_t s) {

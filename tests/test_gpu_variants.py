@@ -54,7 +54,8 @@ PREFILL_VAR = [
     ([300, 17, 64, 129], [300, 17, 64, 129], 16, 8, 2, 128, True, 40, 0, -1, 2.5),
     ([300, 17, 64, 129], [300, 17, 64, 129], 16, 8, 2, 128, False, 3, 0, 70, 4.0),
     ([500, 40], [7, 40], 4, 8, 8, 64, True, 5, 0, 0, 0.0),          # diagonal only
-    ([700, 260], [700, 260], 16, 32, 8, 128, True, 100, 128, 100, 3.0),  # 128-row tiles
+    ([700, 260], [700, 260], 16, 32, 8, 128, True, 100, 128, 100, 3.0),  # 128-row tiles, capped
+    ([700, 260], [700, 260], 16, 32, 8, 128, True, 100, 128, 100, 0.0),  # 128-row shape, window
     ([700, 260], [700, 260], 16, 32, 8, 128, True, 13, 64, 333, 0.0),   # 64-row tiles
     ([250, 90], [250, 90], 1, 12, 4, 128, True, 11, 32, 31, 1.5),       # page size 1, g = 3
     ([20, 100], [50, 3], 16, 4, 1, 128, True, 4, 16, 5, 2.0),           # l_qo > l_kv: empty rows
@@ -88,14 +89,16 @@ def test_variants_fp32(decode):
     compare(o, l, ro, rl, "f32", "fp32 variant")
 
 
-def test_prefill_variants_ragged_full_sampled():
+@pytest.mark.parametrize("cap", [5.0, 0.0])
+def test_prefill_variants_ragged_full_sampled(cap):
     """Ragged causal prefill at full size (batch 16, lengths U[256, 4096]) with a 1024-key
-    window and a soft cap of 5; sampled rows of every request against the oracle."""
+    window, with and without a soft cap of 5; sampled rows of every request against the
+    oracle."""
     from block_sparse_paged_bsr_amd import api
 
     b = I.ragged_prefill_bf16(seed=0)
     C_ = api.query_num_workers("prefill", 32, 8, 128)
-    w, cap = 1024, 5.0
+    w = 1024
     log(f"[prefill_variants_ragged_full] lens={b.kv_lens.tolist()} workers={C_} window={w} cap={cap}")
     p = make_plan(b, num_workers=C_, window_left=w, soft_cap=cap)
     o, l, _ = run_gpu(b, p)
