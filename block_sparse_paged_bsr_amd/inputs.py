@@ -33,6 +33,8 @@ __all__ = [
     "ragged_prefill_bf16",
     "vector_sparse_pair",
     "shared_prefix_decode",
+    "E4m3Batch",
+    "to_e4m3",
 ]
 
 
@@ -565,3 +567,47 @@ def cascade_decode(
         q_f32=q, k_f32=k, v_f32=v, num_pages=pool, levels=levels, suffix=suffix, full=full,
         suffix_lens=suf, dtype=dtype,
     )
+
+
+@dataclass
+class E4m3Batch:
+    """A paged batch whose K and V are stored as E4M3 bytes (OCP "FN" encoding) with one
+    float scale per tensor: byte b stands for value(b) * scale.  Q stays in the base
+    batch's dtype."""
+
+    base: PagedBatch
+    k_bytes: np.ndarray  # uint8 [num_pages, P, H_kv, d]
+    v_bytes: np.ndarray  # uint8 [num_pages, P, H_kv, d]
+    k_scale: float
+    v_scale: float
+
+    def torch_values(self, device="cpu"):
+        """Q (base dtype), K and V bytes (uint8) as torch tensors."""
+        import torch
+
+        q = self.base.torch_values(device)[0]
+        return q, torch.from_numpy(self.k_bytes).to(device), torch.from_numpy(self.v_bytes).to(device)
+
+
+def to_e4m3(b: PagedBatch, k_scale: Optional[float] = None, v_scale: Optional[float] = None) -> E4m3Batch:
+    """Store a batch's K and V as E4M3 bytes.
+
+    Default scales are the per-tensor amax / 448 of the referenced tokens (so the largest
+    value lands on the format's largest finite value); the bytes are torch's
+    float8_e4m3fn rounding (nearest even) of value / scale, clamped to +-448.  Unused
+    (poisoned) slots stay NaN (byte 0x7f).  Input construction only: the oracle decodes
+    the bytes with its own decoder.
+    """
+    import torch
+
+    def enc(x, scale):
+        finite = np.isfinite(x)
+        amax = float(np.max(np.abs(x[finite]))) if finite.any() else 1.0
+        sc = float(scale) if scale is not None else (amax / 448.0 if amax > 0 else 1.0)
+        y = np.clip(x / np.float32(sc), -448.0, 448.0)  # NaN stays NaN
+        t = torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32)).to(torch.float8_e4m3fn)
+        return t.view(torch.uint8).numpy().copy(), sc
+
+    kb, ks = enc(b.k_f32, k_scale)
+    vb, vs = enc(b.v_f32, v_scale)
+    return E4m3Batch(base=b, k_bytes=kb, v_bytes=vb, k_scale=ks, v_scale=vs)
