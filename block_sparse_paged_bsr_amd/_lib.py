@@ -89,6 +89,7 @@ EXPORTED = [
     "bsr_plan_upload",
     "bsr_plan_export",
     "bsr_run_decode",
+    "bsr_run_decode_e4m3",
     "bsr_run_prefill",
     "bsr_merge_state",
     "bsr_debug_gather_rows",
@@ -129,6 +130,9 @@ def lib():
     L.bsr_run_decode.restype = C.c_int
     L.bsr_run_prefill.argtypes = run_args
     L.bsr_run_prefill.restype = C.c_int
+    L.bsr_run_decode_e4m3.argtypes = [vp, vp, vp, vp, vp, vp, C.POINTER(C.c_float), C.c_float, C.c_float,
+                                      C.c_float, vp]
+    L.bsr_run_decode_e4m3.restype = C.c_int
     fp = C.POINTER(C.c_float)
     L.bsr_merge_state.argtypes = [vp, fp, vp, fp, vp, fp, C.c_int64, C.c_int32, C.c_int32, C.c_int32, vp]
     L.bsr_merge_state.restype = C.c_int

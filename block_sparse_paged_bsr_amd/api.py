@@ -213,6 +213,40 @@ def run_prefill(p: Plan, ws, q, k_cache, v_cache, o=None, lse=None, sm_scale=Non
     return _run(lib().bsr_run_prefill, p, ws, q, k_cache, v_cache, o, lse, sm_scale, stream)
 
 
+def run_decode_e4m3(p: Plan, ws, q, k_cache, v_cache, k_scale: float, v_scale: float, o=None, lse=None,
+                    sm_scale=None, stream=None):
+    """bsr_run_decode_e4m3: decode over E4M3 K/V bytes (uint8 tensors [num_pages, P, H_kv, d])
+    with per-tensor scales; Q and O bf16; returns (O, LSE)."""
+    import torch
+
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(p.head_dim)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[0], p.num_qo_heads, dtype=torch.float32, device=q.device)
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("o", o), ("lse", lse)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if q.dtype != torch.bfloat16 or o.dtype != torch.bfloat16 or lse.dtype != torch.float32:
+        raise TypeError("q and o must be bfloat16 and lse float32")
+    if k_cache.dtype not in (torch.uint8, torch.float8_e4m3fn) or v_cache.dtype != k_cache.dtype:
+        raise TypeError("k_cache/v_cache must hold E4M3 bytes (uint8 or float8_e4m3fn)")
+    if tuple(q.shape) != (p.total_q, p.num_qo_heads, p.head_dim) or q.shape != o.shape:
+        raise ValueError(f"q/o shape {tuple(q.shape)} != {(p.total_q, p.num_qo_heads, p.head_dim)}")
+    if k_cache.shape[-2:] != (p.num_kv_heads, p.head_dim) or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache/v_cache must be [num_pages, page_size, num_kv_heads, head_dim]")
+    check(
+        lib().bsr_run_decode_e4m3(
+            p.handle, C.c_void_p(ws.data_ptr()), C.c_void_p(q.data_ptr()), C.c_void_p(k_cache.data_ptr()),
+            C.c_void_p(v_cache.data_ptr()), C.c_void_p(o.data_ptr()),
+            C.cast(C.c_void_p(lse.data_ptr()), C.POINTER(C.c_float)), float(sm_scale), float(k_scale),
+            float(v_scale), _stream(stream),
+        )
+    )
+    return o, lse
+
+
 def merge_state(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, stream=None):
     """bsr_merge_state: (O_a, LSE_a) (+) (O_b, LSE_b) for [rows, heads, d] states."""
     import torch

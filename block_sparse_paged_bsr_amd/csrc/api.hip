@@ -111,19 +111,29 @@ RunArgs make_args(const bsr_plan* p, const void* ws) {
   a.p_shift = p_shift_of(p->P);
   a.window_left = p->window_left;
   a.soft_cap = p->soft_cap;
+  a.k_scale = 1.f;
+  a.v_scale = 1.f;
   return a;
 }
 
+bool positive_finite(float x) { return x > 0.f && x != __builtin_huge_valf(); }
+
+// kv_e4m3: K and V are E4M3 bytes with per-tensor scales (decode only; Q and O are bf16)
 int run_common(const bsr_plan* p, const void* ws, const void* q, const void* k, const void* v,
-               void* o, float* lse, int32_t dtype, float sm_scale, void* stream, bool decode_call) {
+               void* o, float* lse, int32_t dtype, float sm_scale, void* stream, bool decode_call,
+               bool kv_e4m3 = false, float k_scale = 1.f, float v_scale = 1.f) {
   if (!p) return invalid("plan is NULL");
   if (!ws) return invalid("workspace is NULL");
   if (ws != p->uploaded_ws) return invalid("workspace was not uploaded for this plan (call bsr_plan_upload first)");
   if (dtype != BSR_DTYPE_F32 && dtype != BSR_DTYPE_BF16) return invalid("unknown dtype");
   if (decode_call && !p->decode)
     return invalid("bsr_run_decode needs a plan with one query per request (qo_indptr == NULL); use bsr_run_prefill");
-  if (!(sm_scale > 0.f) || sm_scale == __builtin_huge_valf())
-    return invalid("sm_scale must be positive and finite");
+  if (!positive_finite(sm_scale)) return invalid("sm_scale must be positive and finite");
+  if (kv_e4m3 && !(positive_finite(k_scale) && positive_finite(v_scale)))
+    return invalid("k_scale and v_scale must be positive and finite");
+  if (kv_e4m3 && !decode_bf16_supported(p->d, p->g, p->Tq))
+    return unsupported("e4m3 KV decode needs head_dim 64 or 128 and at most 16 query heads per KV head "
+                       "(and a query tile of at least that many rows)");
   if (p->B == 0) return BSR_OK;
   if (!q || !k || !v || !o || !lse) return invalid("q, k_cache, v_cache, o and lse must be non-NULL");
   const bool any_tokens = p->total_kv_tokens > 0;
@@ -135,17 +145,21 @@ int run_common(const bsr_plan* p, const void* ws, const void* q, const void* k, 
   a.o = o;
   a.lse = lse;
   a.sm_scale = sm_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
 
   hipError_t e = hipSuccess;
   if (!p->items.empty()) {
     hipEvent_t t0 = timing_start(s);
-    if (dtype == BSR_DTYPE_F32) {
+    if (kv_e4m3) {
+      e = launch_decode_bf16(a, true, s);
+    } else if (dtype == BSR_DTYPE_F32) {
       if (!attn_f32_supported(p->d)) return unsupported("fp32 head_dim must be one of 16, 32, 64, 128, 256");
       e = launch_attn_f32(a, s);
     } else {
       const bool dec_ok = p->decode && decode_bf16_supported(p->d, p->g, p->Tq);
       if (dec_ok) {
-        e = launch_decode_bf16(a, s);
+        e = launch_decode_bf16(a, false, s);
       } else {
         if (!prefill_bf16_supported(p->d, p->Tq)) return unsupported("bf16 head_dim must be 64 or 128");
         e = launch_prefill_bf16(a, s);
@@ -282,6 +296,13 @@ int bsr_run_decode(const bsr_plan* plan, const void* ws, const void* q, const vo
                    const void* v_cache, void* o, float* lse, int32_t dtype, float sm_scale,
                    void* stream) {
   return run_common(plan, ws, q, k_cache, v_cache, o, lse, dtype, sm_scale, stream, true);
+}
+
+int bsr_run_decode_e4m3(const bsr_plan* plan, const void* ws, const void* q, const void* k_cache,
+                        const void* v_cache, void* o, float* lse, float sm_scale, float k_scale,
+                        float v_scale, void* stream) {
+  return run_common(plan, ws, q, k_cache, v_cache, o, lse, BSR_DTYPE_BF16, sm_scale, stream, true, true,
+                    k_scale, v_scale);
 }
 
 int bsr_run_prefill(const bsr_plan* plan, const void* ws, const void* q, const void* k_cache,

@@ -25,26 +25,46 @@
 // CAP: logits soft cap (eq. 8 of the review), each scaled score s becomes c tanh(s / c).  A
 // sliding window needs nothing here: all rows of a decode item share one query position, so
 // the planned chunks already start at the window.
+// KV8: K and V stored as E4M3 bytes (OCP "FN" encoding) with one scale per tensor, the e4m3
+// KV cache of the review's vLLM integration (Appendix G.4).  A lane's 16-byte load then holds
+// 16 values of a row (two k-blocks of the score product; Q is loaded in the same order), and
+// v_cvt_pk_f32_fp8 widens them exactly (every E4M3 value is a bf16 value, so the high halves of
+// the fp32 results are the bf16 operands).  The K scale is folded into the score scale and the
+// V scale into the output normalisation, so the loop does no extra multiplications; the bytes
+// read per token are half of bf16's.
 #include "common.cuh"
 #include "launch.h"
 
 namespace bsr {
 
-template <int D, bool CAP>
+// four E4M3 bytes -> four bf16 values (exact), as two packed pairs
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  return u32x2{(__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xffff0000u),
+               (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xffff0000u)};
+}
+
+template <int D, bool CAP, bool KV8>
 __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
   constexpr int KB = D / 32;  // k-blocks of the score product
   constexpr int DB = D / 16;  // d-blocks of the output product
   constexpr int VS = D + 8;   // LDS row stride (elements); 16-byte aligned rows
+  constexpr int ES = KV8 ? 1 : 2;                // bytes per K/V element
+  constexpr int NL = KV8 ? D / 64 : D / 32;      // 16-byte loads per row and lane (64 j-apart bytes)
   __shared__ __attribute__((aligned(16))) uint16_t Vs[16 * VS];
 
   const int w = blockIdx.x, hk = blockIdx.y;
   const int lane = threadIdx.x, n = lane & 15, j = lane >> 4;
   const int g = a.g;
-  const float c = CAP ? a.sm_scale / a.soft_cap : a.sm_scale * kLog2e;
+  const float qk_scale = KV8 ? a.sm_scale * a.k_scale : a.sm_scale;  // K's scale joins the score scale
+  const float c = CAP ? qk_scale / a.soft_cap : qk_scale * kLog2e;
   const float cap_l2 = a.soft_cap * kLog2e;
+  const float o_scale = KV8 ? a.v_scale : 1.f;
   const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* __restrict__ K = static_cast<const uint16_t*>(a.k);
-  const uint16_t* __restrict__ V = static_cast<const uint16_t*>(a.v);
+  const uint8_t* __restrict__ K = static_cast<const uint8_t*>(a.k);
+  const uint8_t* __restrict__ V = static_cast<const uint8_t*>(a.v);
   uint16_t* __restrict__ O = static_cast<uint16_t*>(a.o);
   const int head_col = n < g ? n : n % g;  // query head offset served by column n
 
@@ -53,11 +73,15 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
     const ReqRec rq = a.req[item.req];
     const int kv_end = item.kv_end;
 
-    // Q^T as the B operand: column n = query head hk*g + head_col
-    const uint16_t* qp = Q + (int64_t(rq.q_start) * a.Hq + hk * g + head_col) * D + j * 8;
+    // Q^T as the B operand: column n = query head hk*g + head_col; k-block kb covers the
+    // head-dim values this lane's K slice of that block holds
+    const uint16_t* qp = Q + (int64_t(rq.q_start) * a.Hq + hk * g + head_col) * D;
     bf16x8 qb[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) qb[kb] = *reinterpret_cast<const bf16x8*>(qp + kb * 32);
+    for (int kb = 0; kb < KB; ++kb) {
+      const int col = KV8 ? 64 * (kb >> 1) + 16 * j + 8 * (kb & 1) : 32 * kb + 8 * j;
+      qb[kb] = *reinterpret_cast<const bf16x8*>(qp + col);
+    }
 
     float m = kNegInf, l = 0.f;
     f32x4 oacc[DB];
@@ -71,19 +95,20 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
       const int tc = min(t, kv_end - 1);
       return a.indices[pg_start + (a.p_shift >= 0 ? (tc >> a.p_shift) : tc / a.P)];
     };
+    // byte offset of this lane's first 16-byte piece of token t's row
     auto row_base = [&](int t, int32_t page) -> int64_t {
       const int tc = min(t, kv_end - 1);
       const int off = a.p_shift >= 0 ? (tc & ((1 << a.p_shift) - 1)) : tc - (tc / a.P) * a.P;
-      return ((int64_t(page) * a.P + off) * a.Hk + hk) * D + j * 8;
+      return ((int64_t(page) * a.P + off) * a.Hk + hk) * (D * ES) + j * 16;
     };
     int32_t pg_next = page_of(item.kv_start + 16 + n);
-    u32x4 kr[KB], vr[KB];
+    u32x4 kr[NL], vr[NL];
     {
       const int64_t base = row_base(item.kv_start + n, page_of(item.kv_start + n));
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        kr[kb] = *reinterpret_cast<const u32x4*>(K + base + kb * 32);
-        vr[kb] = *reinterpret_cast<const u32x4*>(V + base + kb * 32);
+      for (int l = 0; l < NL; ++l) {
+        kr[l] = *reinterpret_cast<const u32x4*>(K + base + 64 * l);
+        vr[l] = *reinterpret_cast<const u32x4*>(V + base + 64 * l);
       }
     }
 
@@ -91,13 +116,13 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
       const bool has_next = t0 + 16 < kv_end;
       const int32_t pg_after = page_of(t0 + 32 + n);
       // request the next step's rows before touching this step's data
-      u32x4 kn[KB], vn[KB];
+      u32x4 kn[NL], vn[NL];
       if (has_next) {
         const int64_t base = row_base(t0 + 16 + n, pg_next);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          kn[kb] = *reinterpret_cast<const u32x4*>(K + base + kb * 32);
-          vn[kb] = *reinterpret_cast<const u32x4*>(V + base + kb * 32);
+        for (int l = 0; l < NL; ++l) {
+          kn[l] = *reinterpret_cast<const u32x4*>(K + base + 64 * l);
+          vn[l] = *reinterpret_cast<const u32x4*>(V + base + 64 * l);
         }
       }
       pg_next = pg_after;
@@ -105,13 +130,32 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
       // scores S^T[token 4j+i][head n]
       f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[kb]), qb[kb], S, 0, 0, 0);
+      for (int kb = 0; kb < KB; ++kb) {
+        u32x4 ka;
+        if constexpr (KV8) {
+          const u32x4 w = kr[kb >> 1];
+          const u32x2 x0 = e4m3x4_to_bf16x4(w[2 * (kb & 1)]), x1 = e4m3x4_to_bf16x4(w[2 * (kb & 1) + 1]);
+          ka = u32x4{x0[0], x0[1], x1[0], x1[1]};
+        } else {
+          ka = kr[kb];
+        }
+        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka), qb[kb], S, 0, 0, 0);
+      }
 
-      // stage V rows (token n) for the transposing read below
+      // stage V rows (token n) as bf16 for the transposing read below
       __syncthreads();
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) *reinterpret_cast<u32x4*>(Vs + n * VS + kb * 32 + j * 8) = vr[kb];
+      for (int l = 0; l < NL; ++l) {
+        if constexpr (KV8) {
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const u32x2 x0 = e4m3x4_to_bf16x4(vr[l][2 * hb]), x1 = e4m3x4_to_bf16x4(vr[l][2 * hb + 1]);
+            *reinterpret_cast<u32x4*>(Vs + n * VS + 64 * l + 16 * j + 8 * hb) = u32x4{x0[0], x0[1], x1[0], x1[1]};
+          }
+        } else {
+          *reinterpret_cast<u32x4*>(Vs + n * VS + 32 * l + 8 * j) = vr[l];
+        }
+      }
       __syncthreads();
 
       float s[4];
@@ -150,9 +194,9 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
 
       if (has_next) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          kr[kb] = kn[kb];
-          vr[kb] = vn[kb];
+        for (int l = 0; l < NL; ++l) {
+          kr[l] = kn[l];
+          vr[l] = vn[l];
         }
       }
     }
@@ -163,7 +207,7 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
     if (n < g) {
       const int hq = hk * g + n;
       const bool empty = !(l > 0.f);
-      const float inv = empty ? 0.f : 1.f / l;
+      const float inv = empty ? 0.f : o_scale / l;
       const float lse = empty ? kNegInf : (m + log2f(l)) * kLn2;
       if (item.slot < 0) {
         uint16_t* op = O + (int64_t(rq.q_start) * a.Hq + hq) * D + 4 * j;
@@ -193,18 +237,23 @@ int decode_bf16_waves_per_kv_head(int) { return 1; }
 int decode_bf16_blocks_per_cu(int d, int) {
   int nb = 1;
   hipError_t e = hipErrorInvalidValue;
-  if (d == 64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<64, false>, 64, 0);
-  if (d == 128) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<128, false>, 64, 0);
+  if (d == 64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<64, false, false>, 64, 0);
+  if (d == 128) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<128, false, false>, 64, 0);
   return (e == hipSuccess && nb > 0) ? nb : 1;
 }
 
-hipError_t launch_decode_bf16(const RunArgs& a, hipStream_t s) {
-  dim3 grid(a.C, a.Hk), block(64);
-  const bool cap = a.soft_cap > 0.f;
-  if (a.d == 64 && cap) hipLaunchKernelGGL((attn_decode_bf16_kernel<64, true>), grid, block, 0, s, a);
-  else if (a.d == 64) hipLaunchKernelGGL((attn_decode_bf16_kernel<64, false>), grid, block, 0, s, a);
-  else if (a.d == 128 && cap) hipLaunchKernelGGL((attn_decode_bf16_kernel<128, true>), grid, block, 0, s, a);
-  else if (a.d == 128) hipLaunchKernelGGL((attn_decode_bf16_kernel<128, false>), grid, block, 0, s, a);
+template <int D, bool KV8>
+static void launch_cap(const RunArgs& a, dim3 grid, hipStream_t s) {
+  if (a.soft_cap > 0.f) hipLaunchKernelGGL((attn_decode_bf16_kernel<D, true, KV8>), grid, dim3(64), 0, s, a);
+  else hipLaunchKernelGGL((attn_decode_bf16_kernel<D, false, KV8>), grid, dim3(64), 0, s, a);
+}
+
+hipError_t launch_decode_bf16(const RunArgs& a, bool kv_e4m3, hipStream_t s) {
+  const dim3 grid(a.C, a.Hk);
+  if (a.d == 64 && kv_e4m3) launch_cap<64, true>(a, grid, s);
+  else if (a.d == 64) launch_cap<64, false>(a, grid, s);
+  else if (a.d == 128 && kv_e4m3) launch_cap<128, true>(a, grid, s);
+  else if (a.d == 128) launch_cap<128, false>(a, grid, s);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -39,6 +39,7 @@ struct RunArgs {
   float sm_scale;
   int32_t window_left;  // sliding window (keys left of the diagonal), -1 = none
   float soft_cap;       // logits soft cap c (score -> c tanh(score / c)), 0 = none
+  float k_scale, v_scale;  // per-tensor scales of an E4M3 KV cache (1 otherwise)
 };
 
 // ---- bf16 <-> fp32 ----

@@ -16,9 +16,10 @@ bool prefill_bf16_supported(int d, int Tq);
 hipError_t launch_prefill_bf16(const RunArgs& a, hipStream_t s);
 int prefill_bf16_blocks_per_cu(int d);
 
-// bf16 paged decode: MFMA scores, GQA-fused, split-KV partials.
+// bf16 paged decode: MFMA scores, GQA-fused, split-KV partials.  kv_e4m3: K and V are E4M3
+// bytes with per-tensor scales (RunArgs::k_scale, v_scale); Q and O stay bf16.
 bool decode_bf16_supported(int d, int g, int Tq);
-hipError_t launch_decode_bf16(const RunArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const RunArgs& a, bool kv_e4m3, hipStream_t s);
 int decode_bf16_blocks_per_cu(int d, int g);
 int decode_bf16_waves_per_kv_head(int g);
 

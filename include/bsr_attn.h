@@ -188,6 +188,22 @@ int bsr_run_decode(const bsr_plan* plan, const void* ws, const void* q, const vo
                    void* stream);
 
 /*
+ * Paged decode over an E4M3 KV cache: as bsr_run_decode with bf16 Q and O, but k_cache and
+ * v_cache hold one byte per element in the OCP 8-bit float "E4M3FN" encoding (sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; S.1111.111 is NaN; largest finite 448) and
+ * every stored value stands for value * k_scale (K) or value * v_scale (V), one scale per
+ * tensor.  Layout [num_pages, page_size, H_kv, d] bytes, "NHD".  Decode with an e4m3 KV
+ * cache is the configuration of the vLLM integration in "FlashInfer: Making Attention Fit
+ * the Serving Workload" (Appendix G.4, Table 8); the pages leave the encoding and scaling
+ * open, and this is the OCP format with per-tensor scales.  k_scale and v_scale must be
+ * positive and finite.  Supported where the bf16 decode kernel is (head_dim 64 or 128, at
+ * most 16 query heads per KV head), else BSR_UNSUPPORTED.  Reads half the KV bytes of bf16.
+ */
+int bsr_run_decode_e4m3(const bsr_plan* plan, const void* ws, const void* q, const void* k_cache,
+                        const void* v_cache, void* o, float* lse, float sm_scale, float k_scale,
+                        float v_scale, void* stream);
+
+/*
  * Ragged (optionally causal) prefill.  Same arguments as bsr_run_decode but Q and O
  * are [qo_indptr[B], H_qo, d] (packed, no padding) and the causal flag comes from the
  * plan.  A non-causal plan whose "requests" are groups of queries sharing pages is
