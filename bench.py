@@ -232,6 +232,37 @@ def bench_variants(args):
     return out
 
 
+def bench_e4m3(args, num_workers=None):
+    """Batch-64 paged decode with K and V stored as E4M3 bytes (per-tensor scales): the same
+    requests and page tables as the bf16 headline, half the KV bytes."""
+    import torch
+    from block_sparse_paged_bsr_amd import api, inputs
+
+    b = inputs.batched_decode_bf16(seed=0, poison=False)
+    e = inputs.to_e4m3(b)
+    q, k, v = e.torch_values("cuda")
+    C = num_workers or api.query_num_workers("decode", H_QO, H_KV, D)
+    p = api.Plan(b.kv_indptr, b.kv_indices, b.last_page_len, num_pages=b.num_pages, num_qo_heads=H_QO,
+                 num_kv_heads=H_KV, head_dim=D, page_size=b.page_size, num_workers=C)
+    ws = api.alloc_workspace(p)
+    p.upload(ws)
+    pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(2)]
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[0], H_QO, dtype=torch.float32, device="cuda")
+
+    def step(s):
+        kk, vv = pools[s % len(pools)]
+        api.run_decode_e4m3(p, ws, q, kk, vv, e.k_scale, e.v_scale, o=o, lse=lse, sm_scale=SM)
+
+    ms = time_calls(step, args.steps, args.warmup)
+    attn_ms, _, merge_ms, _ = kernel_times(step, 20)
+    nbytes = decode_bytes(b.kv_lens, b.batch, len(b.kv_indices), elt=1) + 2 * b.batch * H_QO * D  # Q/O stay bf16
+    return {"us": round(ms * 1e3, 2), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "attn_kernel_us": round(attn_ms * 1e3, 2), "merge_kernel_us": round(merge_ms * 1e3, 2),
+            "kernel_gbs": round(nbytes / (attn_ms * 1e-3) / 1e9, 1), "bytes": nbytes, "num_workers": C,
+            "k_scale": e.k_scale, "v_scale": e.v_scale}
+
+
 def bench_vector_sparse(args):
     """Page size 1 over a 2^20-row pool vs the same contents contiguous."""
     from block_sparse_paged_bsr_amd import inputs
@@ -448,7 +479,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="decode only, no CPU baseline")
-    ap.add_argument("--only", choices=["decode", "prefill", "vector", "composable", "cascade", "variants"],
+    ap.add_argument("--only", choices=["decode", "prefill", "vector", "composable", "cascade", "variants", "e4m3"],
                     default=None)
     ap.add_argument("--copy-calib", action="store_true")
     args = ap.parse_args()
@@ -478,6 +509,9 @@ def main():
         return
     if args.only == "variants":
         log(json.dumps(bench_variants(args)))
+        return
+    if args.only == "e4m3":
+        log(json.dumps(bench_e4m3(args)))
         return
     dec = bench_decode(args)
     log(f"decode: {dec['ms']*1e3:.1f} us/step, {dec['gbs']:.0f} GB/s; attn kernel "
@@ -543,6 +577,10 @@ def main():
         va = bench_variants(args)
         log(f"variants: {va}")
         out["variants"] = va
+        torch.cuda.empty_cache()
+        e8 = bench_e4m3(args)
+        log(f"e4m3 decode: {e8}")
+        out["decode_e4m3"] = e8
         out["cpu_baseline"] = cpu_baseline(dec)
     print(json.dumps(out), flush=True)
 
