@@ -454,7 +454,26 @@ def bench_cascade(args):
         kk, vv = pools[s % 3]
         api.run_decode(pf, wf, q, kk, vv, o=o, lse=l, sm_scale=SM)
 
+    # the levels are independent until the fold: one stream each (default priority), joined
+    # before the merges, so a small level does not leave the GPU idle while it runs
+    streams = [torch.cuda.Stream() for _ in plans]
+
+    def cascade_streams(s):
+        kk, vv = pools[s % 3]
+        cur = torch.cuda.current_stream()
+        for st, (p, fn), w, (oo, ll) in zip(streams, plans, wss, outs):
+            st.wait_stream(cur)
+            with torch.cuda.stream(st):
+                fn(p, w, q, kk, vv, o=oo, lse=ll, sm_scale=SM)
+        for st in streams:
+            cur.wait_stream(st)
+        api.merge_state(outs[0][0], outs[0][1], outs[1][0], outs[1][1], o_out=o, lse_out=l)
+        for oo, ll in outs[2:]:
+            api.merge_state(o, l, oo, ll, o_out=o, lse_out=l)
+
     ms_c = time_calls(cascade, args.steps, args.warmup)
+    ms_cs = time_calls(cascade_streams, args.steps, args.warmup)
+    ms_csg = graph_replay_ms(cascade_streams, args.steps, args.warmup)
     ms_s = time_calls(single, args.steps, args.warmup)
     # the cascade is several launches per step: replayed as one captured graph per KV pool
     # it is not bound by the host's per-call cost
@@ -469,6 +488,8 @@ def bench_cascade(args):
             "speedup": round(ms_s / ms_c, 3), "levels": len(plans),
             "cascade_graph_us": round(ms_cg * 1e3, 2), "single_level_graph_us": round(ms_sg * 1e3, 2),
             "graph_speedup": round(ms_sg / ms_cg, 3),
+            "cascade_streams_us": round(ms_cs * 1e3, 2), "cascade_streams_graph_us": round(ms_csg * 1e3, 2),
+            "streams_graph_speedup": round(ms_sg / ms_csg, 3),
             "cascade_bytes": casc_bytes, "single_level_bytes": single_bytes,
             "single_level_gbs": round(single_bytes / (ms_s * 1e-3) / 1e9, 1)}
 

@@ -268,3 +268,50 @@ def test_cascade_three_levels():
     compare(o.float().cpu().numpy(), l.cpu().numpy(), ro, rl, "bf16", "cascade merged")
     uo, ul = A.batch_attention(b.q_f32, b.k_f32, b.v_f32, *b.full, b.page_size, 32, 8, sm)
     compare(o.float().cpu().numpy(), l.cpu().numpy(), uo, ul, "bf16", "cascade vs union")
+
+
+def test_cascade_levels_on_separate_streams():
+    """The cascade's levels run on three streams joined before the fold: bitwise equal to the
+    same calls in sequence (each level's plan and workspace are its own)."""
+    import torch
+    from block_sparse_paged_bsr_amd import api
+
+    b = I.cascade_decode(seed=1)
+    log("[cascade_streams] three levels on three streams")
+    q, k, v = b.torch_values("cuda")
+    sm = 1.0 / math.sqrt(b.head_dim)
+    runs = []
+    for qo, ip, ix, la in b.levels:
+        p = api.Plan(ip, ix, la, num_pages=b.num_pages, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                     page_size=b.page_size, qo_indptr=qo, causal=False, num_workers=64)
+        runs.append((p, api.run_prefill))
+    ip, ix, la = b.suffix
+    runs.append((api.Plan(ip, ix, la, num_pages=b.num_pages, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                          page_size=b.page_size, num_workers=128), api.run_decode))
+    wss = []
+    for p, _ in runs:
+        w = api.alloc_workspace(p)
+        p.upload(w)
+        wss.append(w)
+    torch.cuda.synchronize()
+
+    def fold(states):
+        o, l = states[0]
+        for o2, l2 in states[1:]:
+            o, l = api.merge_state(o, l, o2, l2)
+        return o, l
+
+    seq = fold([fn(p, w, q, k, v, sm_scale=sm) for (p, fn), w in zip(runs, wss)])
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in runs]
+    cur = torch.cuda.current_stream()
+    outs = []
+    for st, (p, fn), w in zip(streams, runs, wss):
+        st.wait_stream(cur)
+        with torch.cuda.stream(st):
+            outs.append(fn(p, w, q, k, v, sm_scale=sm))
+    for st in streams:
+        cur.wait_stream(st)
+    par = fold(outs)
+    torch.cuda.synchronize()
+    assert torch.equal(seq[0], par[0]) and torch.equal(seq[1], par[1])
