@@ -26,6 +26,12 @@ Definitions followed, by page:
   window_left (the lower half of the §⑧ predicate; the causal flag supplies the upper
   half); a logits soft cap c > 0 replaces every score s = sm_scale q.k by c tanh(s / c)
   before the mask decides which scores take part.
+* Custom masks ("FlashInfer: Engineering a Customizable, Block-Sparse Attention Engine for
+  LLM Inference Serving" §VII, LogitsMask; tree and importance masks, §III.1): an arbitrary
+  boolean matrix per request, [l_qo, l_kv], stored row-major as bits (bit b of the
+  concatenation is bit b mod 8 of byte b div 8, requests one after another).  The pages
+  do not fix a storage format; this packing is the plainest one.  A key takes part only
+  if the custom mask and every other predicate (causal, window) allow it.
 
 Nothing here tiles, fuses or reorders: the score matrix of every (request, head) is
 materialised and each row goes through softmax on its own.
@@ -118,6 +124,25 @@ def window_allowed(l_qo, l_kv, window_left):
     return kpos + l_qo + window_left >= l_kv + qpos
 
 
+def unpack_custom_mask(bits, qo_lens, kv_lens):
+    """Per-request bool matrices [l_qo, l_kv] from the packed bit string (module
+    docstring): request i starts at bit sum_{r<i} l_qo(r) l_kv(r); inside a request,
+    bit q * l_kv + k says whether query q may see key k."""
+    bits = np.asarray(bits, dtype=np.uint8)
+    out = []
+    start = 0
+    for lq, lk in zip(qo_lens, kv_lens):
+        lq, lk = int(lq), int(lk)
+        out_i = np.zeros((lq, lk), dtype=bool)
+        for q in range(lq):
+            for k in range(lk):
+                b = start + q * lk + k
+                out_i[q, k] = (int(bits[b // 8]) >> (b % 8)) & 1 == 1
+        out.append(out_i)
+        start += lq * lk
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Batched attention over a BSR / paged KV cache
 # ---------------------------------------------------------------------------
@@ -140,6 +165,7 @@ def batch_attention(
     query_subset=None,
     window_left=-1,
     soft_cap=0.0,
+    custom_mask=None,
 ):
     """Attention of every (query, head) of a ragged batch over its own paged KV.
 
@@ -150,7 +176,9 @@ def batch_attention(
     ``query_subset`` maps a request to the query positions (0-based within the
     request) to evaluate; each query row is independent of the others, so a subset
     is the same definition on fewer rows.  ``window_left`` >= 0 adds the sliding-window
-    mask and ``soft_cap`` > 0 the score soft cap (module docstring).
+    mask and ``soft_cap`` > 0 the score soft cap (module docstring).  ``custom_mask``: a
+    list of per-request bool matrices [l_qo, l_kv] (``unpack_custom_mask``), ANDed with
+    the other predicates.
     """
     assert num_qo_heads % num_kv_heads == 0
     g = num_qo_heads // num_kv_heads
@@ -177,6 +205,10 @@ def batch_attention(
         if window_left >= 0:
             win = window_allowed(l_qo, l_kv, window_left)
             allowed = win if allowed is None else (allowed & win)
+        if custom_mask is not None:
+            cm = np.asarray(custom_mask[i], dtype=bool)
+            assert cm.shape == (l_qo, l_kv)
+            allowed = cm if allowed is None else (allowed & cm)
         if allowed is not None:
             allowed = allowed[sel]
         K_i = k_flat[rows].astype(np.float64)  # [l_kv, H_kv, d]

@@ -138,3 +138,58 @@ def test_no_window_plan_unchanged():
     # window_left = -1 is the plain plan: the pinned worked example still holds
     p = PL.make_plan([1000, 100, 100, 50], None, 1, 1, 4, alpha=0, beta=1, window_left=-1)
     assert p.chunk_limit == 313
+
+
+# ---------------------------------------------------------------------------
+# Custom masks (LogitsMask with an arbitrary per-request boolean matrix)
+# ---------------------------------------------------------------------------
+
+
+def test_custom_mask_unpacking_worked_example():
+    # two requests: 2 x 3 and 1 x 2; bits written out by hand, little-endian within a byte
+    # request 0: rows [1 0 1], [0 1 1] -> bits 0..5 = 1,0,1,0,1,1; request 1: [1, 1] -> bits 6, 7
+    bits = np.array([0b11110101], dtype=np.uint8)
+    m = A.unpack_custom_mask(bits, [2, 1], [3, 2])
+    assert m[0].tolist() == [[True, False, True], [False, True, True]]
+    assert m[1].tolist() == [[True, True]]
+
+
+def test_custom_mask_unpacking_matches_numpy_packbits():
+    rng = np.random.default_rng(11)
+    qo, kv = [3, 1, 5], [7, 12, 4]
+    mats = [rng.random((a, b)) < 0.5 for a, b in zip(qo, kv)]
+    bits = np.packbits(np.concatenate([m.reshape(-1) for m in mats]), bitorder="little")
+    for a, b in zip(A.unpack_custom_mask(bits, qo, kv), mats):
+        assert np.array_equal(a, b)
+
+
+def test_all_true_custom_mask_is_no_mask_and_causal_mask_is_causal():
+    b = I.make_paged_batch(21, [40, 9], [6, 9], page_size=4, num_qo_heads=4, num_kv_heads=2, head_dim=16,
+                           dtype="f32", causal=True)
+    args = (b.q_f32, b.k_f32, b.v_f32, b.kv_indptr, b.kv_indices, b.last_page_len, 4, 4, 2, 0.25)
+    ones = [np.ones((q, k), dtype=bool) for q, k in zip([6, 9], [40, 9])]
+    o1, l1 = A.batch_attention(*args, qo_indptr=b.qo_indptr, causal=True, custom_mask=ones)
+    o2, l2 = A.batch_attention(*args, qo_indptr=b.qo_indptr, causal=True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    cm = [A.causal_allowed(q, k) for q, k in zip([6, 9], [40, 9])]
+    o3, l3 = A.batch_attention(*args, qo_indptr=b.qo_indptr, causal=False, custom_mask=cm)
+    assert np.array_equal(o3, o2) and np.array_equal(l3, l2)
+
+
+def test_custom_mask_row_with_no_key_is_empty_and_single_key_row_is_v():
+    b = I.make_paged_batch(22, [10], [3], page_size=4, num_qo_heads=2, num_kv_heads=1, head_dim=8, dtype="f32")
+    m = np.zeros((3, 10), dtype=bool)
+    m[1, 4] = True
+    m[2, [2, 7]] = True
+    o, l = A.batch_attention(b.q_f32, b.k_f32, b.v_f32, b.kv_indptr, b.kv_indices, b.last_page_len, 4, 2, 1,
+                             0.5, qo_indptr=b.qo_indptr, custom_mask=[m])
+    assert np.all(o[0] == 0) and np.all(np.isneginf(l[0]))
+    rows = A.physical_rows(b.kv_indptr, b.kv_indices, b.last_page_len, 4, 0)
+    vflat = b.v_f32.reshape(-1, 1, 8)
+    kflat = b.k_f32.reshape(-1, 1, 8)
+    for h in range(2):
+        assert np.allclose(o[1, h], vflat[rows[4], 0])
+        s = 0.5 * kflat[rows[[2, 7]], 0].astype(np.float64) @ b.q_f32[2, h].astype(np.float64)
+        w = np.exp(s - s.max())
+        assert np.allclose(o[2, h], (w / w.sum()) @ vflat[rows[[2, 7]], 0])
+        assert math.isclose(l[2, h], s.max() + math.log(w.sum()), rel_tol=1e-12)
