@@ -79,6 +79,7 @@ class PlanView(C.Structure):
         ("window_left", C.c_int32),
         ("logits_soft_cap", C.c_float),
         ("tile_lo", i32p),
+        ("custom_mask_bits", C.c_int64),
     ]
 
 
@@ -91,6 +92,7 @@ EXPORTED = [
     "bsr_run_decode",
     "bsr_run_decode_e4m3",
     "bsr_run_prefill",
+    "bsr_run_prefill_masked",
     "bsr_merge_state",
     "bsr_debug_gather_rows",
     "bsr_timing_enable",
@@ -133,6 +135,8 @@ def lib():
     L.bsr_run_decode_e4m3.argtypes = [vp, vp, vp, vp, vp, vp, C.POINTER(C.c_float), C.c_float, C.c_float,
                                       C.c_float, vp]
     L.bsr_run_decode_e4m3.restype = C.c_int
+    L.bsr_run_prefill_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, C.POINTER(C.c_float), C.c_int32, C.c_float, vp]
+    L.bsr_run_prefill_masked.restype = C.c_int
     fp = C.POINTER(C.c_float)
     L.bsr_merge_state.argtypes = [vp, fp, vp, fp, vp, fp, C.c_int64, C.c_int32, C.c_int32, C.c_int32, vp]
     L.bsr_merge_state.restype = C.c_int

@@ -97,6 +97,7 @@ class Plan:
         self.batch = len(kv_indptr) - 1
         self.total_q = self.batch if qo_indptr is None else int(qo_indptr[-1])
         self._ws = None
+        self._mask_bits = None
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -155,6 +156,7 @@ class Plan:
             "tile_lo": arr(v.tile_lo, v.num_tiles),
             "window_left": v.window_left,
             "logits_soft_cap": v.logits_soft_cap,
+            "custom_mask_bits": v.custom_mask_bits,
         }
 
 
@@ -211,6 +213,33 @@ def run_decode(p: Plan, ws, q, k_cache, v_cache, o=None, lse=None, sm_scale=None
 def run_prefill(p: Plan, ws, q, k_cache, v_cache, o=None, lse=None, sm_scale=None, stream=None):
     """bsr_run_prefill: ragged (causal per plan) queries; returns (O, LSE)."""
     return _run(lib().bsr_run_prefill, p, ws, q, k_cache, v_cache, o, lse, sm_scale, stream)
+
+
+def pack_custom_mask(masks) -> np.ndarray:
+    """Pack per-request boolean matrices [l_qo, l_kv] (request order, row-major) into the
+    bit string bsr_run_prefill_masked reads: bit b at bit b % 8 of byte b // 8."""
+    flat = [np.asarray(m, dtype=bool).reshape(-1) for m in masks]
+    allbits = np.concatenate(flat) if flat else np.zeros(0, dtype=bool)
+    return np.packbits(allbits, bitorder="little")
+
+
+def run_prefill_masked(p: Plan, ws, q, k_cache, v_cache, mask, o=None, lse=None, sm_scale=None, stream=None):
+    """bsr_run_prefill_masked: ``mask`` is a uint8 device tensor from ``pack_custom_mask``."""
+    import torch
+
+    if mask.dtype != torch.uint8 or not mask.is_cuda or not mask.is_contiguous():
+        raise TypeError("mask must be a contiguous uint8 device tensor")
+    if p._mask_bits is None:
+        p._mask_bits = int(p.export()["custom_mask_bits"])
+    need = (p._mask_bits + 7) // 8
+    if mask.numel() < need:
+        raise ValueError(f"mask holds {mask.numel()} bytes, the plan needs {need}")
+    mptr = C.c_void_p(mask.data_ptr())
+
+    def fn(h, ws_, q_, k_, v_, o_, lse_, dt, sm, st):
+        return lib().bsr_run_prefill_masked(h, ws_, q_, k_, v_, mptr, o_, lse_, dt, sm, st)
+
+    return _run(fn, p, ws, q, k_cache, v_cache, o, lse, sm_scale, stream)
 
 
 def run_decode_e4m3(p: Plan, ws, q, k_cache, v_cache, k_scale: float, v_scale: float, o=None, lse=None,

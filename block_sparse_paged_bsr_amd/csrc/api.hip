@@ -121,7 +121,8 @@ bool positive_finite(float x) { return x > 0.f && x != __builtin_huge_valf(); }
 // kv_e4m3: K and V are E4M3 bytes with per-tensor scales (decode only; Q and O are bf16)
 int run_common(const bsr_plan* p, const void* ws, const void* q, const void* k, const void* v,
                void* o, float* lse, int32_t dtype, float sm_scale, void* stream, bool decode_call,
-               bool kv_e4m3 = false, float k_scale = 1.f, float v_scale = 1.f) {
+               bool kv_e4m3 = false, float k_scale = 1.f, float v_scale = 1.f,
+               const uint8_t* mask = nullptr) {
   if (!p) return invalid("plan is NULL");
   if (!ws) return invalid("workspace is NULL");
   if (ws != p->uploaded_ws) return invalid("workspace was not uploaded for this plan (call bsr_plan_upload first)");
@@ -147,6 +148,7 @@ int run_common(const bsr_plan* p, const void* ws, const void* q, const void* k, 
   a.sm_scale = sm_scale;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.mask = mask;
 
   hipError_t e = hipSuccess;
   if (!p->items.empty()) {
@@ -157,7 +159,8 @@ int run_common(const bsr_plan* p, const void* ws, const void* q, const void* k, 
       if (!attn_f32_supported(p->d)) return unsupported("fp32 head_dim must be one of 16, 32, 64, 128, 256");
       e = launch_attn_f32(a, s);
     } else {
-      const bool dec_ok = p->decode && decode_bf16_supported(p->d, p->g, p->Tq);
+      // the decode kernel has no custom-mask path: masked runs use the tiled kernel
+      const bool dec_ok = p->decode && !mask && decode_bf16_supported(p->d, p->g, p->Tq);
       if (dec_ok) {
         e = launch_decode_bf16(a, false, s);
       } else {
@@ -289,6 +292,7 @@ int bsr_plan_export(const bsr_plan* p, bsr_plan_view* v) {
   v->window_left = p->window_left;
   v->logits_soft_cap = p->soft_cap;
   v->tile_lo = p->tile_lo.data();
+  v->custom_mask_bits = p->mask_bits;
   return BSR_OK;
 }
 
@@ -296,6 +300,14 @@ int bsr_run_decode(const bsr_plan* plan, const void* ws, const void* q, const vo
                    const void* v_cache, void* o, float* lse, int32_t dtype, float sm_scale,
                    void* stream) {
   return run_common(plan, ws, q, k_cache, v_cache, o, lse, dtype, sm_scale, stream, true);
+}
+
+int bsr_run_prefill_masked(const bsr_plan* plan, const void* ws, const void* q, const void* k_cache,
+                           const void* v_cache, const void* mask, void* o, float* lse, int32_t dtype,
+                           float sm_scale, void* stream) {
+  if (plan && plan->mask_bits > 0 && !mask) return invalid("mask is NULL");
+  return run_common(plan, ws, q, k_cache, v_cache, o, lse, dtype, sm_scale, stream, false, false, 1.f, 1.f,
+                    static_cast<const uint8_t*>(mask));
 }
 
 int bsr_run_decode_e4m3(const bsr_plan* plan, const void* ws, const void* q, const void* k_cache,

@@ -20,7 +20,8 @@ struct ReqRec {
   int32_t page_start;  // kv_indptr[i]
   int32_t kv_len;      // l_kv
   int32_t tok_start;   // prefix sum of l_kv (debug gather output offset)
-  int32_t pad[3];
+  int32_t pad;
+  int64_t mask_off;    // first bit of the request's custom mask: sum of l_qo * l_kv before it
 };
 static_assert(sizeof(ReqRec) == 32, "ReqRec layout");
 
@@ -67,6 +68,7 @@ struct bsr_plan {
   bool decode = true;  // qo_indptr == NULL
   std::vector<int32_t> qo_indptr, kv_indptr, kv_indices, last_page_len;
   std::vector<int32_t> qo_len, kv_len;
+  int64_t mask_bits = 0;  // bits of a custom mask for this plan: sum of l_qo * l_kv
   int32_t max_qo_len = 0;
   int64_t total_kv_tokens = 0;
   // partition

@@ -10,7 +10,8 @@
 // state for the merge pass.
 // Variants ("FlashInfer 原理" §⑧; eq. 8 of the review): a sliding window raises the first
 // visible key of each row, and a logits soft cap c replaces each scaled score s by
-// c tanh(s / c) before the softmax.
+// c tanh(s / c) before the softmax; a custom mask (one bit per query and key, §VII LogitsMask)
+// drops the keys whose bit is clear.
 #include "common.cuh"
 #include "launch.h"
 
@@ -49,7 +50,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(RunArgs a) {
       int kbeg = item.kv_start;
       if (a.window_left >= 0) kbeg = max(kbeg, rq.kv_len - rq.q_len + pos - a.window_left);
       float m = kNegInf, l = 0.f;
+      const int64_t mrow = rq.mask_off + int64_t(pos) * rq.kv_len;
       for (int t = kbeg; t < kend; ++t) {
+        if (a.mask && !mask_bit(a.mask, mrow + t)) continue;
         const int64_t base = (page_row(a.indices, rq.page_start, t, a.P, a.p_shift) * a.Hk + hk) * D;
         float s = 0.f;
 #pragma unroll

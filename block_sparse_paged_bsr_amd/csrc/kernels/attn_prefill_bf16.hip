@@ -51,9 +51,12 @@
 // review).
 //
 // Variants ("FlashInfer 原理" §⑧; eq. 8 of the review) run in separate instantiations (VAR): the
-// sliding window in both kernels, the soft cap in the 4-wave one.  The soft cap turns each score s into
+// sliding window in both kernels, the soft cap and custom masks in the 4-wave one.  The soft cap turns each score s into
 // (c / sm_scale) tanh(sm_scale s / c) before the mask (the softmax then multiplies by
-// sm_scale log2(e) as usual), and a sliding window adds a per-row lower bound to the mask.
+// sm_scale log2(e) as usual), a sliding window adds a per-row lower bound to the mask, and a
+// custom mask is read bit by bit for every block (its loads are ordinary vector loads, so the
+// compiler's wait for them also waits for the tile loads in flight: masked runs give up the
+// prefetch depth).
 #include <climits>
 #include <type_traits>
 
@@ -419,11 +422,19 @@ __device__ __forceinline__ float raise_reference(float& m, float mx_scaled, bool
 // ---------------------------------------------------------------------------------
 // Per-row state of the variants: the first key the sliding window shows this row (INT_MIN
 // without a window), the largest such key over the item's rows (uniform; KV blocks that
-// start before it need the lower-bound test) and the soft cap as S -> k1 tanh(k2 S).
+// start before it need the lower-bound test), the soft cap as S -> k1 tanh(k2 S), and the
+// first bit of this row in a custom mask (-1: no mask, or an absent row).
 struct VarRow {
   int lo = INT_MIN, max_lo = INT_MIN;
   float k1 = 0.f, k2 = 0.f;
-  __device__ __forceinline__ VarRow(const RunArgs& a, const ItemRec& item, const ReqRec& rq, int row_pos) {
+  int64_t mrow = -1;
+  bool masked = false;  // a custom mask is given (uniform): every block is tested
+  __device__ __forceinline__ VarRow(const RunArgs& a, const ItemRec& item, const ReqRec& rq, int row_pos,
+                                    bool row_ok) {
+    if (a.mask) {
+      masked = true;
+      if (row_ok) mrow = rq.mask_off + int64_t(row_pos) * rq.kv_len;
+    }
     if (a.window_left >= 0) {
       const int base = rq.kv_len - rq.q_len - a.window_left;
       lo = base + row_pos;
@@ -435,6 +446,15 @@ struct VarRow {
     }
   }
   __device__ __forceinline__ float cap(float s) const { return k1 * fast_tanh(k2 * s); }
+  // whether key tok takes part: inside [lo, lim) and, with a custom mask, its bit set.  The
+  // mask byte is read unconditionally (bit 0 for keys outside the row's range or absent rows,
+  // so every address is inside the mask) and combined without a branch.
+  __device__ __forceinline__ bool keeps(const uint8_t* __restrict__ mask, int tok, int lim) const {
+    const bool in = tok < lim && tok >= lo;
+    if (!masked) return in;  // uniform
+    const bool live = in & (mrow >= 0);
+    return live & mask_bit(mask, live ? mrow + tok : 0);
+  }
 };
 
 template <int D, bool PIPE, int PG, bool VAR>
@@ -463,7 +483,7 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
   const bool row_ok = r < item.row_end;
   const int row_pos = r / a.g, row_hq = hk * a.g + r % a.g;
   const int lim = (a.causal && row_ok) ? min(kv_end, rq.kv_len - rq.q_len + row_pos + 1) : kv_end;
-  const VarRow var(a, item, rq, row_pos);
+  const VarRow var(a, item, rq, row_pos, row_ok);
   bf16x8 qb[KS16];
   {
     const uint16_t* qp = Q + (int64_t(rq.q_start + row_pos) * a.Hq + row_hq) * D + 8 * h;
@@ -515,11 +535,11 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
 #pragma unroll
         for (int i = 0; i < 16; ++i) S[i] = var.cap(S[i]);
       }
-      if (t0 + 32 * (ks + 1) > min_lim || t0 + 32 * ks < var.max_lo) {
+      if (var.masked || t0 + 32 * (ks + 1) > min_lim || t0 + 32 * ks < var.max_lo) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int tok = t0 + 32 * ks + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (tok >= lim || tok < var.lo) S[i] = kNegInf;
+          S[i] = var.keeps(a.mask, tok, lim) ? S[i] : kNegInf;
         }
       }
     } else if (t0 + 32 * (ks + 1) > min_lim) {
@@ -889,7 +909,7 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
   const bool row_ok = r < item.row_end;
   const int row_pos = r / a.g, row_hq = hk * a.g + r % a.g;
   const int lim = (a.causal && row_ok) ? min(kv_end, rq.kv_len - rq.q_len + row_pos + 1) : kv_end;
-  const VarRow var(a, item, rq, row_pos);
+  const VarRow var(a, item, rq, row_pos, row_ok);
   bf16x8 qb[KB];
   {
     const uint16_t* qp = Q + (int64_t(rq.q_start + row_pos) * a.Hq + row_hq) * D + j * 8;
@@ -933,13 +953,13 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
 #pragma unroll
           for (int i = 0; i < 4; ++i) S[b][i] = var.cap(S[b][i]);
       }
-      if (t0 + kTileKV > min_lim || t0 < var.max_lo) {
+      if (var.masked || t0 + kTileKV > min_lim || t0 < var.max_lo) {
 #pragma unroll
         for (int b = 0; b < NT; ++b)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int tok = t0 + (ks * NT + b) * 16 + 4 * j + i;
-            if (tok >= lim || tok < var.lo) S[b][i] = kNegInf;
+            S[b][i] = var.keeps(a.mask, tok, lim) ? S[b][i] : kNegInf;
           }
       }
     } else if (t0 + kTileKV > min_lim) {
@@ -1120,7 +1140,7 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
   int min_lim = kv_end;  // tiles ending before the smallest visible end need no mask
   if (a.causal) min_lim = min(kv_end, rq.kv_len - rq.q_len + item.row_start / a.g + 1);
   min_lim = __builtin_amdgcn_readfirstlane(min_lim);
-  const VarRow var[2] = {VarRow(a, item, rq, row_pos[0]), VarRow(a, item, rq, row_pos[1])};
+  const VarRow var[2] = {VarRow(a, item, rq, row_pos[0], row_ok[0]), VarRow(a, item, rq, row_pos[1], row_ok[1])};
 
   // running references (log2 units, from a finite floor), sums and rescale factors per block
   float m[2] = {kMFloor, kMFloor}, l[2] = {0.f, 0.f}, corr[2] = {1.f, 1.f};
@@ -1161,7 +1181,8 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
     }
   };
   // causal mask of the tile starting at t0 (only where it reaches past the first row's limit)
-  // (with VAR also below the sliding window's first key; soft-capped plans never come here)
+  // (with VAR also below the sliding window's first key; soft-capped and custom-masked runs
+  // never come here)
   auto mask = [&](f32x16 (&S)[2], int t0) {
     if constexpr (VAR) {
       if (t0 + 32 > min_lim || t0 < var[0].max_lo) {
@@ -1473,14 +1494,15 @@ int prefill_bf16_blocks_per_cu(int d) {
   return (e == hipSuccess && nb > 0) ? nb : 1;
 }
 
-// VAR: the variant instantiations (sliding window, soft cap).  Soft-capped plans use the 4-wave
+// VAR: the variant instantiations (sliding window, soft cap, custom mask).  Soft-capped plans
+// and custom-masked runs use the 4-wave
 // shapes for every tile size: their two waves per SIMD overlap the extra exponential and
 // reciprocal of each capped score with the other wave's matrix work, where the single wave per
 // SIMD of the 128-row shape runs them in series (measured 573 against 542 TFLOP/s on the ragged
 // causal prefill with a cap of 50).
 template <int D, bool VAR>
 static void launch_pg(const RunArgs& a, dim3 grid, hipStream_t s, bool div32, bool pow2) {
-  if (a.Tq == 128 && !(VAR && a.soft_cap > 0.f)) {  // 128-row tiles: two waves of two row blocks each
+  if (a.Tq == 128 && !(VAR && (a.soft_cap > 0.f || a.mask))) {  // 128-row tiles: two waves of two row blocks each
     const dim3 block(kThreads2);
     if (div32) hipLaunchKernelGGL((attn_prefill128_bf16_kernel<D, kPageDiv32, VAR>), grid, block, 0, s, a);
     else if (pow2) hipLaunchKernelGGL((attn_prefill128_bf16_kernel<D, kPagePow2, VAR>), grid, block, 0, s, a);
@@ -1496,7 +1518,7 @@ static void launch_pg(const RunArgs& a, dim3 grid, hipStream_t s, bool div32, bo
 template <int D>
 static void launch_d(const RunArgs& a, dim3 grid, hipStream_t s) {
   const bool div32 = a.p_shift >= 0 && a.P <= 32, pow2 = a.p_shift >= 0;
-  if (a.window_left >= 0 || a.soft_cap > 0.f) launch_pg<D, true>(a, grid, s, div32, pow2);
+  if (a.window_left >= 0 || a.soft_cap > 0.f || a.mask) launch_pg<D, true>(a, grid, s, div32, pow2);
   else launch_pg<D, false>(a, grid, s, div32, pow2);
 }
 

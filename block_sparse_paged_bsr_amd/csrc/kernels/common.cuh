@@ -40,7 +40,13 @@ struct RunArgs {
   int32_t window_left;  // sliding window (keys left of the diagonal), -1 = none
   float soft_cap;       // logits soft cap c (score -> c tanh(score / c)), 0 = none
   float k_scale, v_scale;  // per-tensor scales of an E4M3 KV cache (1 otherwise)
+  const uint8_t* mask;     // packed custom mask (ReqRec::mask_off), or null
 };
+
+// Bit `bit` of a packed custom mask: bit b is bit b mod 8 of byte b / 8.
+__device__ __forceinline__ bool mask_bit(const uint8_t* __restrict__ mask, int64_t bit) {
+  return (mask[bit >> 3] >> (bit & 7)) & 1;
+}
 
 // ---- bf16 <-> fp32 ----
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

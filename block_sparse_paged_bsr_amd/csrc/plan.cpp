@@ -282,15 +282,18 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
 
   p->meta.assign(L.meta_bytes, 0);
   auto* req = reinterpret_cast<ReqRec*>(p->meta.data() + L.req);
-  int64_t tok_start = 0;
+  int64_t tok_start = 0, mask_off = 0;
   for (int32_t i = 0; i < B; ++i) {
     req[i].q_start = p->qo_indptr[i];
     req[i].q_len = p->qo_len[i];
     req[i].page_start = p->kv_indptr[i];
     req[i].kv_len = p->kv_len[i];
     req[i].tok_start = int32_t(tok_start);
+    req[i].mask_off = mask_off;
     tok_start += p->kv_len[i];
+    mask_off += int64_t(p->qo_len[i]) * p->kv_len[i];
   }
+  p->mask_bits = mask_off;
   if (nnz > 0)
     std::memcpy(p->meta.data() + L.indices, p->kv_indices.data(), sizeof(int32_t) * nnz);
   auto* qi = reinterpret_cast<ItemRec*>(p->meta.data() + L.items);

@@ -165,6 +165,7 @@ typedef struct bsr_plan_view {
   int32_t window_left;
   float logits_soft_cap;
   const int32_t* tile_lo;
+  int64_t custom_mask_bits;  /* sum_i l_qo(i) * l_kv(i): bits of a bsr_run_prefill_masked mask */
 } bsr_plan_view;
 
 int bsr_plan_export(const bsr_plan* plan, bsr_plan_view* view);
@@ -212,6 +213,24 @@ int bsr_run_decode_e4m3(const bsr_plan* plan, const void* ws, const void* q, con
 int bsr_run_prefill(const bsr_plan* plan, const void* ws, const void* q, const void* k_cache,
                     const void* v_cache, void* o, float* lse, int32_t dtype, float sm_scale,
                     void* stream);
+
+/*
+ * bsr_run_prefill with a custom mask (any plan, decode or prefill): the LogitsMask variant of
+ * "FlashInfer: Engineering a Customizable, Block-Sparse Attention Engine for LLM Inference
+ * Serving" §VII (tree attention and importance masks, §III.1), one boolean per (query, key)
+ * of each request.  mask: device bytes, the requests' [l_qo, l_kv] boolean matrices in
+ * request order, each row-major, packed 8 per byte with bit b of the whole string at bit
+ * b mod 8 of byte b / 8 (the pages fix no storage format); request i starts at bit
+ * sum_{r<i} l_qo(r) l_kv(r), and the buffer holds at least ceil(custom_mask_bits / 8) bytes
+ * (bsr_plan_view).  A key takes part only if its bit is set and the plan's causal and
+ * window predicates allow it; a query row left with no key is the empty state (O = 0,
+ * LSE = -inf).  The plan's work partition is unchanged (fully masked chunks are computed
+ * and contribute nothing).  bf16 runs use the 4-wave tiled kernel; they are slower than
+ * unmasked runs (every block reads its bits).  mask may be NULL only if custom_mask_bits is 0.
+ */
+int bsr_run_prefill_masked(const bsr_plan* plan, const void* ws, const void* q, const void* k_cache,
+                           const void* v_cache, const void* mask, void* o, float* lse, int32_t dtype,
+                           float sm_scale, void* stream);
 
 /*
  * (O_a, LSE_a) (+) (O_b, LSE_b) for `rows` x `heads` states of dimension head_dim

@@ -219,3 +219,17 @@ def test_null_arguments_rejected_without_gpu():
     assert L.bsr_debug_gather_rows(p.handle, None, None, None) == _lib.BSR_INVALID_ARG
     assert L.bsr_merge_state(None, None, None, None, None, None, -1, 1, 1, 1, None) == _lib.BSR_INVALID_ARG
     assert L.bsr_merge_state(None, None, None, None, None, None, 1, 1, 1, 7, None) == _lib.BSR_INVALID_ARG
+
+
+def test_custom_mask_bits_in_the_plan_view():
+    kv, qo = [40, 0, 17, 300], [3, 5, 17, 1]
+    lp = _lib_plan(kv, qo, 8, 2, 16, P=4)
+    assert lp.export()["custom_mask_bits"] == sum(a * b for a, b in zip(kv, qo))
+    dp = _lib_plan([40, 0, 17], None, 8, 2, 16, P=4)
+    assert dp.export()["custom_mask_bits"] == 57  # one query per request
+
+
+def test_pack_custom_mask_layout():
+    m0 = np.array([[1, 0, 1], [0, 1, 1]], dtype=bool)
+    m1 = np.array([[1, 1]], dtype=bool)
+    assert api.pack_custom_mask([m0, m1]).tolist() == [0b11110101]
