@@ -203,8 +203,9 @@ def windowed_prefill_flops(lens, w):
 
 def bench_variants(args):
     """The attention variants on the headline workloads: logits soft cap 50 and a 4096-key
-    sliding window on batch-64 decode; soft cap 50, a 1024-key window, and both, on the
-    ragged causal prefill.  Rates count only the visible KV (window) or pairs."""
+    sliding window on batch-64 decode; 16 speculative draft tokens per decode request under a
+    tree mask (custom mask) and under the causal mask; soft cap 50, a 1024-key window, and
+    both, on the ragged causal prefill.  Rates count only the visible KV (window) or pairs."""
     from block_sparse_paged_bsr_amd import inputs
 
     out = {}
@@ -219,6 +220,45 @@ def bench_variants(args):
                      "attn_kernel_us": round(attn_ms * 1e3, 2), "merge_kernel_us": round(merge_ms * 1e3, 2),
                      "bytes": nbytes}
         del r
+    # speculative decoding: 16 draft tokens per request of the batch-64 decode workload, each
+    # seeing the prompt and its ancestors in a random tree (custom mask) vs the causal mask
+    import torch
+    from block_sparse_paged_bsr_amd import api
+
+    rng = np.random.default_rng(0)
+    T = 16
+    prompt = inputs.decode_lengths(0)
+    sb = inputs.make_paged_batch(0, prompt + T, np.full(len(prompt), T), page_size=16, num_qo_heads=H_QO,
+                                 num_kv_heads=H_KV, head_dim=D, poison=False)
+    masks = []
+    for L in prompt:
+        m = np.zeros((T, int(L) + T), dtype=bool)
+        m[:, :L] = True
+        par = [-1] + [int(rng.integers(-1, t)) for t in range(1, T)]
+        for t in range(T):
+            a_ = t
+            while a_ >= 0:
+                m[t, L + a_] = True
+                a_ = par[a_]
+        masks.append(m)
+    bits = torch.from_numpy(api.pack_custom_mask(masks)).to("cuda")
+    q, k, v = sb.torch_values("cuda")
+    spec_bytes = int(sb.kv_lens.sum()) * H_KV * D * 2 * 2
+    for name, causal, use_mask in (("spec_tree_mask16", False, True), ("spec_causal16", True, False)):
+        p = make_plan(sb, "prefill", causal)
+        ws = api.alloc_workspace(p)
+        p.upload(ws)
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[0], H_QO, dtype=torch.float32, device="cuda")
+        if use_mask:
+            step = lambda s_: api.run_prefill_masked(p, ws, q, k, v, bits, o=o, lse=lse, sm_scale=SM)
+        else:
+            step = lambda s_: api.run_prefill(p, ws, q, k, v, o=o, lse=lse, sm_scale=SM)
+        ms = time_calls(step, args.steps, args.warmup)
+        out[name] = {"us": round(ms * 1e3, 2), "kv_gbs": round(spec_bytes / (ms * 1e-3) / 1e9, 1),
+                     "tile_q": int(p.export()["tile_q"])}
+    del q, k, v, bits
+    torch.cuda.empty_cache()
     pb = inputs.ragged_prefill_bf16(seed=0, poison=False)
     for name, var, fl in (("prefill_soft_cap50", dict(logits_soft_cap=50.0), prefill_flops(pb.kv_lens)),
                           ("prefill_window1024", dict(window_left=1024), windowed_prefill_flops(pb.kv_lens, 1024)),
