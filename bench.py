@@ -608,7 +608,7 @@ def main():
     ach = dec["bytes"] / (dec["attn_kernel_ms"] * 1e-3) / 1e9
     out["roofline"] = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                       "kernel": "attn_decode_bf16_kernel<128, false>",
+                       "kernel": "attn_decode_bf16_kernel<128, false, false>",
                        "kernel_avg_us": round(dec["attn_kernel_ms"] * 1e3, 2),
                        "merge_avg_us": round(dec["merge_kernel_ms"] * 1e3, 2)}
     if not args.quick:
