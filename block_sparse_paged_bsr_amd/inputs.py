@@ -35,6 +35,7 @@ __all__ = [
     "shared_prefix_decode",
     "E4m3Batch",
     "to_e4m3",
+    "block_sparse_attention",
 ]
 
 
@@ -611,3 +612,45 @@ def to_e4m3(b: PagedBatch, k_scale: Optional[float] = None, v_scale: Optional[fl
     kb, ks = enc(b.k_f32, k_scale)
     vb, vs = enc(b.v_f32, v_scale)
     return E4m3Batch(base=b, k_bytes=kb, v_bytes=vb, k_scale=ks, v_scale=vs)
+
+
+@dataclass
+class BlockSparseBatch:
+    """Block-sparse attention over one dense sequence, as a BSR matrix of B_r x B_c blocks.
+
+    ``dense`` holds Q [L, H_qo, d] and K/V as pages of B_c rows ([L / B_c, B_c, H_kv, d], page j
+    = rows j B_c .. (j+1) B_c - 1); ``block_mask`` [L / B_r, L / B_c] says which blocks are
+    present.  The BSR view: block row i is one "request" with the B_r queries of rows
+    i B_r .. (i+1) B_r - 1 (``qo_indptr``) whose KV pages are the present column blocks in
+    increasing order (``kv_indptr``, ``kv_indices``, full last pages).
+    """
+
+    dense: PagedBatch
+    block_mask: np.ndarray
+    block_r: int
+    block_c: int
+
+
+def block_sparse_attention(seed: int, L: int, block_r: int, block_c: int, density: float, *, num_qo_heads: int,
+                           num_kv_heads: int, head_dim: int, dtype: str = "bf16") -> BlockSparseBatch:
+    """Random block-sparse layout (each block present with probability ``density``; some
+    block rows may be empty) over seeded N(0, 1) values."""
+    assert L % block_r == 0 and L % block_c == 0
+    rng = np.random.default_rng(seed)
+    nr, nc = L // block_r, L // block_c
+    bm = rng.random((nr, nc)) < density
+    q = _round(rng.standard_normal((L, num_qo_heads, head_dim), dtype=np.float32), dtype)
+    k = _round(rng.standard_normal((nc, block_c, num_kv_heads, head_dim), dtype=np.float32), dtype)
+    v = _round(rng.standard_normal((nc, block_c, num_kv_heads, head_dim), dtype=np.float32), dtype)
+    cols = [np.nonzero(bm[i])[0] for i in range(nr)]
+    kv_indptr = np.zeros(nr + 1, dtype=np.int32)
+    kv_indptr[1:] = np.cumsum([len(c) for c in cols])
+    kv_indices = np.concatenate(cols).astype(np.int32) if kv_indptr[-1] else np.zeros(0, dtype=np.int32)
+    last = np.array([block_c if len(c) else 0 for c in cols], dtype=np.int32)
+    qo_indptr = (np.arange(nr + 1) * block_r).astype(np.int32)
+    pb = PagedBatch(page_size=block_c, num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                    qo_indptr=qo_indptr, kv_indptr=kv_indptr, kv_indices=kv_indices, last_page_len=last,
+                    num_pages=nc, q_f32=q, k_f32=k, v_f32=v, dtype=dtype,
+                    kv_lens=(kv_indptr[1:] - kv_indptr[:-1]) * block_c, qo_lens=np.full(nr, block_r, np.int32),
+                    causal=False, name="block_sparse")
+    return BlockSparseBatch(dense=pb, block_mask=bm, block_r=block_r, block_c=block_c)

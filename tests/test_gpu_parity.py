@@ -315,3 +315,20 @@ def test_cascade_levels_on_separate_streams():
     par = fold(outs)
     torch.cuda.synchronize()
     assert torch.equal(seq[0], par[0]) and torch.equal(seq[1], par[1])
+
+
+@pytest.mark.parametrize("br,bc", [(16, 16), (64, 16), (4, 32), (128, 64)])
+def test_block_sparse_attention_bsr(br, bc):
+    """Block-sparse attention of one 1024-token sequence, as a BSR matrix of B_r x B_c blocks
+    (35 % present): block rows are the plan's requests, column blocks its pages; against
+    the oracle's dense attention under the expanded block mask."""
+    bs = I.block_sparse_attention(40 + br, 1024, br, bc, 0.35, num_qo_heads=32, num_kv_heads=8, head_dim=128)
+    b = bs.dense
+    log(f"[block_sparse] L=1024 B_r={br} B_c={bc} blocks={int(bs.block_mask.sum())}/{bs.block_mask.size}")
+    p = make_plan(b, num_workers=64, causal=False)
+    o, l, _ = run_gpu(b, p, decode=False)
+    dense_mask = np.kron(bs.block_mask, np.ones((br, bc), dtype=bool))
+    npg = b.k_f32.shape[0]
+    ro, rl = A.batch_attention(b.q_f32, b.k_f32, b.v_f32, [0, npg], np.arange(npg), [bc], bc, 32, 8,
+                               1.0 / math.sqrt(128), qo_indptr=[0, 1024], custom_mask=[dense_mask])
+    compare(o, l, ro, rl, "bf16", f"block sparse {br}x{bc}")

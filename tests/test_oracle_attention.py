@@ -216,3 +216,21 @@ def test_cascade_three_levels_equals_union():
     empty = np.nonzero(b.suffix_lens == 0)[0]
     for r in empty:
         assert np.all(np.isneginf(states[2][1][r]))
+
+
+@pytest.mark.parametrize("br,bc", [(4, 8), (16, 16), (1, 4)])
+def test_bsr_block_rows_equal_dense_attention_under_the_block_mask(br, bc):
+    """The BSR view of a block-sparse mask (block row = B_r queries, its column blocks = pages
+    of B_c keys) gives the attention of the dense sequence under the expanded mask ("FlashInfer:
+    Engineering ..." §III.1, §IV; block-sparse matrix of B_r x B_c blocks)."""
+    bs = I.block_sparse_attention(5, 64, br, bc, 0.35, num_qo_heads=4, num_kv_heads=2, head_dim=16, dtype="f32")
+    b = bs.dense
+    o, l = A.batch_attention(b.q_f32, b.k_f32, b.v_f32, b.kv_indptr, b.kv_indices, b.last_page_len, bc, 4, 2,
+                             0.25, qo_indptr=b.qo_indptr)
+    dense_mask = np.kron(bs.block_mask, np.ones((br, bc), dtype=bool))
+    npg = b.k_f32.shape[0]
+    od, ld = A.batch_attention(b.q_f32, b.k_f32, b.v_f32, [0, npg], np.arange(npg), [bc], bc, 4, 2, 0.25,
+                               qo_indptr=[0, 64], custom_mask=[dense_mask])
+    assert np.array_equal(np.isneginf(l), np.isneginf(ld))
+    fin = np.isfinite(l)
+    assert np.allclose(o, od, atol=1e-12) and np.allclose(l[fin], ld[fin], atol=1e-12)
