@@ -1156,12 +1156,22 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[b][cb][i] = 0.f;
 
-  // K fragment position of this lane (token r32 of the 32-token tile, half h); V transposing
-  // read: lane 16G + 4e + q addresses token 4(G >> 1) + e (and + 8), chunk 4(G & 1) + q
-  const int k_pos = 16 * ((r32 & 15) + 16 * h);
+  // LDS layout of this shape: in a 1 KB fragment (16 tokens x 32 columns) the four 16-byte
+  // chunks of token t fill slots 4t .. 4t+3, so that each lane quad of an LDS-DMA load reads
+  // one token's 64 contiguous bytes (four quads on four rows cost about a quarter of sixteen
+  // lanes on sixteen rows in the texture path); K chunk c of token t sits at slot
+  // 4t + (c ^ ((t >> 2) & 3)), which puts the 16 tokens of one chunk read in 16 different bank
+  // groups; V is not swizzled (a transposing read spans four tokens 64 bytes apart).
+  // K read of k-step k by lane (token r32, half h): chunk 2 (k & 1) + h of token r32 & 15.
+  const int kt16 = r32 & 15, ksw = (kt16 >> 2) & 3;
+  const int k_pos0 = 16 * (4 * kt16 + (h ^ ksw)), k_pos1 = 16 * (4 * kt16 + ((2 + h) ^ ksw));
+  // V transposing read: lane 16G + 4e + q addresses token 4(G >> 1) + e (and + 8), 8-byte
+  // column unit 4(G & 1) + q
   const int vG = lane >> 4, ve = (lane >> 2) & 3, vq = lane & 3;
-  const int v_lo = v_chunk(4 * (vG >> 1) + ve, 4 * (vG & 1) + vq);
-  const int v_hi = v_chunk(4 * (vG >> 1) + ve + 8, 4 * (vG & 1) + vq);
+  const int v_lo = 64 * (4 * (vG >> 1) + ve) + 8 * (4 * (vG & 1) + vq);
+  const int v_hi = v_lo + 512;
+  // DMA lane roles: token lane >> 2 of the wave's 16, chunk (K swizzled as above)
+  const int d_tok = lane >> 2, dk_col = 8 * ((lane & 3) ^ ((lane >> 4) & 3)), dv_col = 8 * (lane & 3);
 
   const int kv0 = item.kv_start;
   const int n = (kv_end - kv0 + 31) / 32;
@@ -1171,10 +1181,10 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
 
   // scores of both blocks for the tile staged at `kt` (prologue only)
   auto qk = [&](const lds_u8* kt, f32x16 (&S)[2]) {
-    const lds_u8* kp = kt + (r32 >> 4) * KB * FRAG + k_pos;
+    const lds_u8* kp = kt + (r32 >> 4) * KB * FRAG;
 #pragma unroll
     for (int k = 0; k < KS16; ++k) {
-      const bf16x8 ka = *reinterpret_cast<lds_bf16x8*>(kp + (k >> 1) * FRAG + 512 * (k & 1));
+      const bf16x8 ka = *reinterpret_cast<lds_bf16x8*>(kp + (k >> 1) * FRAG + ((k & 1) ? k_pos1 : k_pos0));
 #pragma unroll
       for (int b = 0; b < 2; ++b)
         S[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[b][k], k == 0 ? f32x16{} : S[b], 0, 0, 0);
@@ -1206,25 +1216,22 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
   };
 
   // wave w loads token group w (16 tokens) of every 32-token tile, all KB column groups
-  auto page_k = [&](int j) { return pgn.page_of(T(j) + 16 * wave + k_dma_token(lane)); };
-  auto page_v = [&](int j) { return pgn.page_of(T(j) + 16 * wave + v_dma_token(lane)); };
+  auto page_k = [&](int j) { return pgn.page_of(T(j) + 16 * wave + d_tok); };
+  auto page_v = page_k;  // K and V lanes carry the same tokens
   auto dma_k = [&](int j, int32_t page) {
-    dma_fragments<NF>(K + pgn.template row<D>(T(j) + 16 * wave + k_dma_token(lane), page) + 8 * (lane >> 4),
-                      k_slot(j) + wave * KB * FRAG);
+    dma_fragments<NF>(K + pgn.template row<D>(T(j) + 16 * wave + d_tok, page) + dk_col, k_slot(j) + wave * KB * FRAG);
   };
   auto dma_v = [&](int j, int32_t page) {
-    dma_fragments<NF>(V + pgn.template row<D>(T(j) + 16 * wave + v_dma_token(lane), page) + 8 * (lane >> 4),
-                      v_slot(j) + wave * KB * FRAG);
+    dma_fragments<NF>(V + pgn.template row<D>(T(j) + 16 * wave + d_tok, page) + dv_col, v_slot(j) + wave * KB * FRAG);
   };
   // fast steps (P divides 32): fixed in-page offsets, page-table entries advance by 32 / P
   uint64_t k_add = 0, v_add = 0;
   int32_t k_pn = 0, v_pn = 0, pstep = 0;
   uint32_t page_bytes = 0;
   if constexpr (PG == kPageDiv32) {
-    const int kx = kv0 + 16 * wave + k_dma_token(lane), vx = kv0 + 16 * wave + v_dma_token(lane);
-    const int col = 8 * (lane >> 4);
-    k_add = reinterpret_cast<uint64_t>(K) + 2u * uint32_t(((kx & (a.P - 1)) * a.Hk + hk) * D + col);
-    v_add = reinterpret_cast<uint64_t>(V) + 2u * uint32_t(((vx & (a.P - 1)) * a.Hk + hk) * D + col);
+    const int kx = kv0 + 16 * wave + d_tok, vx = kx;
+    k_add = reinterpret_cast<uint64_t>(K) + 2u * uint32_t(((kx & (a.P - 1)) * a.Hk + hk) * D + dk_col);
+    v_add = reinterpret_cast<uint64_t>(V) + 2u * uint32_t(((vx & (a.P - 1)) * a.Hk + hk) * D + dv_col);
     k_pn = kx >> a.p_shift;
     v_pn = vx >> a.p_shift;
     pstep = 32 >> a.p_shift;
@@ -1263,8 +1270,10 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
   auto fused = [&](const lds_u8* kt, const lds_u8* vt, f32x16 (&Snext)[2], const f32x16 (&Scur)[2],
                    const u32x4 (&pprev)[2][2], u32x4 (&pcur)[2][2]) -> bool {
     constexpr int NS = 4 * KS16;
-    const lds_u8* kp = kt + (r32 >> 4) * KB * FRAG + k_pos;
-    auto kread = [&](int k) { return *reinterpret_cast<lds_bf16x8*>(kp + (k >> 1) * FRAG + 512 * (k & 1)); };
+    const lds_u8* kp = kt + (r32 >> 4) * KB * FRAG;
+    auto kread = [&](int k) {
+      return *reinterpret_cast<lds_bf16x8*>(kp + (k >> 1) * FRAG + ((k & 1) ? k_pos1 : k_pos0));
+    };
     auto vread = [&](int m2) {
       const lds_u8* vf = vt + (m2 / KB) * KB * FRAG + (m2 % KB) * FRAG;
       return cat(tr_read(vf + v_lo), tr_read(vf + v_hi));
