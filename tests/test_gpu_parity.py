@@ -105,6 +105,9 @@ PREFILL_CASES = [
     ([20, 100], [50, 3], 16, 4, 1, 128, True, 4, 16),     # l_qo > l_kv: empty rows
     ([250, 90], [250, 90], 1, 12, 4, 128, True, 11, 32),  # page size 1, g = 3
     ([64, 0, 33], [16, 5, 9], 16, 16, 4, 128, False, 2, 64),  # empty request
+    ([700, 260, 1031], [700, 200, 1031], 16, 32, 8, 64, True, 30, 128),  # 128-row shape, d = 64
+    ([700, 260], [700, 260], 8, 16, 4, 128, True, 40, 128),   # 128-row shape, page size 8
+    ([700, 260], [700, 260], 12, 16, 4, 128, True, 40, 128),  # 128-row shape, page size 12
 ]
 
 
