@@ -124,6 +124,15 @@ def run_case(b, kind, steps, warmup, rotate=1, causal=False, **variant):
     plan_us = (time.perf_counter() - t0) * 1e6
     ws = api.alloc_workspace(p)
     p.upload(ws)
+    # the plan's metadata copy on its own (a second upload: the first one also sets up the
+    # pinned staging), timed with events on the stream it runs on
+    torch.cuda.synchronize()
+    u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    u0.record()
+    p.upload(ws)
+    u1.record()
+    torch.cuda.synchronize()
+    upload_us = u0.elapsed_time(u1) * 1e3
     pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(rotate - 1)]
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[0], H_QO, dtype=torch.float32, device="cuda")
@@ -135,7 +144,8 @@ def run_case(b, kind, steps, warmup, rotate=1, causal=False, **variant):
 
     ms = time_calls(step, steps, warmup)
     e = p.export()
-    res = {"ms": ms, "plan_us": plan_us, "num_workers": e["num_workers"],
+    res = {"ms": ms, "plan_us": plan_us, "upload_us": upload_us, "meta_bytes": int(p.workspace_bytes()),
+           "num_workers": e["num_workers"],
            "items": int(e["items"].shape[0]), "slots": e["num_slots"], "step": step,
            "out": (o, lse)}
     return res
@@ -552,7 +562,11 @@ def main():
     import torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    log(f"device: {torch.cuda.get_device_name(0)}  torch {torch.__version__}")
+    props = torch.cuda.get_device_properties(0)
+    device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "cu_count": props.multi_processor_count,
+              "hbm_gib": round(props.total_memory / 2**30, 1), "torch": torch.__version__,
+              "hip": getattr(torch.version, "hip", None)}
+    log(f"device: {device}")
     if args.copy_calib:
         copy_calibration()
     if args.only == "prefill":
@@ -597,12 +611,14 @@ def main():
             "tokens": dec["tokens"], "algorithmic_bytes": dec["bytes"],
             "num_workers": dec["num_workers"], "work_items": dec["items"],
             "partial_slots": dec["slots"], "plan_host_us": round(dec["plan_us"], 1),
+            "plan_upload_us": round(dec["upload_us"], 2),
             "median_us": round(dec["median_ms"] * 1e3, 2), "min_us": round(dec["min_ms"] * 1e3, 2),
             "p90_us": round(dec["p90_ms"] * 1e3, 2),
             "pct_hbm_peak": round(100 * dec["gbs"] / HBM_PEAK_GBS, 2),
             "kv_pool_rotation": 3,
             "graph_replay_us": round(dec["graph_ms"] * 1e3, 2),
             "graph_replay_gbs": round(dec["bytes"] / (dec["graph_ms"] * 1e-3) / 1e9, 1),
+            "device": device,
         },
     }
     ach = dec["bytes"] / (dec["attn_kernel_ms"] * 1e-3) / 1e9
