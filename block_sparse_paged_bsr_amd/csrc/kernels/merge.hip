@@ -35,14 +35,18 @@ __device__ __forceinline__ float load_in<uint16_t>(const uint16_t* p) { return _
 
 // One workgroup per (merge tile, KV head).  Phase 1: the maximum and denominator of
 // every row's partial LSEs, with the tile's slot list staged in LDS.  Phase 2: every
-// (row, d) element folds the partial outputs in slot order.
+// (row, d) element folds the partial outputs in slot order.  Small tiles (at most
+// kFastSlots slots and two elements per thread, e.g. every split decode tile) load their
+// partial outputs before phase 1, so those loads overlap the LSE reads, and phase 1 leaves
+// each (slot, row) weight in LDS.
 constexpr int kMergeThreads = 256;
 constexpr int kSlotsInLds = 1024;
+constexpr int kFastSlots = 8;
 
 template <typename OutT>
 __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a) {
   __shared__ int s_slot[kSlotsInLds];
-  __shared__ float s_m[128], s_den[128];
+  __shared__ float s_m[128], s_den[128], s_w[kFastSlots * 128];
   const int hk = blockIdx.y, tid = threadIdx.x;
   const MergeRec mr = a.merge[blockIdx.x];
   const ReqRec rq = a.req[mr.req];
@@ -57,6 +61,22 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a
   auto slot_at = [&](int k) { return cached ? s_slot[k] : slots[k]; };
   auto lse_at = [&](int s, int r) { return a.part_lse[(int64_t(s) * a.Hk + hk) * a.Tq + r]; };
 
+  const bool fast = ns <= kFastSlots && nrows * D <= 2 * kMergeThreads;  // uniform
+  float ov[2][kFastSlots];
+  if (fast) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + u * kMergeThreads;
+      const int lr = idx / D, e = idx - lr * D;
+#pragma unroll
+      for (int k = 0; k < kFastSlots; ++k) {
+        ov[u][k] = 0.f;
+        if (idx < nrows * D && k < ns)
+          ov[u][k] = a.part_o[((int64_t(slot_at(k)) * a.Hk + hk) * a.Tq + lr) * D + e];
+      }
+    }
+  }
+
   // phase 1: tpr lanes of one wave per row
   int rp2 = 1;
   while (rp2 < nrows) rp2 <<= 1;
@@ -70,7 +90,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a
   if (r < nrows && mx != kNegInf)
     for (int k = sub; k < ns; k += tpr) {
       const float l = lse_at(slot_at(k), r);
-      den += l == kNegInf ? 0.f : expf(l - mx);
+      const float w = l == kNegInf ? 0.f : expf(l - mx);
+      den += w;
+      if (fast) s_w[k * 128 + r] = w;
     }
   for (int o = 1; o < tpr; o <<= 1) den += shfl_xor(den, o);
   if (r < nrows && sub == 0) {
@@ -81,6 +103,24 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a
 
   // phase 2: weighted sum of the partial outputs, slot order fixed by the plan
   OutT* O = static_cast<OutT*>(a.o);
+  if (fast) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + u * kMergeThreads;
+      if (idx >= nrows * D) continue;
+      const int lr = idx / D, e = idx - lr * D;
+      const float m = s_m[lr];
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < kFastSlots; ++k)
+        if (k < ns && m != kNegInf) acc += s_w[k * 128 + lr] * ov[u][k];
+      const int row = mr.row_start + lr;
+      const int64_t orow = int64_t(rq.q_start + row / a.g) * a.Hq + hk * a.g + row % a.g;
+      store_out<OutT>(O + orow * D + e, m == kNegInf ? 0.f : acc / s_den[lr]);
+      if (e == 0) a.lse[orow] = m == kNegInf ? kNegInf : m + logf(s_den[lr]);
+    }
+    return;
+  }
   for (int idx = tid; idx < nrows * D; idx += kMergeThreads) {
     const int lr = idx / D, e = idx - lr * D;
     const float m = s_m[lr];
