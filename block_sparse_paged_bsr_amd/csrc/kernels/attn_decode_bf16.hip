@@ -28,22 +28,20 @@
 // KV8: K and V stored as E4M3 bytes (OCP "FN" encoding) with one scale per tensor, the e4m3
 // KV cache of the review's vLLM integration (Appendix G.4).  A lane's 16-byte load then holds
 // 16 values of a row (two k-blocks of the score product; Q is loaded in the same order), and
-// v_cvt_pk_f32_fp8 widens them exactly (every E4M3 value is a bf16 value, so the high halves of
-// the fp32 results are the bf16 operands).  The K scale is folded into the score scale and the
-// V scale into the output normalisation, so the loop does no extra multiplications; the bytes
-// read per token are half of bf16's.
+// v_cvt_scalef32_pk_bf16_fp8 (scale 1) widens each pair exactly to the bf16 operands.  The K
+// scale is folded into the score scale and the V scale into the output normalisation, so the
+// loop does no extra multiplications; the bytes read per token are half of bf16's, and a step
+// covers 32 tokens (two 16-token halves loaded together) to keep a bf16 step's bytes in flight.
 #include "common.cuh"
 #include "launch.h"
 
 namespace bsr {
 
-// four E4M3 bytes -> four bf16 values (exact), as two packed pairs
+// four E4M3 bytes -> four bf16 values (exact: every E4M3 value is a bf16 value), as two packed
+// pairs, by gfx950's scaled pair conversion with a scale of 1
 __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  return u32x2{(__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xffff0000u),
-               (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xffff0000u)};
+  return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true))};
 }
 
 template <int D, bool CAP, bool KV8>
@@ -53,6 +51,7 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
   constexpr int VS = D + 8;   // LDS row stride (elements); 16-byte aligned rows
   constexpr int ES = KV8 ? 1 : 2;                // bytes per K/V element
   constexpr int NL = KV8 ? D / 64 : D / 32;      // 16-byte loads per row and lane (64 j-apart bytes)
+  constexpr int PD = KV8 ? 2 : 1;  // 16-token halves per step (E4M3 rows are half as long)
   __shared__ __attribute__((aligned(16))) uint16_t Vs[16 * VS];
 
   const int w = blockIdx.x, hk = blockIdx.y;
@@ -88,8 +87,8 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // page of this lane's token (lane n of a step) for the current, next and
-    // next-but-one steps: the index load runs two steps ahead of the row loads
+    // page of this lane's token (lane n of a step): the index load runs one step ahead of
+    // the row loads, which run one step ahead of the computation
     const int pg_start = rq.page_start;
     auto page_of = [&](int t) -> int32_t {
       const int tc = min(t, kv_end - 1);
@@ -101,32 +100,16 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
       const int off = a.p_shift >= 0 ? (tc & ((1 << a.p_shift) - 1)) : tc - (tc / a.P) * a.P;
       return ((int64_t(page) * a.P + off) * a.Hk + hk) * (D * ES) + j * 16;
     };
-    int32_t pg_next = page_of(item.kv_start + 16 + n);
-    u32x4 kr[NL], vr[NL];
-    {
-      const int64_t base = row_base(item.kv_start + n, page_of(item.kv_start + n));
+    auto load_rows = [&](u32x4 (&kd)[NL], u32x4 (&vd)[NL], int t, int32_t page) {
+      const int64_t base = row_base(t, page);
 #pragma unroll
       for (int l = 0; l < NL; ++l) {
-        kr[l] = *reinterpret_cast<const u32x4*>(K + base + 64 * l);
-        vr[l] = *reinterpret_cast<const u32x4*>(V + base + 64 * l);
+        kd[l] = *reinterpret_cast<const u32x4*>(K + base + 64 * l);
+        vd[l] = *reinterpret_cast<const u32x4*>(V + base + 64 * l);
       }
-    }
-
-    for (int t0 = item.kv_start; t0 < kv_end; t0 += 16) {
-      const bool has_next = t0 + 16 < kv_end;
-      const int32_t pg_after = page_of(t0 + 32 + n);
-      // request the next step's rows before touching this step's data
-      u32x4 kn[NL], vn[NL];
-      if (has_next) {
-        const int64_t base = row_base(t0 + 16 + n, pg_next);
-#pragma unroll
-        for (int l = 0; l < NL; ++l) {
-          kn[l] = *reinterpret_cast<const u32x4*>(K + base + 64 * l);
-          vn[l] = *reinterpret_cast<const u32x4*>(V + base + 64 * l);
-        }
-      }
-      pg_next = pg_after;
-
+    };
+    // one step: tokens t0 .. t0 + 15 (lane n: token t0 + n) from the rows in kr / vr
+    auto compute = [&](int t0, const u32x4 (&kr)[NL], const u32x4 (&vr)[NL]) {
       // scores S^T[token 4j+i][head n]
       f32x4 S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -191,13 +174,54 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
             (__attribute__((address_space(3))) s16x4*)(vtr + db * 16));
         oacc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, oacc[db], 0, 0, 0);
       }
+    };
 
-      if (has_next) {
+    if constexpr (PD == 1) {
+      int32_t pg_next = page_of(item.kv_start + 16 + n);
+      u32x4 kr[NL], vr[NL];
+      load_rows(kr, vr, item.kv_start + n, page_of(item.kv_start + n));
+      for (int t0 = item.kv_start; t0 < kv_end; t0 += 16) {
+        const bool has_next = t0 + 16 < kv_end;
+        const int32_t pg_after = page_of(t0 + 32 + n);
+        // request the next step's rows before touching this step's data
+        u32x4 kn[NL], vn[NL];
+        if (has_next) load_rows(kn, vn, t0 + 16 + n, pg_next);
+        pg_next = pg_after;
+        compute(t0, kr, vr);
+        if (has_next) {
 #pragma unroll
-        for (int l = 0; l < NL; ++l) {
-          kr[l] = kn[l];
-          vr[l] = vn[l];
+          for (int l = 0; l < NL; ++l) {
+            kr[l] = kn[l];
+            vr[l] = vn[l];
+          }
         }
+      }
+    } else {
+      // E4M3: 32 tokens per step, two 16-token halves loaded together, so a wave has as many
+      // bytes in flight as with one step of bf16 rows
+      int32_t pg_next0 = page_of(item.kv_start + 32 + n), pg_next1 = page_of(item.kv_start + 48 + n);
+      u32x4 kr[2][NL], vr[2][NL];
+      load_rows(kr[0], vr[0], item.kv_start + n, page_of(item.kv_start + n));
+      load_rows(kr[1], vr[1], item.kv_start + 16 + n, page_of(item.kv_start + 16 + n));
+      for (int t0 = item.kv_start; t0 < kv_end; t0 += 32) {
+        const bool has_next = t0 + 32 < kv_end;
+        const int32_t pa0 = page_of(t0 + 64 + n), pa1 = page_of(t0 + 80 + n);
+        // (unconditional: past the end the rows clamp to the chunk's last row)
+        u32x4 kn[2][NL], vn[2][NL];
+        load_rows(kn[0], vn[0], t0 + 32 + n, pg_next0);
+        load_rows(kn[1], vn[1], t0 + 48 + n, pg_next1);
+        compute(t0, kr[0], vr[0]);
+        if (t0 + 16 < kv_end) compute(t0 + 16, kr[1], vr[1]);
+        pg_next0 = pa0;
+        pg_next1 = pa1;
+        (void)has_next;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int l = 0; l < NL; ++l) {
+            kr[h2][l] = kn[h2][l];
+            vr[h2][l] = vn[h2][l];
+          }
       }
     }
 
