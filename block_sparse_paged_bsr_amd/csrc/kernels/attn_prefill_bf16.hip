@@ -428,12 +428,14 @@ struct VarRow {
   int lo = INT_MIN, max_lo = INT_MIN;
   float k1 = 0.f, k2 = 0.f;
   int64_t mrow = -1;
-  bool masked = false;  // a custom mask is given (uniform): every block is tested
+  int64_t last_byte = 0;  // last byte holding bits of this request (custom mask)
+  bool masked = false;    // a custom mask is given (uniform): every block is tested
   __device__ __forceinline__ VarRow(const RunArgs& a, const ItemRec& item, const ReqRec& rq, int row_pos,
                                     bool row_ok) {
     if (a.mask) {
       masked = true;
       if (row_ok) mrow = rq.mask_off + int64_t(row_pos) * rq.kv_len;
+      last_byte = (rq.mask_off + int64_t(rq.q_len) * rq.kv_len - 1) >> 3;
     }
     if (a.window_left >= 0) {
       const int base = rq.kv_len - rq.q_len - a.window_left;
@@ -446,14 +448,24 @@ struct VarRow {
     }
   }
   __device__ __forceinline__ float cap(float s) const { return k1 * fast_tanh(k2 * s); }
-  // whether key tok takes part: inside [lo, lim) and, with a custom mask, its bit set.  The
-  // mask byte is read unconditionally (bit 0 for keys outside the row's range or absent rows,
-  // so every address is inside the mask) and combined without a branch.
-  __device__ __forceinline__ bool keeps(const uint8_t* __restrict__ mask, int tok, int lim) const {
+  // With a custom mask: this row's bits of keys tb .. tb + 31 (bit k for key tb + k), from the
+  // five bytes that hold them; each byte index is clamped to the request's last byte, so every
+  // load is inside the mask (clamped bytes only serve keys past the row, which keeps_at drops).
+  __device__ __forceinline__ uint32_t window(const uint8_t* __restrict__ mask, int tb) const {
+    if (!masked) return 0u;  // uniform
+    const int64_t bit0 = (mrow >= 0 ? mrow : 0) + tb;
+    const int64_t b0 = bit0 >> 3;
+    uint64_t w = 0;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) w |= uint64_t(mask[min(b0 + q, last_byte)]) << (8 * q);
+    return uint32_t(w >> (bit0 & 7));
+  }
+  // whether key tok = tb + k takes part: inside [lo, lim) and, with a custom mask, its bit in
+  // win = window(mask, tb) set; combined without a branch (the loads happen in window())
+  __device__ __forceinline__ bool keeps_at(uint32_t win, int k, int tok, int lim) const {
     const bool in = tok < lim && tok >= lo;
     if (!masked) return in;  // uniform
-    const bool live = in & (mrow >= 0);
-    return live & mask_bit(mask, live ? mrow + tok : 0);
+    return in & (mrow >= 0) & ((win >> k) & 1u);
   }
 };
 
@@ -536,10 +548,11 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
         for (int i = 0; i < 16; ++i) S[i] = var.cap(S[i]);
       }
       if (var.masked || t0 + 32 * (ks + 1) > min_lim || t0 + 32 * ks < var.max_lo) {
+        const uint32_t win = var.window(a.mask, t0 + 32 * ks);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int tok = t0 + 32 * ks + 8 * (i >> 2) + 4 * h + (i & 3);
-          S[i] = var.keeps(a.mask, tok, lim) ? S[i] : kNegInf;
+          const int k = 8 * (i >> 2) + 4 * h + (i & 3), tok = t0 + 32 * ks + k;
+          S[i] = var.keeps_at(win, k, tok, lim) ? S[i] : kNegInf;
         }
       }
     } else if (t0 + 32 * (ks + 1) > min_lim) {
@@ -954,12 +967,14 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
           for (int i = 0; i < 4; ++i) S[b][i] = var.cap(S[b][i]);
       }
       if (var.masked || t0 + kTileKV > min_lim || t0 < var.max_lo) {
+        const int tb = t0 + ks * NT * 16;  // this wave's keys: tb .. tb + 16 NT - 1 (NT <= 2)
+        const uint32_t win = var.window(a.mask, tb);
 #pragma unroll
         for (int b = 0; b < NT; ++b)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int tok = t0 + (ks * NT + b) * 16 + 4 * j + i;
-            S[b][i] = var.keeps(a.mask, tok, lim) ? S[b][i] : kNegInf;
+            const int k = b * 16 + 4 * j + i, tok = tb + k;
+            S[b][i] = var.keeps_at(win, k, tok, lim) ? S[b][i] : kNegInf;
           }
       }
     } else if (t0 + kTileKV > min_lim) {
