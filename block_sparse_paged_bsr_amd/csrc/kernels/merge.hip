@@ -33,24 +33,30 @@ __device__ __forceinline__ float load_in<uint16_t>(const uint16_t* p) { return _
 
 }  // namespace
 
-// One workgroup per (merge tile, KV head).  Phase 1: the maximum and denominator of
-// every row's partial LSEs, with the tile's slot list staged in LDS.  Phase 2: every
-// (row, d) element folds the partial outputs in slot order.  Small tiles (at most
-// kFastSlots slots and two elements per thread, e.g. every split decode tile) load their
-// partial outputs before phase 1, so those loads overlap the LSE reads, and phase 1 leaves
-// each (slot, row) weight in LDS.
+// One workgroup per (merge tile, chunk of kRowChunk rows, KV head), so a tile of many rows and
+// many slots (a long shared prefix cut into many chunks) is merged by many workgroups.  Phase 1:
+// the maximum, denominator and per-slot weights e^(lse_s - m) of every row of the chunk, with the
+// tile's slot list staged in LDS and the weights kept there (kWeightSlots slots; any further
+// slot's weight is recomputed from its LSE, the same expression).  Phase 2: every (row, d)
+// element folds the partial outputs in slot order.  Small chunks (at most kFastSlots slots and
+// two elements per thread, e.g. every split decode tile) load their partial outputs before
+// phase 1, so those loads overlap the LSE reads.
 constexpr int kMergeThreads = 256;
 constexpr int kSlotsInLds = 1024;
 constexpr int kFastSlots = 8;
+constexpr int kRowChunk = 16;
+constexpr int kWeightSlots = 256;
 
 template <typename OutT>
-__global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a, int row_chunks) {
   __shared__ int s_slot[kSlotsInLds];
-  __shared__ float s_m[128], s_den[128], s_w[kFastSlots * 128];
+  __shared__ float s_m[kRowChunk], s_den[kRowChunk], s_w[kWeightSlots * kRowChunk];
   const int hk = blockIdx.y, tid = threadIdx.x;
-  const MergeRec mr = a.merge[blockIdx.x];
+  const int mi = blockIdx.x / row_chunks, r0 = (blockIdx.x % row_chunks) * kRowChunk;
+  const MergeRec mr = a.merge[mi];
+  const int nrows = min(kRowChunk, mr.row_end - mr.row_start - r0);  // rows r0 .. r0 + nrows - 1
+  if (nrows <= 0) return;  // uniform: a chunk past the tile's last row
   const ReqRec rq = a.req[mr.req];
-  const int nrows = mr.row_end - mr.row_start;  // <= T_q <= 128
   const int ns = mr.slot_count;
   const int D = a.d;
   const int* __restrict__ slots = a.mslots + mr.slot_begin;
@@ -59,7 +65,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a
     for (int k = tid; k < ns; k += kMergeThreads) s_slot[k] = slots[k];
   __syncthreads();
   auto slot_at = [&](int k) { return cached ? s_slot[k] : slots[k]; };
-  auto lse_at = [&](int s, int r) { return a.part_lse[(int64_t(s) * a.Hk + hk) * a.Tq + r]; };
+  // partial-state row of slot s for row r of this chunk
+  auto prow_at = [&](int s, int r) { return (int64_t(s) * a.Hk + hk) * a.Tq + r0 + r; };
 
   const bool fast = ns <= kFastSlots && nrows * D <= 2 * kMergeThreads;  // uniform
   float ov[2][kFastSlots];
@@ -71,8 +78,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a
 #pragma unroll
       for (int k = 0; k < kFastSlots; ++k) {
         ov[u][k] = 0.f;
-        if (idx < nrows * D && k < ns)
-          ov[u][k] = a.part_o[((int64_t(slot_at(k)) * a.Hk + hk) * a.Tq + lr) * D + e];
+        if (idx < nrows * D && k < ns) ov[u][k] = a.part_o[prow_at(slot_at(k), lr) * D + e];
       }
     }
   }
@@ -84,15 +90,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a
   const int r = tid / tpr, sub = tid % tpr;
   float mx = kNegInf;
   if (r < nrows)
-    for (int k = sub; k < ns; k += tpr) mx = fmaxf(mx, lse_at(slot_at(k), r));
+    for (int k = sub; k < ns; k += tpr) mx = fmaxf(mx, a.part_lse[prow_at(slot_at(k), r)]);
   for (int o = 1; o < tpr; o <<= 1) mx = fmaxf(mx, shfl_xor(mx, o));
   float den = 0.f;
   if (r < nrows && mx != kNegInf)
     for (int k = sub; k < ns; k += tpr) {
-      const float l = lse_at(slot_at(k), r);
+      const float l = a.part_lse[prow_at(slot_at(k), r)];
       const float w = l == kNegInf ? 0.f : expf(l - mx);
       den += w;
-      if (fast) s_w[k * 128 + r] = w;
+      if (k < kWeightSlots) s_w[k * kRowChunk + r] = w;
     }
   for (int o = 1; o < tpr; o <<= 1) den += shfl_xor(den, o);
   if (r < nrows && sub == 0) {
@@ -103,6 +109,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a
 
   // phase 2: weighted sum of the partial outputs, slot order fixed by the plan
   OutT* O = static_cast<OutT*>(a.o);
+  auto finish = [&](int lr, int e, float acc) {
+    const float m = s_m[lr];
+    const int row = mr.row_start + r0 + lr;
+    const int64_t orow = int64_t(rq.q_start + row / a.g) * a.Hq + hk * a.g + row % a.g;
+    store_out<OutT>(O + orow * D + e, m == kNegInf ? 0.f : acc / s_den[lr]);
+    if (e == 0) a.lse[orow] = m == kNegInf ? kNegInf : m + logf(s_den[lr]);
+  };
   if (fast) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -113,11 +126,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a
       float acc = 0.f;
 #pragma unroll
       for (int k = 0; k < kFastSlots; ++k)
-        if (k < ns && m != kNegInf) acc += s_w[k * 128 + lr] * ov[u][k];
-      const int row = mr.row_start + lr;
-      const int64_t orow = int64_t(rq.q_start + row / a.g) * a.Hq + hk * a.g + row % a.g;
-      store_out<OutT>(O + orow * D + e, m == kNegInf ? 0.f : acc / s_den[lr]);
-      if (e == 0) a.lse[orow] = m == kNegInf ? kNegInf : m + logf(s_den[lr]);
+        if (k < ns && m != kNegInf) acc += s_w[k * kRowChunk + lr] * ov[u][k];
+      finish(lr, e, acc);
     }
     return;
   }
@@ -126,19 +136,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a
     const float m = s_m[lr];
     float acc = 0.f;
     if (m != kNegInf) {
-#pragma unroll 4
-      for (int k = 0; k < ns; ++k) {
-        const int s = slot_at(k);
-        const int64_t prow = (int64_t(s) * a.Hk + hk) * a.Tq + lr;
+      const int nw = min(ns, kWeightSlots);
+#pragma unroll 8
+      for (int k = 0; k < nw; ++k) acc += s_w[k * kRowChunk + lr] * a.part_o[prow_at(slot_at(k), lr) * D + e];
+      for (int k = nw; k < ns; ++k) {
+        const int64_t prow = prow_at(slot_at(k), lr);
         const float l = a.part_lse[prow];
-        const float wgt = l == kNegInf ? 0.f : expf(l - m);
-        acc += wgt * a.part_o[prow * D + e];
+        acc += (l == kNegInf ? 0.f : expf(l - m)) * a.part_o[prow * D + e];
       }
     }
-    const int row = mr.row_start + lr;
-    const int64_t orow = int64_t(rq.q_start + row / a.g) * a.Hq + hk * a.g + row % a.g;
-    store_out<OutT>(O + orow * D + e, m == kNegInf ? 0.f : acc / s_den[lr]);
-    if (e == 0) a.lse[orow] = m == kNegInf ? kNegInf : m + logf(s_den[lr]);
+    finish(lr, e, acc);
   }
 }
 
@@ -179,9 +186,10 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(RunArgs a, int64_t* ro
 
 hipError_t launch_merge(const RunArgs& a, int dtype, hipStream_t s) {
   if (a.num_merge == 0) return hipSuccess;
-  dim3 grid(a.num_merge, a.Hk), block(256);
-  if (dtype == BSR_DTYPE_F32) hipLaunchKernelGGL(merge_partials_kernel<float>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(merge_partials_kernel<uint16_t>, grid, block, 0, s, a);
+  const int row_chunks = (a.Tq + kRowChunk - 1) / kRowChunk;
+  dim3 grid(a.num_merge * row_chunks, a.Hk), block(kMergeThreads);
+  if (dtype == BSR_DTYPE_F32) hipLaunchKernelGGL(merge_partials_kernel<float>, grid, block, 0, s, a, row_chunks);
+  else hipLaunchKernelGGL(merge_partials_kernel<uint16_t>, grid, block, 0, s, a, row_chunks);
   return hipGetLastError();
 }
 
