@@ -187,6 +187,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(RunArgs a, int64_t* ro
 hipError_t launch_merge(const RunArgs& a, int dtype, hipStream_t s) {
   if (a.num_merge == 0) return hipSuccess;
   const int row_chunks = (a.Tq + kRowChunk - 1) / kRowChunk;
+  if (int64_t(a.num_merge) * row_chunks > INT32_MAX) return hipErrorInvalidConfiguration;
   dim3 grid(a.num_merge * row_chunks, a.Hk), block(kMergeThreads);
   if (dtype == BSR_DTYPE_F32) hipLaunchKernelGGL(merge_partials_kernel<float>, grid, block, 0, s, a, row_chunks);
   else hipLaunchKernelGGL(merge_partials_kernel<uint16_t>, grid, block, 0, s, a, row_chunks);
