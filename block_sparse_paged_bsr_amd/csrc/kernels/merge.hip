@@ -137,8 +137,18 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a
     float acc = 0.f;
     if (m != kNegInf) {
       const int nw = min(ns, kWeightSlots);
+      // unrolled by the slot count (uniform), so that the loads of a short fold are issued together
+      auto fold = [&](int k) { acc += s_w[k * kRowChunk + lr] * a.part_o[prow_at(slot_at(k), lr) * D + e]; };
+      if (nw >= 8) {
 #pragma unroll 8
-      for (int k = 0; k < nw; ++k) acc += s_w[k * kRowChunk + lr] * a.part_o[prow_at(slot_at(k), lr) * D + e];
+        for (int k = 0; k < nw; ++k) fold(k);
+      } else if (nw >= 4) {
+#pragma unroll 4
+        for (int k = 0; k < nw; ++k) fold(k);
+      } else {
+#pragma unroll 2
+        for (int k = 0; k < nw; ++k) fold(k);
+      }
       for (int k = nw; k < ns; ++k) {
         const int64_t prow = prow_at(slot_at(k), lr);
         const float l = a.part_lse[prow];
