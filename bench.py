@@ -181,7 +181,7 @@ def graph_replay_ms(step, steps, warmup, variants=3):
 
 
 def bench_decode(args):
-    from block_sparse_paged_bsr_amd import inputs
+    import workloads as inputs
 
     b = inputs.batched_decode_bf16(seed=0, poison=False)
     r = run_case(b, "decode", args.steps, args.warmup, rotate=3)
@@ -196,7 +196,7 @@ def bench_decode(args):
 
 
 def bench_prefill(args):
-    from block_sparse_paged_bsr_amd import inputs
+    import workloads as inputs
 
     b = inputs.ragged_prefill_bf16(seed=0, poison=False)
     # ~1 ms per call: enough warm-up calls for the clocks to settle, then a few tens timed
@@ -223,7 +223,7 @@ def bench_variants(args):
     sliding window on batch-64 decode; 16 speculative draft tokens per decode request under a
     tree mask (custom mask) and under the causal mask; soft cap 50, a 1024-key window, and
     both, on the ragged causal prefill.  Rates count only the visible KV (window) or pairs."""
-    from block_sparse_paged_bsr_amd import inputs
+    import workloads as inputs
 
     out = {}
     b = inputs.batched_decode_bf16(seed=0, poison=False)
@@ -293,7 +293,8 @@ def bench_e4m3(args, num_workers=None):
     """Batch-64 paged decode with K and V stored as E4M3 bytes (per-tensor scales): the same
     requests and page tables as the bf16 headline, half the KV bytes."""
     import torch
-    from block_sparse_paged_bsr_amd import api, inputs
+    from block_sparse_paged_bsr_amd import api
+    import workloads as inputs
 
     b = inputs.batched_decode_bf16(seed=0, poison=False)
     e = inputs.to_e4m3(b)
@@ -322,7 +323,7 @@ def bench_e4m3(args, num_workers=None):
 
 def bench_vector_sparse(args):
     """Page size 1 over a 2^20-row pool vs the same contents contiguous."""
-    from block_sparse_paged_bsr_amd import inputs
+    import workloads as inputs
 
     out = {}
     lens = inputs.decode_lengths(0)
@@ -351,7 +352,8 @@ def bench_composable(args):
     """Two BSR views (shared prefix at 4 queries per block row, private suffixes) merged,
     vs the single-level view (each request reads prefix ++ suffix itself)."""
     import torch
-    from block_sparse_paged_bsr_amd import api, inputs
+    from block_sparse_paged_bsr_amd import api
+    import workloads as inputs
 
     b = inputs.shared_prefix_decode(seed=0, poison=False)
     q, k, v = b.torch_values("cuda")
@@ -469,7 +471,8 @@ def bench_cascade(args):
     """Three BSR views (a prompt shared by all 64 requests, 16 group prefixes of 4, private
     suffixes) merged left to right, vs the single-level view over the same pages."""
     import torch
-    from block_sparse_paged_bsr_amd import api, inputs
+    from block_sparse_paged_bsr_amd import api
+    import workloads as inputs
 
     b = inputs.cascade_decode(seed=0, poison=False)
     q, k, v = b.torch_values("cuda")
@@ -562,7 +565,8 @@ def bench_shared_prefix(args):
     (no pool rotation).  The composed and single-level outputs are compared with each other
     here; tests/test_gpu_shared_prefix.py checks both shapes against the oracle."""
     import torch
-    from block_sparse_paged_bsr_amd import api, inputs
+    from block_sparse_paged_bsr_amd import api
+    import workloads as inputs
 
     out = {}
     for R, P in ((64, 32768), (16, 1024)):

@@ -46,7 +46,7 @@ class PlanDesc(C.Structure):
         ("tile_q", C.c_int32),
         ("alpha", C.c_int32),
         ("beta", C.c_int32),
-        ("window_left", C.c_int32),
+        ("window_size", C.c_int32),
         ("logits_soft_cap", C.c_float),
     ]
 

@@ -84,7 +84,9 @@ class Plan:
             tile_q=int(tile_q),
             alpha=int(alpha),
             beta=int(beta),
-            window_left=int(window_left),
+            # the ABI counts the window in keys (0 = none); window_left keeps the pages'
+            # notation, keys left of the diagonal (-1 = none)
+            window_size=int(window_left) + 1,
             logits_soft_cap=float(logits_soft_cap),
         )
         h = C.c_void_p()
@@ -93,6 +95,8 @@ class Plan:
         self.num_qo_heads = int(num_qo_heads)
         self.num_kv_heads = int(num_kv_heads)
         self.head_dim = int(head_dim)
+        self.num_pages = int(num_pages)
+        self.page_size = int(page_size)
         self.decode = qo_indptr is None
         self.batch = len(kv_indptr) - 1
         self.total_q = self.batch if qo_indptr is None else int(qo_indptr[-1])
@@ -170,6 +174,38 @@ def alloc_workspace(p: Plan, device="cuda"):
     return torch.empty(max(p.workspace_bytes(), 256), dtype=torch.uint8, device=device)
 
 
+def _check_run_args(p: Plan, q, k_cache, v_cache, o, lse, kv_dtypes=None):
+    """Reject, before any launch, arguments the kernels would read or write out of bounds:
+    shapes against the plan (the cache must hold the plan's num_pages pages of page_size
+    tokens), dtypes, then device placement and layout."""
+    import torch
+
+    want_q = (p.total_q, p.num_qo_heads, p.head_dim)
+    if tuple(q.shape) != want_q or tuple(o.shape) != want_q:
+        raise ValueError(f"q/o shapes {tuple(q.shape)}, {tuple(o.shape)} != {want_q}")
+    if tuple(lse.shape) != (p.total_q, p.num_qo_heads):
+        raise ValueError(f"lse shape {tuple(lse.shape)} != {(p.total_q, p.num_qo_heads)}")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dim() != 4 or tuple(t.shape[1:]) != (p.page_size, p.num_kv_heads, p.head_dim):
+            raise ValueError(f"{name} shape {tuple(t.shape)} is not [num_pages, {p.page_size}, "
+                             f"{p.num_kv_heads}, {p.head_dim}]")
+        if t.shape[0] < p.num_pages:
+            raise ValueError(f"{name} holds {t.shape[0]} pages, the plan indexes {p.num_pages}")
+    if kv_dtypes is None:
+        if not (q.dtype == k_cache.dtype == v_cache.dtype == o.dtype):
+            raise TypeError("q/k/v/o must share one dtype")
+    else:
+        if q.dtype != torch.bfloat16 or o.dtype != torch.bfloat16:
+            raise TypeError("q and o must be bfloat16")
+        if k_cache.dtype not in kv_dtypes or v_cache.dtype != k_cache.dtype:
+            raise TypeError("k_cache/v_cache must hold E4M3 bytes (uint8 or float8_e4m3fn)")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("o", o), ("lse", lse)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+
+
 def _run(fn, p: Plan, ws, q, k_cache, v_cache, o, lse, sm_scale, stream):
     import torch
 
@@ -179,15 +215,7 @@ def _run(fn, p: Plan, ws, q, k_cache, v_cache, o, lse, sm_scale, stream):
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty(q.shape[0], p.num_qo_heads, dtype=torch.float32, device=q.device)
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("o", o), ("lse", lse)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
-    if not (q.dtype == k_cache.dtype == v_cache.dtype == o.dtype) or lse.dtype != torch.float32:
-        raise TypeError("q/k/v/o must share one dtype and lse must be float32")
-    if tuple(q.shape) != (p.total_q, p.num_qo_heads, p.head_dim) or q.shape != o.shape:
-        raise ValueError(f"q/o shape {tuple(q.shape)} != {(p.total_q, p.num_qo_heads, p.head_dim)}")
-    if k_cache.shape[-2:] != (p.num_kv_heads, p.head_dim) or k_cache.shape != v_cache.shape:
-        raise ValueError("k_cache/v_cache must be [num_pages, page_size, num_kv_heads, head_dim]")
+    _check_run_args(p, q, k_cache, v_cache, o, lse)
     check(
         fn(
             p.handle,
@@ -254,17 +282,7 @@ def run_decode_e4m3(p: Plan, ws, q, k_cache, v_cache, k_scale: float, v_scale: f
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty(q.shape[0], p.num_qo_heads, dtype=torch.float32, device=q.device)
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("o", o), ("lse", lse)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
-    if q.dtype != torch.bfloat16 or o.dtype != torch.bfloat16 or lse.dtype != torch.float32:
-        raise TypeError("q and o must be bfloat16 and lse float32")
-    if k_cache.dtype not in (torch.uint8, torch.float8_e4m3fn) or v_cache.dtype != k_cache.dtype:
-        raise TypeError("k_cache/v_cache must hold E4M3 bytes (uint8 or float8_e4m3fn)")
-    if tuple(q.shape) != (p.total_q, p.num_qo_heads, p.head_dim) or q.shape != o.shape:
-        raise ValueError(f"q/o shape {tuple(q.shape)} != {(p.total_q, p.num_qo_heads, p.head_dim)}")
-    if k_cache.shape[-2:] != (p.num_kv_heads, p.head_dim) or k_cache.shape != v_cache.shape:
-        raise ValueError("k_cache/v_cache must be [num_pages, page_size, num_kv_heads, head_dim]")
+    _check_run_args(p, q, k_cache, v_cache, o, lse, kv_dtypes=(torch.uint8, torch.float8_e4m3fn))
     check(
         lib().bsr_run_decode_e4m3(
             p.handle, C.c_void_p(ws.data_ptr()), C.c_void_p(q.data_ptr()), C.c_void_p(k_cache.data_ptr()),
@@ -284,12 +302,21 @@ def merge_state(o_a, lse_a, o_b, lse_b, o_out=None, lse_out=None, stream=None):
         o_out = torch.empty_like(o_a)
     if lse_out is None:
         lse_out = torch.empty_like(lse_a)
+    if o_a.dim() != 3:
+        raise ValueError("o_a must be [rows, heads, head_dim]")
     rows, heads, d = o_a.shape
+    if o_b.shape != o_a.shape or o_out.shape != o_a.shape:
+        raise ValueError("merge_state: o_a, o_b and o_out must have one shape")
+    for name, t in (("lse_a", lse_a), ("lse_b", lse_b), ("lse_out", lse_out)):
+        if tuple(t.shape) != (rows, heads):
+            raise ValueError(f"merge_state: {name} shape {tuple(t.shape)} != {(rows, heads)}")
+        if t.dtype != torch.float32:
+            raise TypeError(f"merge_state: {name} must be float32")
+    if not (o_a.dtype == o_b.dtype == o_out.dtype):
+        raise TypeError("merge_state: o_a, o_b and o_out must share one dtype")
     for t in (o_a, lse_a, o_b, lse_b, o_out, lse_out):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("merge_state arguments must be contiguous device tensors")
-    if o_b.shape != o_a.shape or o_out.shape != o_a.shape or lse_a.shape != (rows, heads):
-        raise ValueError("merge_state shape mismatch")
     fp = C.POINTER(C.c_float)
     check(
         lib().bsr_merge_state(

@@ -32,7 +32,7 @@
 // scale is folded into the score scale and the V scale into the output normalisation, so the
 // loop does no extra multiplications; the bytes read per token are half of bf16's, and a step
 // covers 32 tokens (two 16-token halves loaded together) to keep a bf16 step's bytes in flight.
-#include "common.cuh"
+#include "common.h"
 #include "launch.h"
 
 namespace bsr {

@@ -12,7 +12,7 @@
 // visible key of each row, and a logits soft cap c replaces each scaled score s by
 // c tanh(s / c) before the softmax; a custom mask (one bit per query and key, §VII LogitsMask)
 // drops the keys whose bit is clear.
-#include "common.cuh"
+#include "common.h"
 #include "launch.h"
 
 namespace bsr {

@@ -60,7 +60,7 @@
 #include <climits>
 #include <type_traits>
 
-#include "common.cuh"
+#include "common.h"
 #include "launch.h"
 
 namespace bsr {

@@ -10,7 +10,7 @@
 // (§VIII.3: no atomics).  Folding k states with one shared maximum m gives the same
 // value as the left fold of pairwise merges in exact arithmetic: both equal
 // sum_s e^(lse_s - m) O_s / sum_s e^(lse_s - m).
-#include "common.cuh"
+#include "common.h"
 #include "launch.h"
 
 namespace bsr {

@@ -52,7 +52,7 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
     return fail("tile_q must be 0 or a multiple of 16 up to 128");
   if (desc->alpha < 0 || desc->beta < 0) return fail("alpha and beta must be >= 0");
   if (desc->num_pages < 0) return fail("num_pages must be >= 0");
-  if (desc->window_left < -1) return fail("window_left must be -1 (no window) or >= 0");
+  if (desc->window_size < 0) return fail("window_size must be 0 (no window) or >= 1");
   if (!(desc->logits_soft_cap >= 0.f) || desc->logits_soft_cap == __builtin_huge_valf())
     return fail("logits_soft_cap must be 0 (off) or positive and finite");
   if (B > 0 && (!desc->kv_indptr || !desc->last_page_len))
@@ -73,7 +73,7 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
     p->beta = 1;
   }
   p->num_pages = desc->num_pages;
-  p->window_left = desc->window_left;
+  p->window_left = desc->window_size - 1;  // keys left of the diagonal, -1 = no window
   p->soft_cap = desc->logits_soft_cap;
   p->decode = desc->qo_indptr == nullptr;
 

@@ -78,13 +78,14 @@ typedef struct bsr_plan_desc {
   int32_t tile_q;               /* packed query rows per tile; 0 => tile rule */
   int32_t alpha, beta;          /* item cost = alpha * (query positions of its tile) +
                                    beta * chunk_len; both 0 => (2, 1) */
-  int32_t window_left;          /* sliding window: -1 = none (note: a zero-filled
-                                   description asks for a window of 0, which keeps only
-                                   the diagonal key); w >= 0 => key k is visible to query q
-                                   only if k + l_qo + w >= l_kv + q, i.e. the w keys left of
-                                   q's aligned position and that position itself
-                                   ("FlashInfer 原理" §⑧, the mask of the window variant).
-                                   Combines with causal, which supplies the upper bound. */
+  int32_t window_size;          /* sliding window, in keys: 0 = none (so a zero-filled
+                                   description asks for no window); s >= 1 => key k is
+                                   visible to query q only if k + l_qo + (s - 1) >= l_kv + q,
+                                   i.e. the s keys that end at q's aligned position
+                                   ("FlashInfer 原理" §⑧, the mask of the window variant,
+                                   whose window_left is s - 1).  Combines with causal, which
+                                   supplies the upper bound.  Negative values are
+                                   BSR_INVALID_ARG. */
   float logits_soft_cap;        /* 0 = none; c > 0 => every score s = sm_scale * q.k is
                                    replaced by c * tanh(s / c) before masking and softmax
                                    ("FlashInfer: Making Attention Fit the Serving Workload"
@@ -124,15 +125,35 @@ void bsr_plan_destroy(bsr_plan* plan);
 int bsr_plan_workspace_bytes(const bsr_plan* plan, size_t* bytes);
 
 /*
- * Copy the plan metadata into `dev_ws` (device, >= bsr_plan_workspace_bytes) on
- * `stream`, asynchronously, from library-owned pinned staging.  Returns BSR_CAPACITY
- * if ws_bytes is too small.  The run calls must use the same workspace pointer.
+ * Copy the plan metadata (work queue per worker, partial -> final reduction map, request
+ * records and the page list) into fixed offsets of `dev_ws` (device, >=
+ * bsr_plan_workspace_bytes) on `stream`, asynchronously, from pinned host staging the
+ * plan owns: the CPU plans, the copy goes to a fixed workspace offset, and the GPU runs
+ * from there ("FlashInfer: Engineering a Customizable, Block-Sparse Attention Engine for
+ * LLM Inference Serving" §VIII.4; "FlashInfer: Making Attention Fit the Serving Workload"
+ * §6.3, whose serving-step lifecycle copies metadata into fixed workspace sections and
+ * orders that copy before the run).
+ *   - Ordering: the copy is ordered only on `stream`.  A run call on another stream must
+ *     be ordered after it by the caller (an event or stream wait); the run calls do not
+ *     wait for the upload themselves.
+ *   - The host staging is filled at the first upload and reused; the plan keeps it until
+ *     bsr_plan_destroy, which first waits for the last upload's copy.
+ *   - Errors: BSR_INVALID_ARG for a NULL plan or workspace; BSR_CAPACITY if ws_bytes is
+ *     below bsr_plan_workspace_bytes (nothing is copied); BSR_HIP_ERROR if the pinned
+ *     allocation, the copy or the event record fails.
+ *   - The run calls must pass the same workspace pointer (they check it).
  */
 int bsr_plan_upload(bsr_plan* plan, void* dev_ws, size_t ws_bytes, void* stream);
 
 /*
- * Read-only host view of a plan, for inspection and parity checks.  Arrays belong to
- * the plan and live until bsr_plan_destroy.
+ * Read-only host view of a plan, for inspection and parity checks: the two outputs of the
+ * scheduler, the work queue of every worker and the partial -> final reduction map
+ * ("FlashInfer: Engineering a Customizable, Block-Sparse Attention Engine for LLM
+ * Inference Serving" §VIII.5, Figure 6: some final outputs come from one partial, others
+ * from several), plus the tiles and items they are built from.  Arrays belong to the plan
+ * and live until bsr_plan_destroy; nothing is copied.  window_left is the window of the
+ * description as keys left of the diagonal (window_size - 1; -1 = no window).  Errors:
+ * BSR_INVALID_ARG for a NULL plan or view.
  *   tiles[num_tiles][5]   = {req, row_start, row_end, vis, n_items}, creation order
  *                           (rows are packed GQA rows of the request; vis = visible
  *                           KV length of the tile)

@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or links t
 package: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may use it.  It shares no code, header, table or helper with the HIP
 library under ``block_sparse_paged_bsr_amd/``; the two meet only through the seeded
-inputs of ``block_sparse_paged_bsr_amd/inputs.py``, which hold no attention or
+inputs of ``workloads.py`` (repository root), which hold no attention or
 planning arithmetic.
 
 Modules

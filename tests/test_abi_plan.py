@@ -12,7 +12,7 @@ import pytest
 
 from block_sparse_paged_bsr_amd import _lib
 from block_sparse_paged_bsr_amd import api
-from block_sparse_paged_bsr_amd import inputs as I
+import workloads as I
 from oracle import plan as PL
 from tests.conftest import ROOT, load_golden
 
@@ -178,7 +178,7 @@ def _desc_errors():
         dict(tile_q=24),
         dict(qo_indptr=[0, 2, 1]),
         dict(qo_indptr=[1, 2, 3]),
-        dict(window_left=-2),
+        dict(window_left=-2),  # window_size -1
         dict(logits_soft_cap=-1.0),
         dict(logits_soft_cap=float("nan")),
         dict(logits_soft_cap=float("inf")),
@@ -233,3 +233,128 @@ def test_pack_custom_mask_layout():
     m0 = np.array([[1, 0, 1], [0, 1, 1]], dtype=bool)
     m1 = np.array([[1, 1]], dtype=bool)
     assert api.pack_custom_mask([m0, m1]).tolist() == [0b11110101]
+
+
+def _raw_plan(desc):
+    h = C.c_void_p()
+    rc = _lib.lib().bsr_plan_create(C.byref(desc), C.byref(h))
+    assert rc == _lib.BSR_OK, _lib.lib().bsr_last_error().decode()
+    return h
+
+
+def _view(h):
+    v = _lib.PlanView()
+    assert _lib.lib().bsr_plan_export(h, C.byref(v)) == _lib.BSR_OK
+    items = np.ctypeslib.as_array(v.items, shape=(v.num_items * 8,)).copy() if v.num_items else np.zeros(0)
+    lo = np.ctypeslib.as_array(v.tile_lo, shape=(v.num_tiles,)).copy() if v.num_tiles else np.zeros(0)
+    return v.window_left, v.total_work, v.chunk_limit, items, lo
+
+
+def test_zero_filled_description_means_no_window():
+    """A C caller that zero-fills bsr_plan_desc and sets only the BSR arrays and sizes gets the
+    unwindowed attention: window_size 0 is "no window" (a window of one key is window_size 1)."""
+    kv = np.array([37, 0, 300, 5], dtype=np.int64)
+    ip, ix, last = I.page_table_from_lengths(kv, 8, np.arange(int(((kv + 7) // 8).sum())))
+    ip, ix, last = (np.ascontiguousarray(a, dtype=np.int32) for a in (ip, ix, last))
+    qo = np.ascontiguousarray([0, 3, 3, 40, 41], dtype=np.int32)
+
+    def desc(**kw):
+        d = _lib.PlanDesc()  # ctypes zero-fills every field
+        d.batch, d.num_pages, d.num_qo_heads, d.num_kv_heads = 4, len(ix), 8, 2
+        d.head_dim, d.page_size, d.causal, d.num_workers = 128, 8, 1, 7
+        d.kv_indptr, d.kv_indices = ip.ctypes.data_as(_lib.i32p), ix.ctypes.data_as(_lib.i32p)
+        d.last_page_len, d.qo_indptr = last.ctypes.data_as(_lib.i32p), qo.ctypes.data_as(_lib.i32p)
+        for k, v in kw.items():
+            setattr(d, k, v)
+        return d
+
+    zero = _raw_plan(desc())
+    try:
+        wl, W, L, items, lo = _view(zero)
+        assert wl == -1 and not lo.any()
+        ref = api.Plan(ip, ix, last, num_pages=len(ix), num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=8,
+                       qo_indptr=qo, causal=True, num_workers=7, window_left=-1)
+        e = ref.export()
+        assert (W, L) == (e["total_work"], e["chunk_limit"]) and np.array_equal(items, e["items"].reshape(-1))
+        # and window_size 1 is the diagonal-only window of the pages' window_left = 0
+        one = _raw_plan(desc(window_size=1))
+        try:
+            wl1, W1, L1, items1, lo1 = _view(one)
+            e0 = api.Plan(ip, ix, last, num_pages=len(ix), num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                          page_size=8, qo_indptr=qo, causal=True, num_workers=7, window_left=0).export()
+            assert wl1 == 0 and W1 == e0["total_work"] and np.array_equal(items1, e0["items"].reshape(-1))
+            assert np.array_equal(lo1, e0["tile_lo"]) and lo1.any()
+        finally:
+            _lib.lib().bsr_plan_destroy(one)
+    finally:
+        _lib.lib().bsr_plan_destroy(zero)
+
+
+def _cpu_tensors(p, pages=None, page_size=None, lse_shape=None, dtype="bfloat16"):
+    import torch
+
+    dt = getattr(torch, dtype)
+    pages = p.num_pages if pages is None else pages
+    P = p.page_size if page_size is None else page_size
+    q = torch.zeros(p.total_q, p.num_qo_heads, p.head_dim, dtype=dt)
+    k = torch.zeros(pages, P, p.num_kv_heads, p.head_dim, dtype=dt)
+    lse = torch.zeros(*(lse_shape or (p.total_q, p.num_qo_heads)), dtype=torch.float32)
+    return q, k, k.clone(), torch.zeros_like(q), lse
+
+
+@pytest.mark.parametrize("bad", ["short_cache", "page_size", "lse_shape", "lse_dtype", "cpu"])
+def test_binding_rejects_mismatched_buffers_before_launch(bad):
+    """The binding checks every buffer against the plan before the C call: a cache with fewer
+    pages than the plan indexes, a different page size, or a short LSE would otherwise reach the
+    kernels as out-of-bounds reads or writes."""
+    import torch
+
+    p = _lib_plan([40, 3, 17], None, 8, 2, 4, P=4)
+    kw = {"short_cache": dict(pages=p.num_pages - 1), "page_size": dict(page_size=8),
+          "lse_shape": dict(lse_shape=(p.total_q - 1, p.num_qo_heads)), "lse_dtype": {}, "cpu": {}}[bad]
+    q, k, v, o, lse = _cpu_tensors(p, **kw)
+    if bad == "lse_dtype":
+        lse = lse.to(torch.float64)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    err = TypeError if bad == "lse_dtype" else ValueError
+    with pytest.raises(err) as ei:
+        api.run_decode(p, ws, q, k, v, o=o, lse=lse)
+    if bad == "cpu":
+        assert "device tensor" in str(ei.value)
+    with pytest.raises(err):
+        api.run_decode_e4m3(p, ws, q, k.to(torch.uint8) if bad != "lse_dtype" else k.to(torch.uint8),
+                            v.to(torch.uint8), 1.0, 1.0, o=o, lse=lse)
+
+
+def test_merge_state_binding_checks_every_lse():
+    import torch
+
+    o = torch.zeros(5, 4, 64)
+    l = torch.zeros(5, 4)
+    with pytest.raises(ValueError):
+        api.merge_state(o, l, o, torch.zeros(4, 4))
+    with pytest.raises(ValueError):
+        api.merge_state(o, l, o, l, o_out=torch.zeros_like(o), lse_out=torch.zeros(5, 3))
+    with pytest.raises(TypeError):
+        api.merge_state(o, l, o, l.double())
+    with pytest.raises(ValueError):  # right shapes, but host tensors
+        api.merge_state(o, l, o, l)
+
+
+def test_prefill_lpt_hand_worked_example_in_the_library():
+    """The C++ planner against the hand-worked prefill schedule itself (not only against the
+    oracle's copy of the rule)."""
+    g = load_golden("lpt_prefill_hand.json")
+    lp = _lib_plan(g["kv_lens"], g["qo_lens"], g["num_qo_heads"], g["num_kv_heads"], g["num_workers"], P=2,
+                   tq=g["tile_q"], causal=g["causal"], alpha=g["alpha"], beta=g["beta"])
+    e = lp.export()
+    assert e["tiles"][:, :4].tolist() == g["expected_tiles"]
+    assert (e["total_work"], e["chunk_limit"]) == (g["expected_total_work"], g["expected_chunk_limit"])
+    assert e["items"][:, [1, 4, 5]].tolist() == g["expected_items"]
+    qp, qi = e["queue_ptr"], e["queue_items"]
+    assert [qi[qp[w]:qp[w + 1]].tolist() for w in range(g["num_workers"])] == g["expected_queues"]
+    assert e["worker_cost"].tolist() == g["expected_worker_cost"]
+    assert e["items"][:, 7].tolist() == g["expected_slots"]
+    assert e["merge_tiles"].tolist() == g["expected_merge_tiles"]
+    mp = e["merge_ptr"]
+    assert [e["merge_slots"][mp[k]:mp[k + 1]].tolist() for k in range(len(mp) - 1)] == g["expected_merge_slots"]

@@ -11,7 +11,7 @@ import math
 import numpy as np
 import pytest
 
-from block_sparse_paged_bsr_amd import inputs as I
+import workloads as I
 from tests.gpu_helpers import compare, log, make_plan, oracle
 
 pytestmark = pytest.mark.gpu

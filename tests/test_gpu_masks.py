@@ -7,7 +7,7 @@ import math
 import numpy as np
 import pytest
 
-from block_sparse_paged_bsr_amd import inputs as I
+import workloads as I
 from oracle import attention as A
 from tests.gpu_helpers import compare, log, make_plan
 

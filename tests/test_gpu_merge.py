@@ -9,7 +9,7 @@ Workload".  Tolerances: bf16 O max-abs 2e-2, LSE max-abs 1e-2.
 import numpy as np
 import pytest
 
-from block_sparse_paged_bsr_amd import inputs as I
+import workloads as I
 from tests.gpu_helpers import compare, log, make_plan, oracle, run_gpu
 
 pytestmark = pytest.mark.gpu

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from block_sparse_paged_bsr_amd import inputs as I
+import workloads as I
 from oracle import attention as A
 from tests.conftest import load_golden
 

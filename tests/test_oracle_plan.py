@@ -135,3 +135,60 @@ def test_causal_long_query_short_kv_has_empty_tiles():
     p = PL.make_plan([8], [64], 1, 1, 4, tile_q=16, causal=True)
     assert [t.vis for t in p.tiles] == [0, 0, 0, 8]
     assert p.merge_tiles[:3] == [0, 1, 2]
+
+
+def _prefill_hand_plan(tp=None, monkeypatch=None):
+    g = load_golden("lpt_prefill_hand.json")
+    if tp is not None:
+        monkeypatch.setattr(PL, "tile_positions", tp)
+    return g, PL.make_plan(g["kv_lens"], g["qo_lens"], g["num_qo_heads"], g["num_kv_heads"], g["num_workers"],
+                           tile_q=g["tile_q"], alpha=g["alpha"], beta=g["beta"], causal=g["causal"])
+
+
+def _matches_prefill_golden(g, p):
+    items = [[it.tile, it.kv_start, it.kv_len] for it in p.items]
+    order = sorted(range(len(p.items)), key=lambda m: -p.items[m].kv_len)
+    return (
+        [[t.req, t.row_start, t.row_end, t.vis] for t in p.tiles] == g["expected_tiles"]
+        and [PL.tile_positions(t, p.group_size) for t in p.tiles] == g["expected_tile_positions"]
+        and p.total_work == g["expected_total_work"]
+        and p.chunk_limit == g["expected_chunk_limit"]
+        and items == g["expected_items"]
+        and order == g["expected_sorted_items"]
+        and p.queues == g["expected_queues"]
+        and p.worker_cost == g["expected_worker_cost"]
+        and [it.slot for it in p.items] == g["expected_slots"]
+        and p.merge_tiles == g["expected_merge_tiles"]
+        and p.merge_slots == g["expected_merge_slots"]
+    )
+
+
+def test_prefill_lpt_hand_worked_example():
+    """The prefill item cost (query positions of the item's own tile) against a schedule worked
+    out by hand (tests/golden/lpt_prefill_hand.json)."""
+    g, p = _prefill_hand_plan()
+    assert _matches_prefill_golden(g, p)
+    costs = [2 * PL.tile_positions(it, p.group_size) + it.kv_len for it in p.items]
+    assert costs == g["expected_item_costs"]
+
+
+# plausible mistakes in the item cost, each planted in the oracle: the whole request's query
+# length charged to every tile, the row count divided by g (floor or ceil), the position span
+# without its + 1
+_WRONG_POSITIONS = {
+    "request_qo_len": None,  # filled in below (needs the plan's requests)
+    "rows_floor_div_g": lambda it, g: (it.row_end - it.row_start) // g,
+    "rows_ceil_div_g": lambda it, g: -(-(it.row_end - it.row_start) // g),
+    "span_without_plus_one": lambda it, g: (it.row_end - 1) // g - it.row_start // g,
+}
+
+
+@pytest.mark.parametrize("variant", sorted(_WRONG_POSITIONS))
+def test_prefill_lpt_golden_rejects_wrong_cost(variant, monkeypatch):
+    gold = load_golden("lpt_prefill_hand.json")
+    tp = _WRONG_POSITIONS[variant]
+    if tp is None:
+        qo = gold["qo_lens"]
+        tp = lambda it, g: qo[it.req]  # noqa: E731
+    g, p = _prefill_hand_plan(tp, monkeypatch)
+    assert not _matches_prefill_golden(g, p), variant

@@ -9,7 +9,7 @@ import math
 
 import numpy as np
 
-from block_sparse_paged_bsr_amd import inputs as I
+import workloads as I
 from oracle import attention as A
 from oracle import plan as PL
 
@@ -62,11 +62,41 @@ def _batch(seed, kv, qo, P=4, Hq=4, Hk=2, d=8):
 
 
 def test_window_predicate_by_hand():
-    # l_qo = 3, l_kv = 6, window 1: query q sees keys k with k >= q + 3 - 1
-    allowed = A.window_allowed(3, 6, 1)
-    for q in range(3):
-        for k in range(6):
-            assert allowed[q, k] == (k + 3 + 1 >= 6 + q)
+    """Masks written out by hand from the meaning of the window: with 3 queries over 6 keys, query
+    q's aligned position is q + 3 (bottom-right), and a window of w keys to the left shows keys
+    q + 3 - w onwards; causal adds the upper bound q + 3."""
+    # w = 1: query 0 (aligned to key 3) sees keys 2.., query 1 keys 3.., query 2 keys 4..
+    w1 = [[0, 0, 1, 1, 1, 1],
+          [0, 0, 0, 1, 1, 1],
+          [0, 0, 0, 0, 1, 1]]
+    assert A.window_allowed(3, 6, 1).astype(int).tolist() == w1
+    # w = 0: from the aligned key on
+    w0 = [[0, 0, 0, 1, 1, 1],
+          [0, 0, 0, 0, 1, 1],
+          [0, 0, 0, 0, 0, 1]]
+    assert A.window_allowed(3, 6, 0).astype(int).tolist() == w0
+    # w = 4: query 0 would start at key -1, i.e. sees every key; query 2 starts at key 1
+    w4 = [[1, 1, 1, 1, 1, 1],
+          [1, 1, 1, 1, 1, 1],
+          [0, 1, 1, 1, 1, 1]]
+    assert A.window_allowed(3, 6, 4).astype(int).tolist() == w4
+    # more queries than keys (4 over 2): query q is aligned to key q - 2, so a window of w = 1
+    # starts at key q - 3 <= 0 and shows both keys to every query; with causal and w = 0 each
+    # query sees only its aligned key, which exists for queries 2 and 3 alone
+    assert A.window_allowed(4, 2, 1).astype(int).tolist() == [[1, 1], [1, 1], [1, 1], [1, 1]]
+    both = A.window_allowed(4, 2, 0) & A.causal_allowed(4, 2)
+    assert both.astype(int).tolist() == [[0, 0], [0, 0], [1, 0], [0, 1]]
+    # combined with causal through the attention itself: each row of 3 queries over 6 keys with
+    # w = 1 sees exactly its aligned key and the one before it
+    b = I.make_paged_batch(5, [6], [3], page_size=2, num_qo_heads=1, num_kv_heads=1, head_dim=4, dtype="f32",
+                           poison=False)
+    o, l = A.batch_attention(b.q_f32, b.k_f32, b.v_f32, b.kv_indptr, b.kv_indices, b.last_page_len, 2, 1, 1, 0.7,
+                             qo_indptr=b.qo_indptr, causal=True, window_left=1)
+    rows = A.physical_rows(b.kv_indptr, b.kv_indices, b.last_page_len, 2, 0)
+    kf, vf = b.k_f32.reshape(-1, 1, 4)[rows, 0], b.v_f32.reshape(-1, 1, 4)[rows, 0]
+    for r, keys in enumerate(([2, 3], [3, 4], [4, 5])):
+        o_ref, l_ref = A.attention_one_head(b.q_f32[r:r + 1, 0], kf[keys], vf[keys], 0.7)
+        assert np.allclose(o[r, 0], o_ref[0], atol=1e-14) and abs(l[r, 0] - l_ref[0]) < 1e-14
 
 
 def test_window_wider_than_context_is_no_window():

@@ -1,4 +1,5 @@
-"""Seeded synthetic workloads shared by the tests, the benchmark and the oracle checks.
+"""Seeded synthetic workloads shared by the tests, the benchmark and the oracle checks
+(a module of its own, outside the library package).
 
 This module only *builds inputs*: request lengths, BSR page tables (``kv_indptr``,
 ``kv_indices``, ``last_page_len``), ragged query offsets and random Q/K/V values.
