@@ -358,6 +358,46 @@ __device__ __forceinline__ void sched_mfma_interleave() {
 // order), leaving LDS and export counters alone.  n must be a compile-time constant.
 #define BSR_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
+// LDS-DMA accounting of the two pipelined shapes.  Step j of the stream reads K(j+1) and V(j-1);
+// in step j a wave issues one batch of NF loads of K(j + kKAhead), then one of V(j + kVAhead), so
+// the loads of every tile go out kIssueToUseSteps steps before the barrier that publishes it.  At
+// that barrier's wait, the batches younger than the ones needed are those of the steps in between:
+// at most kMaxBatchesInFlight batches may stay in flight.  vmcnt counts every vector-memory
+// instruction of the wave, in issue order; nothing else in the step loop touches vector memory
+// (page ids come from the LDS window, and a window refill waits for its own loads, hence for every
+// older load too), so the limits below count exactly these batches.
+constexpr int kKAhead = 4, kVAhead = 2;
+constexpr int kIssueToUseSteps = 3;
+constexpr int kDmaBatchesPerStep = 2;
+constexpr int kMaxBatchesInFlight = 4;
+static_assert(kKAhead - 1 == kIssueToUseSteps && kVAhead + 1 == kIssueToUseSteps,
+              "step j reads K(j+1) and V(j-1): both issued kIssueToUseSteps steps earlier");
+static_assert(kMaxBatchesInFlight == kDmaBatchesPerStep * (kIssueToUseSteps - 1),
+              "the batches of the steps between a tile's issue and its barrier");
+
+// Batches issued in the steps between the needed ones and step j (steps j - kIssueToUseSteps + 1
+// .. j - 1) that exist in an item of n tiles (the last steps skip loads past the end).
+__device__ __forceinline__ int batches_in_between(int j, int n) {
+  int c = 0;
+#pragma unroll
+  for (int s = 1; s < kIssueToUseSteps; ++s) c += (j - s + kKAhead < n) + (j - s + kVAhead < n);
+  return c;
+}
+
+// Wait until at most nb (0 .. kMaxBatchesInFlight) batches of NF loads are in flight.
+template <int NF>
+__device__ __forceinline__ void wait_dma_batches(int nb) {
+  static_assert(kMaxBatchesInFlight * NF <= 63, "the vmcnt field holds 0 .. 63");
+  static_assert(kMaxBatchesInFlight == 4, "one case per batch count");
+  switch (nb) {
+    case 4: BSR_WAIT_VMCNT(4 * NF); break;
+    case 3: BSR_WAIT_VMCNT(3 * NF); break;
+    case 2: BSR_WAIT_VMCNT(2 * NF); break;
+    case 1: BSR_WAIT_VMCNT(NF); break;
+    default: BSR_WAIT_VMCNT(0); break;
+  }
+}
+
 // The plain double-buffered tile loop of the smaller shapes: compute(k_slot, v_slot, t0) is
 // called once per 64-token tile while the next tile's DMA is in flight.
 template <int D, class PG, typename F>
@@ -681,15 +721,6 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
       const uint64_t addr = uint64_t(uint32_t(page)) * page_bytes + v_add;
       dma_fragments<NF>(reinterpret_cast<const uint16_t*>(addr), v_slot(j) + f0 * FRAG);
     };
-    auto wait_batches = [&](int nb) {  // at most nb batches of NF loads in flight
-      switch (nb) {
-        case 4: BSR_WAIT_VMCNT(4 * NF); break;
-        case 3: BSR_WAIT_VMCNT(3 * NF); break;
-        case 2: BSR_WAIT_VMCNT(2 * NF); break;
-        case 1: BSR_WAIT_VMCNT(NF); break;
-        default: BSR_WAIT_VMCNT(0); break;
-      }
-    };
 
     const float inv_c = 1.f / c;
     float thr = __builtin_fmaf(m, inv_c, kRescaleMargin * inv_c);  // raw-score threshold of a raise
@@ -785,7 +816,8 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
       dma_v(0, v0);
       if (n > 1) dma_v(1, v1);
     }
-    int32_t nk = page_k(4), nv = page_v(2);  // for step 0's loads
+    static_assert(kKAhead == 4 && kVAhead == 2, "the prologue stages K(0..3) and V(0..1)");
+    int32_t nk = page_k(kKAhead), nv = page_v(kVAhead);  // for step 0's loads
     BSR_WAIT_VMCNT(0);
     __syncthreads();  // K(0..3), V(0..1) staged
     qk(k_slot(0), Sa);
@@ -800,21 +832,20 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
     const int n_full = PG == kPageDiv32 ? (kv_end - kv0) / 32 : 0;
     // step j with S(j) in Scur and P(j-1) in pprev; writes S(j+1) to Snext and P(j) to pcur
     auto step = [&](int j, f32x16& Scur, f32x16& Snext, const u32x4 (&pprev)[2], u32x4 (&pcur)[2]) {
-      const bool fast = PG == kPageDiv32 && j >= 1 && j + 5 < n_full;
-      pgn.cover(T(j + 3), T(j + 6) - 1);  // this step's lookups: K(j+5), V(j+3)
-      if (fast) wait_batches(4);
-      else wait_batches((j + 2 < n) + (j < n) + (j + 3 < n) + (j + 1 < n));
+      const bool fast = PG == kPageDiv32 && j >= 1 && j + kKAhead + 1 < n_full;
+      pgn.cover(T(j + kVAhead + 1), T(j + kKAhead + 2) - 1);  // this step's lookups: K(j+5), V(j+3)
+      wait_dma_batches<NF>(fast ? kMaxBatchesInFlight : batches_in_between(j, n));
       __builtin_amdgcn_s_barrier();
       if (fast) {
-        const int32_t nk2 = page_k_fast(j + 5), nv2 = page_v_fast(j + 3);
-        dma_k_fast(j + 4, nk);
-        dma_v_fast(j + 2, nv);
+        const int32_t nk2 = page_k_fast(j + kKAhead + 1), nv2 = page_v_fast(j + kVAhead + 1);
+        dma_k_fast(j + kKAhead, nk);
+        dma_v_fast(j + kVAhead, nv);
         nk = nk2;
         nv = nv2;
       } else {
-        const int32_t nk2 = page_k(j + 5), nv2 = page_v(j + 3);
-        if (j + 4 < n) dma_k(j + 4, nk);
-        if (j + 2 < n) dma_v(j + 2, nv);
+        const int32_t nk2 = page_k(j + kKAhead + 1), nv2 = page_v(j + kVAhead + 1);
+        if (j + kKAhead < n) dma_k(j + kKAhead, nk);
+        if (j + kVAhead < n) dma_v(j + kVAhead, nv);
         nk = nk2;
         nv = nv2;
       }
@@ -1262,15 +1293,6 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
     const uint64_t addr = uint64_t(uint32_t(page)) * page_bytes + v_add;
     dma_fragments<NF>(reinterpret_cast<const uint16_t*>(addr), v_slot(j) + wave * KB * FRAG);
   };
-  auto wait_batches = [&](int nb) {  // at most nb batches of NF loads in flight
-    switch (nb) {
-      case 4: BSR_WAIT_VMCNT(4 * NF); break;
-      case 3: BSR_WAIT_VMCNT(3 * NF); break;
-      case 2: BSR_WAIT_VMCNT(2 * NF); break;
-      case 1: BSR_WAIT_VMCNT(NF); break;
-      default: BSR_WAIT_VMCNT(0); break;
-    }
-  };
 
   // One step's stream: 4 D/16 slots s = 4g + m, each one matrix instruction followed by one
   // chunk of vector work, in a fixed order (scheduling barriers between the slots keep the
@@ -1385,7 +1407,8 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
     dma_v(0, v0);
     if (n > 1) dma_v(1, v1);
   }
-  int32_t nk = page_k(4), nv = page_v(2);  // for step 0's loads
+  static_assert(kKAhead == 4 && kVAhead == 2, "the prologue stages K(0..3) and V(0..1)");
+  int32_t nk = page_k(kKAhead), nv = page_v(kVAhead);  // for step 0's loads
   BSR_WAIT_VMCNT(0);
   __syncthreads();  // K(0..3), V(0..1) staged
   qk(k_slot(0), Sa);
@@ -1395,21 +1418,20 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
   // the nonexistent tile n are all masked, so step n only adds P.V of the last tile.
   const int n_full = PG == kPageDiv32 ? (kv_end - kv0) / 32 : 0;
   auto step = [&](int j, f32x16 (&Scur)[2], f32x16 (&Snext)[2], const u32x4 (&pprev)[2][2], u32x4 (&pcur)[2][2]) {
-    const bool fast = PG == kPageDiv32 && j >= 1 && j + 5 < n_full;
-    pgn.template cover<kThreads2>(T(j + 3), T(j + 6) - 1);  // this step's lookups: K(j+5), V(j+3)
-    if (fast) wait_batches(4);
-    else wait_batches((j + 2 < n) + (j < n) + (j + 3 < n) + (j + 1 < n));
+    const bool fast = PG == kPageDiv32 && j >= 1 && j + kKAhead + 1 < n_full;
+    pgn.template cover<kThreads2>(T(j + kVAhead + 1), T(j + kKAhead + 2) - 1);  // lookups: K(j+5), V(j+3)
+    wait_dma_batches<NF>(fast ? kMaxBatchesInFlight : batches_in_between(j, n));
     __builtin_amdgcn_s_barrier();
     if (fast) {
-      const int32_t nk2 = page_k_fast(j + 5), nv2 = page_v_fast(j + 3);
-      dma_k_fast(j + 4, nk);
-      dma_v_fast(j + 2, nv);
+      const int32_t nk2 = page_k_fast(j + kKAhead + 1), nv2 = page_v_fast(j + kVAhead + 1);
+      dma_k_fast(j + kKAhead, nk);
+      dma_v_fast(j + kVAhead, nv);
       nk = nk2;
       nv = nv2;
     } else {
-      const int32_t nk2 = page_k(j + 5), nv2 = page_v(j + 3);
-      if (j + 4 < n) dma_k(j + 4, nk);
-      if (j + 2 < n) dma_v(j + 2, nv);
+      const int32_t nk2 = page_k(j + kKAhead + 1), nv2 = page_v(j + kVAhead + 1);
+      if (j + kKAhead < n) dma_k(j + kKAhead, nk);
+      if (j + kVAhead < n) dma_v(j + kVAhead, nv);
       nk = nk2;
       nv = nv2;
     }

@@ -1,0 +1,111 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration bench.py times.
+
+* Ragged causal prefill (batch 16, q_len = kv_len U[256, 4096], page size 16): every row of the
+  three longest requests, which run through the middle of long 128-row work items.
+* Page size 1 over a 2^20-row pool: the batch-64 decode on all 64 requests, and the batch-8 x
+  2048 causal prefill on all 8 sequences (bitwise equal to the contiguous layout everywhere;
+  against the oracle on every decode request and on sampled prefill rows).
+* Work items longer than the kernels' page-id window (2048 pages, refilled mid-item): a
+  5,000-token causal request at page size 1 for every tile shape of the bf16 prefill kernels.
+
+Tolerances: bf16 inputs with fp32 accumulation -> O max-abs 2e-2, LSE max-abs 1e-2.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import workloads as I
+from tests.gpu_helpers import compare, log, make_plan, oracle, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from block_sparse_paged_bsr_amd import api
+
+    api.version()  # loads the library or raises
+
+
+@pytest.fixture(scope="module")
+def ragged_prefill_run():
+    from block_sparse_paged_bsr_amd import api
+
+    b = I.ragged_prefill_bf16(seed=0)
+    C_ = api.query_num_workers("prefill", 32, 8, 128)
+    log(f"[ragged prefill full] lens={b.kv_lens.tolist()} workers={C_}")
+    p = make_plan(b, num_workers=C_)
+    assert p.export()["tile_q"] == 128
+    o, l, _ = run_gpu(b, p)
+    return b, o, l
+
+
+@pytest.mark.parametrize("rank", [0, 1, 2])
+def test_ragged_prefill_longest_requests_every_row(ragged_prefill_run, rank):
+    b, o, l = ragged_prefill_run
+    i = int(np.argsort(-b.kv_lens, kind="stable")[rank])
+    log(f"    request {i}: {int(b.kv_lens[i])} queries x 32 heads, every row")
+    ro, rl = oracle(b, requests=[i])
+    compare(o, l, ro, rl, "bf16", f"ragged prefill request {i} (all rows)")
+
+
+def test_vector_sparse_decode_all_requests():
+    """The batch-64 decode at page size 1 in a 2^20-row pool vs its contiguous twin."""
+    from block_sparse_paged_bsr_amd import api
+
+    lens = I.decode_lengths(0)
+    a, c = I.vector_sparse_pair(0, lens, pool_rows=1 << 20)
+    log(f"[vector sparse decode] batch {len(lens)}, tokens={int(lens.sum())}")
+    C_ = api.query_num_workers("decode", 32, 8, 128)
+    oa, la, _ = run_gpu(a, make_plan(a, num_workers=C_))
+    oc, lc, _ = run_gpu(c, make_plan(c, num_workers=C_))
+    assert np.array_equal(oa, oc) and np.array_equal(la, lc)
+    ro, rl = oracle(c)
+    compare(oa, la, ro, rl, "bf16", "vector-sparse decode, all 64 requests")
+
+
+def test_vector_sparse_prefill_all_sequences():
+    """Batch 8 x 2048 causal prefill at page size 1 vs contiguous: bitwise equal on every row;
+    oracle on sampled rows of all eight sequences (the first, the last, 32-row tile edges)."""
+    from block_sparse_paged_bsr_amd import api
+
+    lens = [2048] * 8
+    a, c = I.vector_sparse_pair(1, lens, lens, pool_rows=1 << 20, causal=True)
+    log("[vector sparse prefill] 8 x 2048 causal")
+    C_ = api.query_num_workers("prefill", 32, 8, 128)
+    oa, la, _ = run_gpu(a, make_plan(a, num_workers=C_))
+    oc, lc, _ = run_gpu(c, make_plan(c, num_workers=C_))
+    assert np.array_equal(oa, oc) and np.array_equal(la, lc)
+    rng = np.random.default_rng(4)
+    sub = {i: np.unique(np.concatenate([[0, 31, 32, 1023, 1024, 2047], rng.integers(0, 2048, 26)]))
+           for i in range(8)}
+    ro, rl = oracle(c, query_subset=sub)
+    compare(oa, la, ro, rl, "bf16", "vector-sparse prefill, 8 sequences (sampled rows)")
+
+
+@pytest.mark.parametrize("tile_q,soft_cap,shape", [
+    (128, 0.0, "128-row kernel"),
+    (128, 30.0, "pipelined 4-wave kernel (soft cap)"),
+    (64, 0.0, "two 32-row blocks, tokens split"),
+    (32, 0.0, "16-row blocks"),
+])
+def test_items_longer_than_the_page_window(tile_q, soft_cap, shape):
+    """One causal request of 5,000 tokens at page size 1 on a single worker: the later tiles'
+    items hold up to 5,000 pages, so the 2048-entry page-id window is refilled inside an item."""
+    L = 5000
+    b = I.make_paged_batch(11, [L], [L], page_size=1, num_qo_heads=8, num_kv_heads=2, head_dim=128, causal=True,
+                           num_pages=L + 300)
+    log(f"[page window refill] {shape}: tile_q={tile_q} soft_cap={soft_cap}, {L} tokens, 1 worker")
+    p = make_plan(b, num_workers=1, tile_q=tile_q, soft_cap=soft_cap)
+    e = p.export()
+    assert int(e["items"][:, 5].max()) > 2048
+    o, l, _ = run_gpu(b, p)
+    rng = np.random.default_rng(5)
+    sub = {0: np.unique(np.concatenate([[0, 2047, 2048, 2049, L - 1], rng.integers(0, L, 200)]))}
+    ro, rl = oracle(b, query_subset=sub, soft_cap=soft_cap)
+    compare(o, l, ro, rl, "bf16", f"page window refill ({shape})")

@@ -139,36 +139,6 @@ def test_prefill_bf16_ragged_full_sampled():
     compare(o, l, ro, rl, "bf16", "prefill ragged full (sampled rows)")
 
 
-def test_vector_sparse_decode_paged_equals_contiguous():
-    """Page size 1 in a 2^20-row pool vs the same contents contiguous: bitwise equal."""
-    from block_sparse_paged_bsr_amd import api
-
-    lens = I.decode_lengths(0)[:16]
-    a, c = I.vector_sparse_pair(0, lens, pool_rows=1 << 20)
-    log(f"[vector_sparse_decode] tokens={int(lens.sum())}")
-    C_ = api.query_num_workers("decode", 32, 8, 128)
-    oa, la, _ = run_gpu(a, make_plan(a, num_workers=C_))
-    oc, lc, _ = run_gpu(c, make_plan(c, num_workers=C_))
-    assert np.array_equal(oa, oc) and np.array_equal(la, lc)
-    ro, rl = oracle(c)
-    compare(oa, la, ro, rl, "bf16", "vector-sparse decode")
-
-
-def test_vector_sparse_prefill_paged_equals_contiguous():
-    from block_sparse_paged_bsr_amd import api
-
-    lens = [2048, 2048]
-    a, c = I.vector_sparse_pair(1, lens, lens, pool_rows=1 << 20, causal=True)
-    log("[vector_sparse_prefill] 2 x 2048 causal")
-    C_ = api.query_num_workers("prefill", 32, 8, 128)
-    oa, la, _ = run_gpu(a, make_plan(a, num_workers=C_))
-    oc, lc, _ = run_gpu(c, make_plan(c, num_workers=C_))
-    assert np.array_equal(oa, oc) and np.array_equal(la, lc)
-    sub = {i: np.array([0, 5, 700, 2047]) for i in range(2)}
-    ro, rl = oracle(c, query_subset=sub)
-    compare(oa, la, ro, rl, "bf16", "vector-sparse prefill")
-
-
 def test_merge_state_kernel():
     import torch
     from block_sparse_paged_bsr_amd import api

@@ -1,0 +1,304 @@
+"""Host model of the bf16 prefill kernels' page-window lookups and LDS-DMA wait accounting.
+
+The prefill kernels (block_sparse_paged_bsr_amd/csrc/kernels/attn_prefill_bf16.hip) stage a
+window of up to kPageWindow page ids of the request's page list in LDS, look token pages up
+there, and gather K/V rows into LDS rings with asynchronous DMA loads whose completion they wait
+for with hand-counted `vmcnt` limits.  A page id read from outside the filled window, or a wait
+that lets a tile's loads still be in flight when a barrier publishes it, would turn into a wild
+address or a stale tile on the GPU.  This module replays, on the CPU, the sequence of window
+fills, page lookups (general and fast forms), DMA issues, waits, barriers and ring reads that
+each kernel shape performs for the work items of a plan, and asserts:
+
+* every window lookup index lies in [0, filled entries) for every token a lane loads (page_no
+  is monotone in the token, so a tile's first and last token bound all of its lanes);
+* the fast (page size divides 32) lookup indices and in-page row offsets equal the general ones;
+* every DMA targets a tile that exists, into a ring slot whose previous tile was last read
+  before the barrier that precedes the issue, with no other load in flight into that slot;
+* at every barrier the tiles the following stream reads have completed (loads of one wave
+  complete in issue order, so "at most n batches in flight" completes all but the n youngest);
+* the batches per step and the wait limits agree with the kernel's compile-time constants
+  (kDmaBatchesPerStep, kMaxBatchesInFlight).
+
+The plans come from the library's own planner (bsr_plan_export), so the model runs the work
+items the kernels run.
+"""
+import functools
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_sparse_paged_bsr_amd import _lib
+from block_sparse_paged_bsr_amd import api
+import workloads as I
+from tests.conftest import ROOT
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libbsr_attn.so not built")
+
+SRC = os.path.join(ROOT, "block_sparse_paged_bsr_amd", "csrc", "kernels", "attn_prefill_bf16.hip")
+
+
+def _kernel_constant(name):
+    m = re.search(r"constexpr int %s = (\d+)[;,]" % name, open(SRC).read())
+    assert m, name
+    return int(m.group(1))
+
+
+PAGE_WINDOW = _kernel_constant("kPageWindow")
+TILE_KV = _kernel_constant("kTileKV")
+BATCHES_PER_STEP = _kernel_constant("kDmaBatchesPerStep")
+MAX_IN_FLIGHT = _kernel_constant("kMaxBatchesInFlight")
+K_AHEAD = _kernel_constant("kKAhead")
+
+
+def _page_no(t, kv_end, P):
+    return np.minimum(t, kv_end - 1) // P
+
+
+def window_states(kv_end, P, covers, fill_short=0):
+    """Paging::cover over a sequence of (lo, hi) token ranges: the window's first page and its
+    filled length after each call, and the number of refills after the first fill.
+    (fill_short plants a mistake: a fill that stops that many entries early.)"""
+    base, cnt, fills = -PAGE_WINDOW, 0, 0
+    last = (kv_end - 1) // P
+    bases, cnts = [], []
+    for lo, hi in covers:
+        plo, phi = min(lo, kv_end - 1) // P, min(hi, kv_end - 1) // P
+        if not (plo >= base and phi < base + PAGE_WINDOW):
+            base, cnt, fills = plo, min(PAGE_WINDOW, last - plo + 1) - fill_short, fills + 1
+            assert phi - plo < cnt, "a cover() range wider than the window"
+        bases.append(base)
+        cnts.append(cnt)
+    return np.array(bases), np.array(cnts), fills - 1
+
+
+def check_lookups(first_tok, base, cnt, kv_end, P, span):
+    """Table reads for tokens first_tok + 0 .. span-1 under windows (base, cnt), arrays over
+    steps: the first and last token bound the index of every lane."""
+    lo = _page_no(first_tok, kv_end, P) - base
+    hi = _page_no(first_tok + span - 1, kv_end, P) - base
+    assert lo.min() >= 0 and (hi - cnt).max() < 0, "a page id read outside the filled window"
+
+
+@functools.lru_cache(maxsize=None)
+def check_rings(n, n_full):
+    return replay_rings(n, n_full)
+
+
+def replay_rings(n, n_full, loose=0):
+    """The DMA issue / wait / barrier / read sequence of one item of n 32-token tiles (n_full
+    of them full; fast steps exist only where it is > 0).  Returns the number of fast steps.
+    (loose plants a mistake: every wait lets that many more batches stay in flight.)"""
+    queue = []  # batches of this wave not yet known complete, in issue order: (ring, tile)
+    holds = {"K": {}, "V": {}}
+    inflight = {"K": {}, "V": {}}
+    last_read = {"K": {}, "V": {}}
+    epoch = [0]
+    issued = [0]
+
+    def issue(ring, tile):
+        assert 0 <= tile < n, f"DMA of nonexistent tile {ring}({tile})"
+        slot = tile % 4
+        assert last_read[ring].get(slot, -1) < epoch[0], f"{ring}({tile}) overwrites a slot read this step"
+        assert slot not in inflight[ring], f"two loads in flight into {ring} slot {slot}"
+        inflight[ring][slot] = tile
+        queue.append((ring, tile))
+        issued[0] += 1
+
+    def wait(n_allowed):
+        done = queue[: len(queue) - n_allowed] if n_allowed else list(queue)
+        for ring, tile in done:
+            assert inflight[ring].pop(tile % 4) == tile
+            holds[ring][tile % 4] = tile
+        del queue[: len(done)]
+
+    def barrier():
+        epoch[0] += 1
+        issued[0] = 0
+
+    def read(ring, tile, must_hold=True):
+        slot = tile % 4
+        assert slot not in inflight[ring], f"read of {ring} slot {slot} while a load fills it"
+        if must_hold:
+            assert holds[ring].get(slot) == tile, f"{ring}({tile}) not staged when read"
+        last_read[ring][slot] = epoch[0]
+
+    # prologue: K(0..3), V(0..1), then a full wait and a barrier; the first scores read K(0)
+    for t in range(4):
+        if t < n:
+            issue("K", t)
+    for t in range(2):
+        if t < n:
+            issue("V", t)
+    wait(0)
+    barrier()
+    read("K", 0)
+    fast_steps = 0
+    for j in range(n + 1):
+        fast = j >= 1 and j + 5 < n_full
+        nb = MAX_IN_FLIGHT if fast else (j + 2 < n) + (j < n) + (j + 3 < n) + (j + 1 < n)
+        assert nb <= MAX_IN_FLIGHT
+        wait(nb + loose)
+        barrier()
+        if fast:
+            fast_steps += 1
+            issue("K", j + 4)
+            issue("V", j + 2)
+            assert issued[0] == BATCHES_PER_STEP
+        else:
+            if j + 4 < n:
+                issue("K", j + 4)
+            if j + 2 < n:
+                issue("V", j + 2)
+            assert issued[0] <= BATCHES_PER_STEP
+        # the stream: scores of tile j+1 (masked out entirely when it does not exist), P.V of j-1
+        read("K", j + 1, must_hold=j + 1 < n)
+        read("V", 0 if j == 0 else j - 1)
+    wait(0)
+    return fast_steps
+
+
+def model_pipelined(kv0, kv_end, P, div32, rings=True):
+    """prefill_item128 and the pipelined prefill_item32: one 32-token tile per step, K loaded
+    four tiles ahead and V two, lookups of K(j+5) and V(j+3) after cover(T(j+3), T(j+6) - 1).
+    Every lane of either shape loads one of a tile's 32 tokens.  Returns (refills, fast steps)."""
+    n = (kv_end - kv0 + 31) // 32
+    T = lambda j: kv0 + 32 * np.asarray(j)  # noqa: E731
+    js = np.arange(n + 1)
+    covers = [(kv0, kv0 + 6 * 32 - 1)] + [(kv0 + 32 * (j + 3), kv0 + 32 * (j + 6) - 1) for j in range(n + 1)]
+    base, cnt, refills = window_states(kv_end, P, covers)
+    # prologue lookups K(0..4), V(0..2) under the first window
+    check_lookups(T(np.arange(5)), base[0], cnt[0], kv_end, P, 32)
+    # step j looks up K(j+5) and V(j+3) under the window after its cover()
+    check_lookups(T(js + 5), base[1:], cnt[1:], kv_end, P, 32)
+    check_lookups(T(js + 3), base[1:], cnt[1:], kv_end, P, 32)
+    n_full = (kv_end - kv0) // 32 if div32 else 0
+    fast = (js >= 1) & (js + 5 < n_full)
+    if div32 and fast.any():
+        # fast lookups: table[(kv0 + tok) / P + (j + ahead) (32 / P) - base], every token offset
+        jf, tok = js[fast][:, None], np.arange(32)[None, :]
+        bf, cf = base[1:][fast][:, None], cnt[1:][fast][:, None]
+        for ahead in (5, 3):
+            idx = (kv0 + tok) // P + (jf + ahead) * (32 // P) - bf
+            want = _page_no(kv0 + 32 * (jf + ahead) + tok, kv_end, P) - bf
+            assert np.array_equal(idx, want) and idx.min() >= 0 and (idx - cf).max() < 0
+        # and the row offset inside the page is the same in every tile
+        assert np.array_equal((kv0 + 32 * jf + tok) % P, np.broadcast_to((kv0 + tok) % P, (len(jf), 32)))
+    fast_steps = check_rings(n, n_full) if rings else int(fast.sum())
+    return refills, fast_steps
+
+
+def model_tile_loop(kv0, kv_end, P):
+    """tile_loop of the smaller shapes: 64-token tiles in two stages; the four waves' lanes
+    load tokens 0 .. 63 of a tile; every wait drains all loads.  Returns the refills."""
+    ntiles = (kv_end - kv0 + TILE_KV - 1) // TILE_KV
+    tis = np.arange(0, ntiles, 2)
+    covers = [(kv0, kv0 + 2 * TILE_KV - 1)] + [(kv0 + (ti + 2) * TILE_KV, kv0 + (ti + 4) * TILE_KV - 1)
+                                               for ti in tis]
+    base, cnt, refills = window_states(kv_end, P, covers)
+    check_lookups(np.array([kv0, kv0 + TILE_KV]), base[0], cnt[0], kv_end, P, TILE_KV)
+    for ahead in (2, 3):
+        check_lookups(kv0 + (tis + ahead) * TILE_KV, base[1:], cnt[1:], kv_end, P, TILE_KV)
+    return refills
+
+
+def _tables(kv_lens, P, seed, pool=None):
+    """BSR arrays for requests of the given lengths, pages drawn from a random permutation of
+    the pool (the layout of the workloads)."""
+    kv_lens = np.asarray(kv_lens, dtype=np.int64)
+    need = int(((kv_lens + P - 1) // P).sum())
+    perm = np.random.default_rng(seed).permutation(pool or need)
+    return I.page_table_from_lengths(kv_lens, P, perm)
+
+
+def _run_plan(kv_lens, qo_indptr, P, C, causal, tile_q=0, shapes=("pipelined",), Hq=32, Hk=8, pool=None, seed=0,
+              rings=True):
+    ip, ix, last = _tables(kv_lens, P, seed, pool)
+    p = api.Plan(ip, ix, last, num_pages=pool or max(len(ix), 1), num_qo_heads=Hq, num_kv_heads=Hk, head_dim=128,
+                 page_size=P, qo_indptr=qo_indptr, causal=causal, num_workers=C, tile_q=tile_q)
+    e = p.export()
+    div32 = P <= 32 and (P & (P - 1)) == 0
+    refills = fast = 0
+    for it in e["items"]:
+        kv_start, kv_len = int(it[4]), int(it[5])
+        if "pipelined" in shapes:
+            r, f = model_pipelined(kv_start, kv_start + kv_len, P, div32, rings)
+            refills, fast = refills + r, fast + f
+        if "loop" in shapes:
+            refills += model_tile_loop(kv_start, kv_start + kv_len, P)
+    return {"items": len(e["items"]), "refills": refills, "fast_steps": fast, "tile_q": int(e["tile_q"])}
+
+
+def _qo(lens):
+    return np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+
+
+def test_constants_agree_with_the_kernel():
+    assert BATCHES_PER_STEP == 2 and MAX_IN_FLIGHT == 2 * BATCHES_PER_STEP and K_AHEAD == 4
+
+
+@pytest.mark.parametrize("n", range(1, 80))
+def test_rings_every_short_item(n):
+    """Every item length up to 80 tiles, with and without fast steps (n_full = n or n - 1)."""
+    check_rings(n, 0)
+    check_rings(n, n)
+    check_rings(n, n - 1)
+
+
+def test_ragged_causal_prefill_plan():
+    """The batch-16 ragged causal prefill (page size 16) at 64 workers."""
+    lens = I.prefill_lengths(0)
+    r = _run_plan(lens, _qo(lens), 16, 64, True, shapes=("pipelined", "loop"))
+    assert r["tile_q"] == 128 and r["fast_steps"] > 0
+
+
+def test_vector_sparse_prefill_plan():
+    """Batch 8 x 2048 causal prefill at page size 1 in a 2^20-row pool: items of up to 2048
+    pages, exactly one full window."""
+    lens = [2048] * 8
+    r = _run_plan(lens, _qo(lens), 1, 64, True, shapes=("pipelined", "loop"), pool=1 << 20)
+    assert r["refills"] == 0
+
+
+def test_shared_prefix_level_plans():
+    """The shared-prefix level of the batch-64 / 32,768-token shape: one block row of all 64
+    queries, non-causal; chunked at 64 workers and as one 2048-page item per tile."""
+    for C in (64, 1):
+        r = _run_plan([32768], np.array([0, 64], dtype=np.int32), 16, C, False, shapes=("pipelined", "loop"))
+        assert r["refills"] == 0
+
+
+@pytest.mark.parametrize("P,L", [(1, 5000), (1, 2049), (16, 40000), (8, 17000), (12, 30000), (32, 70000)])
+def test_items_longer_than_the_window(P, L):
+    """Single causal requests whose work items span more than kPageWindow pages (mid-item
+    window refills), for the pipelined shapes and the plain loop.  The ring accounting depends
+    only on an item's tile count and is replayed in full above and for the shorter items here."""
+    r = _run_plan([L], _qo([L]), P, 1, True, tile_q=128, shapes=("pipelined",), Hq=4, Hk=1, rings=L <= 6000)
+    assert r["refills"] > 0
+    for tq in (32, 64):
+        r = _run_plan([L], _qo([L]), P, 1, True, tile_q=tq, shapes=("loop",), Hq=4, Hk=1)
+        assert r["refills"] > 0
+
+
+def test_model_catches_planted_mistakes():
+    """The model is not vacuous: a wait one batch too loose, and a window fill one entry short,
+    both fail it."""
+    with pytest.raises(AssertionError, match="not staged|while a load fills it"):
+        replay_rings(20, 20, loose=1)
+    with pytest.raises(AssertionError, match="outside the filled window"):
+        kv_end = 3000
+        n = (kv_end + 31) // 32
+        covers = [(0, 191)] + [(32 * (j + 3), 32 * (j + 6) - 1) for j in range(n + 1)]
+        base, cnt, _ = window_states(kv_end, 1, covers, fill_short=1)
+        js = np.arange(n + 1)
+        check_lookups(32 * (js + 5), base[1:], cnt[1:], kv_end, 1, 32)
+
+
+@pytest.mark.parametrize("tile_q", [128, 64, 32])
+def test_page_window_refill_gpu_case(tile_q):
+    """The exact plans of the GPU test of items longer than the window (5,000 tokens at page
+    size 1, 8/2 heads, one worker), replayed here before they run on the GPU."""
+    r = _run_plan([5000], _qo([5000]), 1, 1, True, tile_q=tile_q, shapes=("pipelined", "loop"), Hq=8, Hk=2,
+                  pool=5300, seed=11)
+    assert r["refills"] > 0

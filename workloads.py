@@ -260,6 +260,11 @@ def decode_lengths(seed: int, batch: int = 64, lo: int = 512, hi: int = 8192) ->
     return np.random.default_rng(seed).integers(lo, hi, size=batch, endpoint=True).astype(np.int32)
 
 
+def prefill_lengths(seed: int, batch: int = 16, lo: int = 256, hi: int = 4096) -> np.ndarray:
+    """Query (= KV) lengths of the ragged prefill, uniform in [lo, hi] (inclusive)."""
+    return np.random.default_rng(seed).integers(lo, hi, size=batch, endpoint=True).astype(np.int32)
+
+
 def batched_decode_bf16(
     seed: int = 0,
     batch: int = 64,
@@ -296,7 +301,7 @@ def ragged_prefill_bf16(
     qo_lens=None,
 ) -> PagedBatch:
     """Ragged causal prefill: q_len = kv_len uniform in [256, 4096], page size 16."""
-    lens = np.random.default_rng(seed).integers(lo, hi, size=batch, endpoint=True).astype(np.int32)
+    lens = prefill_lengths(seed, batch, lo, hi)
     ql = lens if qo_lens is None else np.asarray(qo_lens, dtype=np.int32)
     rng = np.random.default_rng(seed + 2000)
     return make_paged_batch(
