@@ -392,8 +392,8 @@ int bsr_query_num_workers(int32_t device, int32_t kind, int32_t num_qo_heads, in
   const int g = num_qo_heads / num_kv_heads;
   int per_cu = 1, per_worker = num_kv_heads;
   if (kind == 0 && decode_bf16_supported(head_dim, g, 128)) {
-    per_cu = decode_bf16_blocks_per_cu(head_dim, g);
-    per_worker = num_kv_heads * decode_bf16_waves_per_kv_head(g);
+    per_cu = decode_bf16_blocks_per_cu(head_dim, num_kv_heads);
+    per_worker = decode_bf16_blocks_per_worker(num_kv_heads);
   } else if (head_dim == 64 || head_dim == 128) {
     per_cu = prefill_bf16_blocks_per_cu(head_dim);
   }

@@ -44,18 +44,32 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true))};
 }
 
+// A workgroup serves up to kDecodeWaves KV heads of one worker, one wave per head: its waves run
+// the same work items over the same tokens, so together they read whole token rows (all KV heads
+// of a token are adjacent, 2 KB at 8 heads x 128 bf16) and whole pages at about the same time,
+// instead of one head's 256-byte slice of each row from a workgroup of its own.
+constexpr int kDecodeWaves = 8;
+
+template <int D>
+constexpr int decode_vs_bytes() { return 16 * (D + 8) * 2; }  // one wave's V staging tile
+
 template <int D, bool CAP, bool KV8>
-__global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
+__global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(RunArgs a) {
   constexpr int KB = D / 32;  // k-blocks of the score product
   constexpr int DB = D / 16;  // d-blocks of the output product
   constexpr int VS = D + 8;   // LDS row stride (elements); 16-byte aligned rows
   constexpr int ES = KV8 ? 1 : 2;                // bytes per K/V element
   constexpr int NL = KV8 ? D / 64 : D / 32;      // 16-byte loads per row and lane (64 j-apart bytes)
   constexpr int PD = KV8 ? 2 : 1;  // 16-token halves per step (E4M3 rows are half as long)
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[16 * VS];
+  extern __shared__ __attribute__((aligned(16))) uint16_t decode_lds[];
 
-  const int w = blockIdx.x, hk = blockIdx.y;
-  const int lane = threadIdx.x, n = lane & 15, j = lane >> 4;
+  const int wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
+  const int w = blockIdx.x, hk = blockIdx.y * waves + wave;
+  if (hk >= a.Hk) return;  // (no workgroup barrier below: every wave runs on its own)
+  // the wave's private V tile; LDS operations of one wave complete in order, so staging and the
+  // transposing reads need no barrier
+  uint16_t* Vs = decode_lds + wave * (16 * VS);
+  const int lane = threadIdx.x & 63, n = lane & 15, j = lane >> 4;
   const int g = a.g;
   const float qk_scale = KV8 ? a.sm_scale * a.k_scale : a.sm_scale;  // K's scale joins the score scale
   const float c = CAP ? qk_scale / a.soft_cap : qk_scale * kLog2e;
@@ -125,8 +139,8 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
         S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka), qb[kb], S, 0, 0, 0);
       }
 
-      // stage V rows (token n) as bf16 for the transposing read below
-      __syncthreads();
+      // stage V rows (token n) as bf16 for the transposing read below (the previous step's
+      // reads of the tile were issued before these writes and complete first)
 #pragma unroll
       for (int l = 0; l < NL; ++l) {
         if constexpr (KV8) {
@@ -139,7 +153,6 @@ __global__ __launch_bounds__(64) void attn_decode_bf16_kernel(RunArgs a) {
           *reinterpret_cast<u32x4*>(Vs + n * VS + 32 * l + 8 * j) = vr[l];
         }
       }
-      __syncthreads();
 
       float s[4];
       float mt = kNegInf;
@@ -256,28 +269,40 @@ bool decode_bf16_supported(int d, int g, int Tq) {
   return (d == 64 || d == 128) && g >= 1 && g <= 16 && g <= Tq;
 }
 
-int decode_bf16_waves_per_kv_head(int) { return 1; }
+int decode_bf16_waves_per_block(int Hk) { return Hk < kDecodeWaves ? Hk : kDecodeWaves; }
 
-int decode_bf16_blocks_per_cu(int d, int) {
+int decode_bf16_blocks_per_worker(int Hk) {
+  const int wv = decode_bf16_waves_per_block(Hk);
+  return (Hk + wv - 1) / wv;
+}
+
+int decode_bf16_blocks_per_cu(int d, int Hk) {
+  const int wv = decode_bf16_waves_per_block(Hk);
   int nb = 1;
   hipError_t e = hipErrorInvalidValue;
-  if (d == 64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<64, false, false>, 64, 0);
-  if (d == 128) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<128, false, false>, 64, 0);
+  if (d == 64)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<64, false, false>, 64 * wv,
+                                                     wv * decode_vs_bytes<64>());
+  if (d == 128)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<128, false, false>, 64 * wv,
+                                                     wv * decode_vs_bytes<128>());
   return (e == hipSuccess && nb > 0) ? nb : 1;
 }
 
 template <int D, bool KV8>
-static void launch_cap(const RunArgs& a, dim3 grid, hipStream_t s) {
-  if (a.soft_cap > 0.f) hipLaunchKernelGGL((attn_decode_bf16_kernel<D, true, KV8>), grid, dim3(64), 0, s, a);
-  else hipLaunchKernelGGL((attn_decode_bf16_kernel<D, false, KV8>), grid, dim3(64), 0, s, a);
+static void launch_cap(const RunArgs& a, dim3 grid, int waves, hipStream_t s) {
+  const size_t lds = size_t(waves) * decode_vs_bytes<D>();
+  if (a.soft_cap > 0.f) hipLaunchKernelGGL((attn_decode_bf16_kernel<D, true, KV8>), grid, dim3(64 * waves), lds, s, a);
+  else hipLaunchKernelGGL((attn_decode_bf16_kernel<D, false, KV8>), grid, dim3(64 * waves), lds, s, a);
 }
 
 hipError_t launch_decode_bf16(const RunArgs& a, bool kv_e4m3, hipStream_t s) {
-  const dim3 grid(a.C, a.Hk);
-  if (a.d == 64 && kv_e4m3) launch_cap<64, true>(a, grid, s);
-  else if (a.d == 64) launch_cap<64, false>(a, grid, s);
-  else if (a.d == 128 && kv_e4m3) launch_cap<128, true>(a, grid, s);
-  else if (a.d == 128) launch_cap<128, false>(a, grid, s);
+  const int waves = decode_bf16_waves_per_block(a.Hk);
+  const dim3 grid(a.C, decode_bf16_blocks_per_worker(a.Hk));
+  if (a.d == 64 && kv_e4m3) launch_cap<64, true>(a, grid, waves, s);
+  else if (a.d == 64) launch_cap<64, false>(a, grid, waves, s);
+  else if (a.d == 128 && kv_e4m3) launch_cap<128, true>(a, grid, waves, s);
+  else if (a.d == 128) launch_cap<128, false>(a, grid, waves, s);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

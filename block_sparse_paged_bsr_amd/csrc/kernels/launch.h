@@ -20,8 +20,10 @@ int prefill_bf16_blocks_per_cu(int d);
 // bytes with per-tensor scales (RunArgs::k_scale, v_scale); Q and O stay bf16.
 bool decode_bf16_supported(int d, int g, int Tq);
 hipError_t launch_decode_bf16(const RunArgs& a, bool kv_e4m3, hipStream_t s);
-int decode_bf16_blocks_per_cu(int d, int g);
-int decode_bf16_waves_per_kv_head(int g);
+// One workgroup per worker holds min(H_kv, 8) waves, one per KV head; H_kv above 8 takes several
+// workgroups per worker.
+int decode_bf16_blocks_per_cu(int d, int Hk);
+int decode_bf16_blocks_per_worker(int Hk);
 
 // Reduction-map merge of partial states into final outputs (dtype of O).
 hipError_t launch_merge(const RunArgs& a, int dtype, hipStream_t s);
