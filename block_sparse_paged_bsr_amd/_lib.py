@@ -91,6 +91,7 @@ EXPORTED = [
     "bsr_plan_export",
     "bsr_run_decode",
     "bsr_run_decode_e4m3",
+    "bsr_run_decode_scratch",
     "bsr_run_prefill",
     "bsr_run_prefill_masked",
     "bsr_merge_state",
@@ -115,6 +116,13 @@ def lib():
             f"{LIB_PATH} is missing: build it with `python -m block_sparse_paged_bsr_amd.build` "
             "(there is no fallback path)"
         )
+    # torch's HIP runtime and the one the library links carry the same soname: load torch first,
+    # so the process holds exactly one runtime (the library binds to the already-loaded copy);
+    # loading the library first leaves torch's device calls on a second runtime without devices
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = C.CDLL(LIB_PATH)
     vp = C.c_void_p
     L.bsr_plan_create.argtypes = [C.POINTER(PlanDesc), C.POINTER(vp)]
@@ -132,6 +140,8 @@ def lib():
     L.bsr_run_decode.restype = C.c_int
     L.bsr_run_prefill.argtypes = run_args
     L.bsr_run_prefill.restype = C.c_int
+    L.bsr_run_decode_scratch.argtypes = [vp, vp, vp, vp, vp, C.POINTER(C.c_float), C.c_int32, C.c_float, vp]
+    L.bsr_run_decode_scratch.restype = C.c_int
     L.bsr_run_decode_e4m3.argtypes = [vp, vp, vp, vp, vp, vp, C.POINTER(C.c_float), C.c_float, C.c_float,
                                       C.c_float, vp]
     L.bsr_run_decode_e4m3.restype = C.c_int
