@@ -238,6 +238,19 @@ def run_decode(p: Plan, ws, q, k_cache, v_cache, o=None, lse=None, sm_scale=None
     return _run(lib().bsr_run_decode, p, ws, q, k_cache, v_cache, o, lse, sm_scale, stream)
 
 
+def run_decode_scratch(p: Plan, q, k_cache, v_cache, o, lse, sm_scale=None, stream=None):
+    """bsr_run_decode_scratch: bsr_run_decode on the library's static scratch (no workspace, no
+    allocation in the call; o and lse are the caller's)."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(p.head_dim)
+    _check_run_args(p, q, k_cache, v_cache, o, lse)
+    check(lib().bsr_run_decode_scratch(
+        p.handle, C.c_void_p(q.data_ptr()), C.c_void_p(k_cache.data_ptr()), C.c_void_p(v_cache.data_ptr()),
+        C.c_void_p(o.data_ptr()), C.cast(C.c_void_p(lse.data_ptr()), C.POINTER(C.c_float)), _dtype_code(q),
+        float(sm_scale), _stream(stream)))
+    return o, lse
+
+
 def run_prefill(p: Plan, ws, q, k_cache, v_cache, o=None, lse=None, sm_scale=None, stream=None):
     """bsr_run_prefill: ragged (causal per plan) queries; returns (O, LSE)."""
     return _run(lib().bsr_run_prefill, p, ws, q, k_cache, v_cache, o, lse, sm_scale, stream)

@@ -118,14 +118,16 @@ RunArgs make_args(const bsr_plan* p, const void* ws) {
 
 bool positive_finite(float x) { return x > 0.f && x != __builtin_huge_valf(); }
 
-// kv_e4m3: K and V are E4M3 bytes with per-tensor scales (decode only; Q and O are bf16)
+// kv_e4m3: K and V are E4M3 bytes with per-tensor scales (decode only; Q and O are bf16).
+// ws_ready: the caller has just copied the plan's metadata into ws (the static-scratch entry).
 int run_common(const bsr_plan* p, const void* ws, const void* q, const void* k, const void* v,
                void* o, float* lse, int32_t dtype, float sm_scale, void* stream, bool decode_call,
                bool kv_e4m3 = false, float k_scale = 1.f, float v_scale = 1.f,
-               const uint8_t* mask = nullptr) {
+               const uint8_t* mask = nullptr, bool ws_ready = false) {
   if (!p) return invalid("plan is NULL");
   if (!ws) return invalid("workspace is NULL");
-  if (ws != p->uploaded_ws) return invalid("workspace was not uploaded for this plan (call bsr_plan_upload first)");
+  if (!ws_ready && ws != p->uploaded_ws)
+    return invalid("workspace was not uploaded for this plan (call bsr_plan_upload first)");
   if (dtype != BSR_DTYPE_F32 && dtype != BSR_DTYPE_BF16) return invalid("unknown dtype");
   if (decode_call && !p->decode)
     return invalid("bsr_run_decode needs a plan with one query per request (qo_indptr == NULL); use bsr_run_prefill");
@@ -182,6 +184,33 @@ int run_common(const bsr_plan* p, const void* ws, const void* q, const void* k, 
     timing_stop(t1, s, 1);
     if (e != hipSuccess) return hip_fail("merge kernel launch", e);
   }
+  return BSR_OK;
+}
+
+// ---- the static scratch of bsr_run_decode_scratch ----
+// For callers that cannot allocate device memory: a file-scope device array that every GPU the
+// library runs on holds from module load until the process ends.  Host code never passes its
+// name to a kernel or a copy: the array's device address on the current GPU comes from
+// hipGetSymbolAddress, once per device, and is kept in g_scratch.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+int scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+  if (dev < 0 || dev >= kMaxDevices) return unsupported("device index beyond the library's scratch table");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail("hipGetSymbolAddress(scratch)", e);
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
   return BSR_OK;
 }
 
@@ -300,6 +329,32 @@ int bsr_run_decode(const bsr_plan* plan, const void* ws, const void* q, const vo
                    const void* v_cache, void* o, float* lse, int32_t dtype, float sm_scale,
                    void* stream) {
   return run_common(plan, ws, q, k_cache, v_cache, o, lse, dtype, sm_scale, stream, true);
+}
+
+int bsr_run_decode_scratch(const bsr_plan* plan, const void* q, const void* k_cache, const void* v_cache,
+                           void* o, float* lse, int32_t dtype, float sm_scale, void* stream) {
+  if (!plan) return invalid("plan is NULL");
+  if (plan->ws.total > kScratchBytes) {
+    std::ostringstream os;
+    os << "the plan needs " << plan->ws.total << " bytes of workspace; bsr_run_decode_scratch holds at most "
+       << kScratchBytes << " (use bsr_run_decode with a workspace of that size)";
+    set_error(os.str());
+    return BSR_CAPACITY;
+  }
+  if (!plan->decode)
+    return invalid("bsr_run_decode_scratch needs a plan with one query per request (qo_indptr == NULL)");
+  if (plan->B == 0) return BSR_OK;
+  void* ws = nullptr;
+  int rc = scratch_on_current_device(&ws);
+  if (rc != BSR_OK) return rc;
+  // this call's plan metadata into the scratch (stream-ordered; partial states need no clearing:
+  // the merge reads only slots the attention kernel wrote in the same call)
+  const void* src = plan->pinned ? plan->pinned : static_cast<const void*>(plan->meta.data());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(ws, src, plan->meta.size(), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail("hipMemcpyAsync(plan metadata into the scratch)", e);
+  return run_common(plan, ws, q, k_cache, v_cache, o, lse, dtype, sm_scale, stream, true, false, 1.f, 1.f,
+                    nullptr, true);
 }
 
 int bsr_run_prefill_masked(const bsr_plan* plan, const void* ws, const void* q, const void* k_cache,

@@ -210,6 +210,22 @@ int bsr_run_decode(const bsr_plan* plan, const void* ws, const void* q, const vo
                    void* stream);
 
 /*
+ * bsr_run_decode without a caller workspace, for callers that cannot allocate device memory
+ * (code under graph capture, serving loops, harnesses that forbid allocation).  The workspace is
+ * a static device array of the library, at most 32 MiB (plans needing more return BSR_CAPACITY
+ * before touching the GPU), which every GPU the library runs on holds until the process ends.
+ * Each call copies the plan's metadata into that array on `stream` (from the plan's pinned
+ * staging once bsr_plan_upload has created it, else from ordinary host memory, which the HIP
+ * runtime copies before returning), then runs the same kernels as bsr_run_decode; the results
+ * are identical.  Arguments, layouts and errors are those of bsr_run_decode; the call allocates
+ * nothing.  All calls on one GPU share the array and it keeps the last call's contents: calls
+ * that overlap on one GPU (other streams, other threads, other plans) race, so order them.
+ * Nothing in the array needs clearing between calls.
+ */
+int bsr_run_decode_scratch(const bsr_plan* plan, const void* q, const void* k_cache, const void* v_cache,
+                           void* o, float* lse, int32_t dtype, float sm_scale, void* stream);
+
+/*
  * Paged decode over an E4M3 KV cache: as bsr_run_decode with bf16 Q and O, but k_cache and
  * v_cache hold one byte per element in the OCP 8-bit float "E4M3FN" encoding (sign, 4
  * exponent bits with bias 7, 3 mantissa bits; S.1111.111 is NaN; largest finite 448) and
