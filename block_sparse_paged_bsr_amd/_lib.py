@@ -80,11 +80,15 @@ class PlanView(C.Structure):
         ("logits_soft_cap", C.c_float),
         ("tile_lo", i32p),
         ("custom_mask_bits", C.c_int64),
+        ("num_levels", C.c_int32),
+        ("level_req_start", i32p),
+        ("merge_row_off", i32p),
     ]
 
 
 EXPORTED = [
     "bsr_plan_create",
+    "bsr_plan_create_composable",
     "bsr_plan_destroy",
     "bsr_plan_workspace_bytes",
     "bsr_plan_upload",
@@ -127,6 +131,8 @@ def lib():
     vp = C.c_void_p
     L.bsr_plan_create.argtypes = [C.POINTER(PlanDesc), C.POINTER(vp)]
     L.bsr_plan_create.restype = C.c_int
+    L.bsr_plan_create_composable.argtypes = [C.POINTER(PlanDesc), C.c_int32, C.c_int32, C.POINTER(vp)]
+    L.bsr_plan_create_composable.restype = C.c_int
     L.bsr_plan_destroy.argtypes = [vp]
     L.bsr_plan_destroy.restype = None
     L.bsr_plan_workspace_bytes.argtypes = [vp, C.POINTER(C.c_size_t)]

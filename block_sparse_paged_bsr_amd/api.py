@@ -38,6 +38,41 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _plan_desc(kv_indptr, kv_indices, last_page_len, *, num_pages, num_qo_heads, num_kv_heads, head_dim, page_size,
+               qo_indptr=None, causal=False, num_workers=0, tile_q=0, alpha=2, beta=1, window_left=-1,
+               logits_soft_cap=0.0):
+    """A bsr_plan_desc and the int32 arrays it points to (keep them alive while it is used)."""
+    kv_indptr, p_ip = _i32(kv_indptr)
+    kv_indices, p_ix = _i32(kv_indices)
+    last_page_len, p_last = _i32(last_page_len)
+    if qo_indptr is not None:
+        qo_indptr, p_qo = _i32(qo_indptr)
+    else:
+        p_qo = C.cast(None, _lib.i32p)
+    d = _lib.PlanDesc(
+        batch=len(kv_indptr) - 1,
+        qo_indptr=p_qo,
+        kv_indptr=p_ip,
+        kv_indices=p_ix,
+        last_page_len=p_last,
+        num_pages=int(num_pages),
+        num_qo_heads=int(num_qo_heads),
+        num_kv_heads=int(num_kv_heads),
+        head_dim=int(head_dim),
+        page_size=int(page_size),
+        causal=int(bool(causal)),
+        num_workers=int(num_workers),
+        tile_q=int(tile_q),
+        alpha=int(alpha),
+        beta=int(beta),
+        # the ABI counts the window in keys (0 = none); window_left keeps the pages'
+        # notation, keys left of the diagonal (-1 = none)
+        window_size=int(window_left) + 1,
+        logits_soft_cap=float(logits_soft_cap),
+    )
+    return d, (kv_indptr, kv_indices, last_page_len, qo_indptr)
+
+
 class Plan:
     """Host plan: the load-balanced split-KV partition of one batch (bsr_plan_create)."""
 
@@ -61,45 +96,25 @@ class Plan:
         window_left: int = -1,
         logits_soft_cap: float = 0.0,
     ):
-        kv_indptr, p_ip = _i32(kv_indptr)
-        kv_indices, p_ix = _i32(kv_indices)
-        last_page_len, p_last = _i32(last_page_len)
-        if qo_indptr is not None:
-            qo_indptr, p_qo = _i32(qo_indptr)
-        else:
-            p_qo = C.cast(None, _lib.i32p)
-        d = _lib.PlanDesc(
-            batch=len(kv_indptr) - 1,
-            qo_indptr=p_qo,
-            kv_indptr=p_ip,
-            kv_indices=p_ix,
-            last_page_len=p_last,
-            num_pages=int(num_pages),
-            num_qo_heads=int(num_qo_heads),
-            num_kv_heads=int(num_kv_heads),
-            head_dim=int(head_dim),
-            page_size=int(page_size),
-            causal=int(bool(causal)),
-            num_workers=int(num_workers),
-            tile_q=int(tile_q),
-            alpha=int(alpha),
-            beta=int(beta),
-            # the ABI counts the window in keys (0 = none); window_left keeps the pages'
-            # notation, keys left of the diagonal (-1 = none)
-            window_size=int(window_left) + 1,
-            logits_soft_cap=float(logits_soft_cap),
-        )
+        d, keep = _plan_desc(kv_indptr, kv_indices, last_page_len, num_pages=num_pages, num_qo_heads=num_qo_heads,
+                             num_kv_heads=num_kv_heads, head_dim=head_dim, page_size=page_size,
+                             qo_indptr=qo_indptr, causal=causal, num_workers=num_workers, tile_q=tile_q,
+                             alpha=alpha, beta=beta, window_left=window_left, logits_soft_cap=logits_soft_cap)
         h = C.c_void_p()
         check(lib().bsr_plan_create(C.byref(d), C.byref(h)))
+        self._init(h, num_qo_heads, num_kv_heads, head_dim, num_pages, page_size, qo_indptr is None,
+                   len(keep[0]) - 1, None if qo_indptr is None else int(keep[3][-1]))
+
+    def _init(self, h, num_qo_heads, num_kv_heads, head_dim, num_pages, page_size, decode, batch, total_q):
         self._h = h
         self.num_qo_heads = int(num_qo_heads)
         self.num_kv_heads = int(num_kv_heads)
         self.head_dim = int(head_dim)
         self.num_pages = int(num_pages)
         self.page_size = int(page_size)
-        self.decode = qo_indptr is None
-        self.batch = len(kv_indptr) - 1
-        self.total_q = self.batch if qo_indptr is None else int(qo_indptr[-1])
+        self.decode = decode
+        self.batch = batch
+        self.total_q = batch if total_q is None else total_q
         self._ws = None
         self._mask_bits = None
 
@@ -161,7 +176,37 @@ class Plan:
             "window_left": v.window_left,
             "logits_soft_cap": v.logits_soft_cap,
             "custom_mask_bits": v.custom_mask_bits,
+            "num_levels": v.num_levels,
+            "level_req_start": arr(v.level_req_start, v.num_levels + 1) if v.level_req_start else None,
+            "merge_row_off": (arr(v.merge_row_off, int(merge_ptr[-1]) if nm else 0)
+                              if v.merge_row_off else None),
         }
+
+
+class ComposablePlan(Plan):
+    """bsr_plan_create_composable: several BSR views ("levels") of one KV pool over the same
+    queries, scheduled as one plan whose run folds every query's states over the levels.
+
+    ``levels``: one dict per level with kv_indptr, kv_indices, last_page_len and optionally
+    qo_indptr (None: one query per request); the other arguments are shared by all levels."""
+
+    def __init__(self, levels, *, num_pages, num_qo_heads, num_kv_heads, head_dim, page_size, num_workers=0,
+                 alpha=2, beta=1, logits_soft_cap=0.0):
+        descs, keep = [], []
+        for lv in levels:
+            d, k = _plan_desc(lv["kv_indptr"], lv["kv_indices"], lv["last_page_len"], num_pages=num_pages,
+                              num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                              page_size=page_size, qo_indptr=lv.get("qo_indptr"), alpha=alpha, beta=beta,
+                              logits_soft_cap=logits_soft_cap)
+            descs.append(d)
+            keep.append(k)
+        arr_t = _lib.PlanDesc * len(descs)
+        h = C.c_void_p()
+        check(lib().bsr_plan_create_composable(arr_t(*descs), len(descs), int(num_workers), C.byref(h)))
+        k0 = keep[0]
+        total_q = (len(k0[0]) - 1) if k0[3] is None else int(k0[3][-1])
+        self._init(h, num_qo_heads, num_kv_heads, head_dim, num_pages, page_size, False, total_q, total_q)
+        self.num_levels = len(descs)
 
 
 def plan(*args, **kw) -> Plan:

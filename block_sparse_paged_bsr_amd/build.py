@@ -19,6 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 
 SOURCES = [
     os.path.join(CSRC, "plan.cpp"),
+    os.path.join(CSRC, "compose.cpp"),
     os.path.join(CSRC, "api.hip"),
     os.path.join(CSRC, "kernels", "attn_f32.hip"),
     os.path.join(CSRC, "kernels", "attn_prefill_bf16.hip"),

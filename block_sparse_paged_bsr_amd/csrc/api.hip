@@ -96,6 +96,7 @@ RunArgs make_args(const bsr_plan* p, const void* ws) {
   a.qptr = reinterpret_cast<const int32_t*>(base + p->ws.qptr);
   a.merge = reinterpret_cast<const MergeRec*>(base + p->ws.merge);
   a.mslots = reinterpret_cast<const int32_t*>(base + p->ws.mslots);
+  a.mroff = reinterpret_cast<const int32_t*>(base + p->ws.mroff);
   a.part_o = reinterpret_cast<float*>(const_cast<char*>(base) + p->ws.part_o);
   a.part_lse = reinterpret_cast<float*>(const_cast<char*>(base) + p->ws.part_lse);
   a.B = p->B;
@@ -161,8 +162,10 @@ int run_common(const bsr_plan* p, const void* ws, const void* q, const void* k, 
       if (!attn_f32_supported(p->d)) return unsupported("fp32 head_dim must be one of 16, 32, 64, 128, 256");
       e = launch_attn_f32(a, s);
     } else {
-      // the decode kernel has no custom-mask path: masked runs use the tiled kernel
-      const bool dec_ok = p->decode && !mask && decode_bf16_supported(p->d, p->g, p->Tq);
+      // the decode kernel (no custom-mask, causal or window path) serves decode plans and
+      // non-causal plans of tiles of at most 16 packed rows; everything else the tiled kernels
+      const bool dec_ok = !mask && ((p->decode && decode_bf16_supported(p->d, p->g, p->Tq)) ||
+                                    (!p->causal && p->window_left < 0 && decode_bf16_tiles(p->d, p->g, p->Tq)));
       if (dec_ok) {
         e = launch_decode_bf16(a, false, s);
       } else {
@@ -233,6 +236,26 @@ int bsr_plan_create(const bsr_plan_desc* desc, bsr_plan** out) {
   int rc;
   try {
     rc = build_plan(desc, p);
+  } catch (const std::bad_alloc&) {
+    set_error("out of host memory while planning");
+    rc = BSR_INVALID_ARG;
+  }
+  if (rc != BSR_OK) {
+    delete p;
+    return rc;
+  }
+  *out = p;
+  return BSR_OK;
+}
+
+int bsr_plan_create_composable(const bsr_plan_desc* levels, int32_t n_levels, int32_t num_workers, bsr_plan** out) {
+  if (!out) return invalid("out is NULL");
+  *out = nullptr;
+  bsr_plan* p = new (std::nothrow) bsr_plan();
+  if (!p) return invalid("out of host memory");
+  int rc;
+  try {
+    rc = build_composable_plan(levels, n_levels, num_workers, p);
   } catch (const std::bad_alloc&) {
     set_error("out of host memory while planning");
     rc = BSR_INVALID_ARG;
@@ -322,6 +345,9 @@ int bsr_plan_export(const bsr_plan* p, bsr_plan_view* v) {
   v->logits_soft_cap = p->soft_cap;
   v->tile_lo = p->tile_lo.data();
   v->custom_mask_bits = p->mask_bits;
+  v->num_levels = p->num_levels;
+  v->level_req_start = p->level_req_start.empty() ? nullptr : p->level_req_start.data();
+  v->merge_row_off = p->merge_roff.empty() ? nullptr : p->merge_roff.data();
   return BSR_OK;
 }
 

@@ -33,25 +33,29 @@ struct ItemRec {
   int32_t kv_start;   // logical tokens [kv_start, kv_end) of the request
   int32_t kv_end;
   int32_t slot;       // partial slot, or -1: write the final output
-  int32_t tile;
-  int32_t pad;
+  int32_t q_start;    // the request's first query row and first page-list entry, copied from its
+  int32_t page_start; //   request record so that the decode kernel needs only this record
 };
 static_assert(sizeof(ItemRec) == 32, "ItemRec layout");
 
-// Per tile written by the merge pass (split tiles and empty tiles).
+// Per block of output rows written by the merge pass: a split or empty tile of a plan, or one
+// query (all of its GQA rows) of a composable plan.  Slot k of the list holds the partial state of
+// rows row_start .. row_end-1 at partial rows (slot * H_kv + h_kv) * T_q + roff_k + (row - row_start),
+// with roff_k = 0 unless the record has row offsets (composable plans).
 struct MergeRec {
-  int32_t req;
-  int32_t row_start;
-  int32_t row_end;
-  int32_t slot_begin;  // into the merge slot list
+  int32_t q_start;     // first query row in Q/O that packed row 0 refers to
+  int32_t row_start;   // packed GQA rows [row_start, row_end): row r is query q_start + r / g,
+  int32_t row_end;     //   head g * h_kv + r % g
+  int32_t slot_begin;  // into the merge slot list (and the row-offset list)
   int32_t slot_count;  // 0 => empty state
-  int32_t pad[3];
+  int32_t has_roff;    // 1: the row-offset list carries roff_k for each slot
+  int32_t pad[2];
 };
 static_assert(sizeof(MergeRec) == 32, "MergeRec layout");
 
 // Byte offsets of the workspace sections (all 256-byte aligned).
 struct WsLayout {
-  size_t req = 0, indices = 0, items = 0, qptr = 0, merge = 0, mslots = 0;
+  size_t req = 0, indices = 0, items = 0, qptr = 0, merge = 0, mslots = 0, mroff = 0;
   size_t meta_bytes = 0;  // end of metadata
   size_t part_o = 0, part_lse = 0;
   size_t total = 0;
@@ -80,7 +84,11 @@ struct bsr_plan {
   std::vector<int32_t> queue_items;  // [num_items]
   std::vector<int64_t> worker_cost;  // [C]
   std::vector<int32_t> merge_tiles, merge_ptr, merge_slots;
+  std::vector<int32_t> merge_roff;   // composable plans: partial-row offset of each merge slot
   int32_t num_slots = 0;
+  // composable plans: number of levels and the first (flattened) request of each level
+  int32_t num_levels = 1;
+  std::vector<int32_t> level_req_start;
   // device image
   bsr::WsLayout ws;
   std::vector<uint8_t> meta;  // host copy of the metadata region (ws.meta_bytes)
@@ -92,5 +100,7 @@ struct bsr_plan {
 namespace bsr {
 // host planner (plan.cpp); returns BSR_OK or an error with the message set
 int build_plan(const bsr_plan_desc* desc, bsr_plan* p);
+// composable plan over several BSR views (compose.cpp)
+int build_composable_plan(const bsr_plan_desc* levels, int32_t n_levels, int32_t num_workers, bsr_plan* p);
 void set_error(const std::string& msg);
 }  // namespace bsr

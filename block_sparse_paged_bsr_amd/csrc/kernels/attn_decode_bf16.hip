@@ -12,8 +12,9 @@
 //           kb = 0 .. D/32-1, 16 bytes each, rows found through the page table (eq. 7);
 //           the next step's rows are requested before the current step is computed.
 //   scores  S^T = K Q^T on v_mfma_f32_16x16x32_bf16: the K fragment is the A operand
-//           as loaded, Q^T (column n = query head n mod g) is the B operand; lane (n, j)
-//           receives the scores of tokens 4j..4j+3 for head n.
+//           as loaded, Q^T (column n = packed row n of the tile: one of the g query heads, or
+//           of the rows of a several-query tile) is the B operand; lane (n, j) receives the
+//           scores of tokens 4j..4j+3 for row n.
 //   softmax per head (one column per lane group), in log2 units, with the running
 //           maximum of the online-softmax recurrence ("FlashInfer: Engineering ...",
 //           §II.2); the accumulator is rescaled only when the maximum grows.
@@ -79,22 +80,66 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
   const uint8_t* __restrict__ K = static_cast<const uint8_t*>(a.k);
   const uint8_t* __restrict__ V = static_cast<const uint8_t*>(a.v);
   uint16_t* __restrict__ O = static_cast<uint16_t*>(a.o);
-  const int head_col = n < g ? n : n % g;  // query head offset served by column n
 
-  for (int it = a.qptr[w]; it < a.qptr[w + 1]; ++it) {
-    const ItemRec item = a.items[it];
-    const ReqRec rq = a.req[item.req];
-    const int kv_end = item.kv_end;
-
-    // Q^T as the B operand: column n = query head hk*g + head_col; k-block kb covers the
-    // head-dim values this lane's K slice of that block holds
-    const uint16_t* qp = Q + (int64_t(rq.q_start) * a.Hq + hk * g + head_col) * D;
-    bf16x8 qb[KB];
+  // Column n of an item serves packed row row_start + n of its tile (GQA packing, eq. 3 of the
+  // review): query q_start + row / g, head g * h_kv + row % g.  A decode tile is the g heads of one
+  // query; a tile of a non-causal block row of several queries (the shared level of a composable
+  // format) holds up to 16 rows.  Columns past the tile repeat one of its rows.
+  auto out_row = [&](const ItemRec& itm) -> int64_t {
+    const int rows = itm.row_end - itm.row_start;
+    const int row = itm.row_start + (n < rows ? n : n % rows);
+    return int64_t(itm.q_start + row / g) * a.Hq + hk * g + row % g;
+  };
+  // Q^T as the B operand: column n = that row's query and head; k-block kb covers the head-dim
+  // values this lane's K slice of that block holds
+  auto load_q = [&](const ItemRec& itm, bf16x8 (&dst)[KB]) {
+    const uint16_t* qp = Q + out_row(itm) * D;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int col = KV8 ? 64 * (kb >> 1) + 16 * j + 8 * (kb & 1) : 32 * kb + 8 * j;
-      qb[kb] = *reinterpret_cast<const bf16x8*>(qp + col);
+      dst[kb] = *reinterpret_cast<const bf16x8*>(qp + col);
     }
+  };
+  // page of token t of an item (eq. 7), t clamped to the item's last token
+  auto page_in = [&](const ItemRec& itm, int t) -> int32_t {
+    const int tc = min(t, itm.kv_end - 1);
+    return a.indices[itm.page_start + (a.p_shift >= 0 ? (tc >> a.p_shift) : tc / a.P)];
+  };
+
+  // The work item record carries everything this kernel needs (rows, KV range, slot, query and
+  // page-list starts).  The next item's record is fetched when an item starts, and its queries and
+  // first page ids during the item's last step, so that a new item starts with only its first
+  // rows to wait for.
+  constexpr int NPRE = KV8 ? 4 : 2;  // page ids of the first two steps (16 tokens each)
+  const int it_end = a.qptr[w + 1];
+  int it = a.qptr[w];
+  ItemRec next = a.items[it < it_end ? it : 0];
+  bf16x8 qb[KB], qn[KB];
+  int32_t pre[NPRE];
+  bool have_pre = false;
+  for (; it < it_end; ++it) {
+    const ItemRec item = next;
+    if (it + 1 < it_end) next = a.items[it + 1];
+    const bool more = it + 1 < it_end;
+    const int kv_end = item.kv_end;
+    const int64_t orow = out_row(item);
+    if (have_pre) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) qb[kb] = qn[kb];
+    } else {
+      load_q(item, qb);
+#pragma unroll
+      for (int u = 0; u < NPRE; ++u) pre[u] = page_in(item, item.kv_start + 16 * u + n);
+    }
+    have_pre = false;
+    // the next item's queries and first page ids (issued in this item's last step)
+    auto preload_next = [&]() {
+      if (!more) return;
+      load_q(next, qn);
+#pragma unroll
+      for (int u = 0; u < NPRE; ++u) pre[u] = page_in(next, next.kv_start + 16 * u + n);
+      have_pre = true;
+    };
 
     float m = kNegInf, l = 0.f;
     f32x4 oacc[DB];
@@ -103,11 +148,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
 
     // page of this lane's token (lane n of a step): the index load runs one step ahead of
     // the row loads, which run one step ahead of the computation
-    const int pg_start = rq.page_start;
-    auto page_of = [&](int t) -> int32_t {
-      const int tc = min(t, kv_end - 1);
-      return a.indices[pg_start + (a.p_shift >= 0 ? (tc >> a.p_shift) : tc / a.P)];
-    };
+    auto page_of = [&](int t) -> int32_t { return page_in(item, t); };
     // byte offset of this lane's first 16-byte piece of token t's row
     auto row_base = [&](int t, int32_t page) -> int64_t {
       const int tc = min(t, kv_end - 1);
@@ -190,15 +231,17 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
     };
 
     if constexpr (PD == 1) {
-      int32_t pg_next = page_of(item.kv_start + 16 + n);
+      int32_t pg_next = pre[1];
       u32x4 kr[NL], vr[NL];
-      load_rows(kr, vr, item.kv_start + n, page_of(item.kv_start + n));
+      load_rows(kr, vr, item.kv_start + n, pre[0]);
       for (int t0 = item.kv_start; t0 < kv_end; t0 += 16) {
         const bool has_next = t0 + 16 < kv_end;
         const int32_t pg_after = page_of(t0 + 32 + n);
-        // request the next step's rows before touching this step's data
+        // request the next step's rows (or, in the last step, the next item's queries and first
+        // page ids) before touching this step's data
         u32x4 kn[NL], vn[NL];
         if (has_next) load_rows(kn, vn, t0 + 16 + n, pg_next);
+        else preload_next();
         pg_next = pg_after;
         compute(t0, kr, vr);
         if (has_next) {
@@ -212,10 +255,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
     } else {
       // E4M3: 32 tokens per step, two 16-token halves loaded together, so a wave has as many
       // bytes in flight as with one step of bf16 rows
-      int32_t pg_next0 = page_of(item.kv_start + 32 + n), pg_next1 = page_of(item.kv_start + 48 + n);
+      int32_t pg_next0 = pre[2], pg_next1 = pre[3];
       u32x4 kr[2][NL], vr[2][NL];
-      load_rows(kr[0], vr[0], item.kv_start + n, page_of(item.kv_start + n));
-      load_rows(kr[1], vr[1], item.kv_start + 16 + n, page_of(item.kv_start + 16 + n));
+      load_rows(kr[0], vr[0], item.kv_start + n, pre[0]);
+      load_rows(kr[1], vr[1], item.kv_start + 16 + n, pre[1]);
       for (int t0 = item.kv_start; t0 < kv_end; t0 += 32) {
         const bool has_next = t0 + 32 < kv_end;
         const int32_t pa0 = page_of(t0 + 64 + n), pa1 = page_of(t0 + 80 + n);
@@ -223,6 +266,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
         u32x4 kn[2][NL], vn[2][NL];
         load_rows(kn[0], vn[0], t0 + 32 + n, pg_next0);
         load_rows(kn[1], vn[1], t0 + 48 + n, pg_next1);
+        if (!has_next) preload_next();
         compute(t0, kr[0], vr[0]);
         if (t0 + 16 < kv_end) compute(t0 + 16, kr[1], vr[1]);
         pg_next0 = pa0;
@@ -241,21 +285,20 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
     // lane (n, j) summed tokens 4j..4j+3 of every step; add the four token groups
     l += shfl_xor(l, 16);
     l += shfl_xor(l, 32);
-    if (n < g) {
-      const int hq = hk * g + n;
+    if (n < item.row_end - item.row_start) {
       const bool empty = !(l > 0.f);
       const float inv = empty ? 0.f : o_scale / l;
       const float lse = empty ? kNegInf : (m + log2f(l)) * kLn2;
       if (item.slot < 0) {
-        uint16_t* op = O + (int64_t(rq.q_start) * a.Hq + hq) * D + 4 * j;
+        uint16_t* op = O + orow * D + 4 * j;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const f32x4 v = oacc[db] * inv;
           *reinterpret_cast<u32x2*>(op + db * 16) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         }
-        if (j == 0) a.lse[int64_t(rq.q_start) * a.Hq + hq] = lse;
+        if (j == 0) a.lse[orow] = lse;
       } else {
-        const int64_t prow = (int64_t(item.slot) * a.Hk + hk) * a.Tq + n;  // packed row = head offset
+        const int64_t prow = (int64_t(item.slot) * a.Hk + hk) * a.Tq + n;  // row n of the tile
         float* pp = a.part_o + prow * D + 4 * j;
 #pragma unroll
         for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(pp + db * 16) = oacc[db] * inv;
@@ -268,6 +311,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
 bool decode_bf16_supported(int d, int g, int Tq) {
   return (d == 64 || d == 128) && g >= 1 && g <= 16 && g <= Tq;
 }
+
+bool decode_bf16_tiles(int d, int g, int Tq) { return (d == 64 || d == 128) && g >= 1 && Tq <= 16; }
 
 int decode_bf16_waves_per_block(int Hk) { return Hk < kDecodeWaves ? Hk : kDecodeWaves; }
 

@@ -27,6 +27,7 @@ struct RunArgs {
   const int32_t* qptr;
   const MergeRec* merge;
   const int32_t* mslots;
+  const int32_t* mroff;  // partial-row offset per merge slot (records with has_roff)
   float* part_o;
   float* part_lse;
   const void* q;

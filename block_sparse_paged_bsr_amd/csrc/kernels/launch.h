@@ -19,6 +19,9 @@ int prefill_bf16_blocks_per_cu(int d);
 // bf16 paged decode: MFMA scores, GQA-fused, split-KV partials.  kv_e4m3: K and V are E4M3
 // bytes with per-tensor scales (RunArgs::k_scale, v_scale); Q and O stay bf16.
 bool decode_bf16_supported(int d, int g, int Tq);
+// Non-causal plans whose query tiles hold at most 16 packed rows (several queries each) also run
+// on the decode kernel: every row of a tile sees the same keys.
+bool decode_bf16_tiles(int d, int g, int Tq);
 hipError_t launch_decode_bf16(const RunArgs& a, bool kv_e4m3, hipStream_t s);
 // One workgroup per worker holds min(H_kv, 8) waves, one per KV head; H_kv above 8 takes several
 // workgroups per worker.

@@ -43,30 +43,34 @@ __device__ __forceinline__ float load_in<uint16_t>(const uint16_t* p) { return _
 // phase 1, so those loads overlap the LSE reads.
 constexpr int kMergeThreads = 256;
 constexpr int kSlotsInLds = 1024;
-constexpr int kFastSlots = 8;
+constexpr int kFastSlots = 16;
 constexpr int kRowChunk = 16;
 constexpr int kWeightSlots = 256;
 
 template <typename OutT>
 __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a, int row_chunks) {
-  __shared__ int s_slot[kSlotsInLds];
+  __shared__ int64_t s_base[kSlotsInLds];  // partial row of row 0 of this chunk, per slot
   __shared__ float s_m[kRowChunk], s_den[kRowChunk], s_w[kWeightSlots * kRowChunk];
   const int hk = blockIdx.y, tid = threadIdx.x;
   const int mi = blockIdx.x / row_chunks, r0 = (blockIdx.x % row_chunks) * kRowChunk;
   const MergeRec mr = a.merge[mi];
   const int nrows = min(kRowChunk, mr.row_end - mr.row_start - r0);  // rows r0 .. r0 + nrows - 1
   if (nrows <= 0) return;  // uniform: a chunk past the tile's last row
-  const ReqRec rq = a.req[mr.req];
   const int ns = mr.slot_count;
   const int D = a.d;
   const int* __restrict__ slots = a.mslots + mr.slot_begin;
+  const int* __restrict__ roffs = a.mroff + mr.slot_begin;
+  const bool has_roff = mr.has_roff != 0;
   const bool cached = ns <= kSlotsInLds;
+  auto base_of = [&](int k) -> int64_t {
+    return (int64_t(slots[k]) * a.Hk + hk) * a.Tq + (has_roff ? roffs[k] : 0) + r0;
+  };
   if (cached)
-    for (int k = tid; k < ns; k += kMergeThreads) s_slot[k] = slots[k];
+    for (int k = tid; k < ns; k += kMergeThreads) s_base[k] = base_of(k);
   __syncthreads();
-  auto slot_at = [&](int k) { return cached ? s_slot[k] : slots[k]; };
-  // partial-state row of slot s for row r of this chunk
-  auto prow_at = [&](int s, int r) { return (int64_t(s) * a.Hk + hk) * a.Tq + r0 + r; };
+  // partial-state row of the k-th slot of the list for row r of this chunk (one LDS read per
+  // slot, so the unrolled folds below issue their loads together)
+  auto prow_at = [&](int k, int r) { return (cached ? s_base[k] : base_of(k)) + r; };
 
   const bool fast = ns <= kFastSlots && nrows * D <= 2 * kMergeThreads;  // uniform
   float ov[2][kFastSlots];
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a
 #pragma unroll
       for (int k = 0; k < kFastSlots; ++k) {
         ov[u][k] = 0.f;
-        if (idx < nrows * D && k < ns) ov[u][k] = a.part_o[prow_at(slot_at(k), lr) * D + e];
+        if (idx < nrows * D && k < ns) ov[u][k] = a.part_o[prow_at(k, lr) * D + e];
       }
     }
   }
@@ -90,12 +94,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a
   const int r = tid / tpr, sub = tid % tpr;
   float mx = kNegInf;
   if (r < nrows)
-    for (int k = sub; k < ns; k += tpr) mx = fmaxf(mx, a.part_lse[prow_at(slot_at(k), r)]);
+    for (int k = sub; k < ns; k += tpr) mx = fmaxf(mx, a.part_lse[prow_at(k, r)]);
   for (int o = 1; o < tpr; o <<= 1) mx = fmaxf(mx, shfl_xor(mx, o));
   float den = 0.f;
   if (r < nrows && mx != kNegInf)
     for (int k = sub; k < ns; k += tpr) {
-      const float l = a.part_lse[prow_at(slot_at(k), r)];
+      const float l = a.part_lse[prow_at(k, r)];
       const float w = l == kNegInf ? 0.f : expf(l - mx);
       den += w;
       if (k < kWeightSlots) s_w[k * kRowChunk + r] = w;
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a
   auto finish = [&](int lr, int e, float acc) {
     const float m = s_m[lr];
     const int row = mr.row_start + r0 + lr;
-    const int64_t orow = int64_t(rq.q_start + row / a.g) * a.Hq + hk * a.g + row % a.g;
+    const int64_t orow = int64_t(mr.q_start + row / a.g) * a.Hq + hk * a.g + row % a.g;
     store_out<OutT>(O + orow * D + e, m == kNegInf ? 0.f : acc / s_den[lr]);
     if (e == 0) a.lse[orow] = m == kNegInf ? kNegInf : m + logf(s_den[lr]);
   };
@@ -137,9 +141,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a
     float acc = 0.f;
     if (m != kNegInf) {
       const int nw = min(ns, kWeightSlots);
-      // unrolled by the slot count (uniform), so that the loads of a short fold are issued together
-      auto fold = [&](int k) { acc += s_w[k * kRowChunk + lr] * a.part_o[prow_at(slot_at(k), lr) * D + e]; };
-      if (nw >= 8) {
+      // unrolled by the slot count (uniform), so that the loads of a short fold are issued together;
+      // the slots' row bases come from LDS (a slot list beyond it takes the plain loop)
+      auto fold = [&](int k) { acc += s_w[k * kRowChunk + lr] * a.part_o[(s_base[k] + lr) * D + e]; };
+      if (!cached) {
+        for (int k = 0; k < nw; ++k) acc += s_w[k * kRowChunk + lr] * a.part_o[prow_at(k, lr) * D + e];
+      } else if (nw >= 8) {
 #pragma unroll 8
         for (int k = 0; k < nw; ++k) fold(k);
       } else if (nw >= 4) {
@@ -150,7 +157,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a
         for (int k = 0; k < nw; ++k) fold(k);
       }
       for (int k = nw; k < ns; ++k) {
-        const int64_t prow = prow_at(slot_at(k), lr);
+        const int64_t prow = prow_at(k, lr);
         const float l = a.part_lse[prow];
         acc += (l == kNegInf ? 0.f : expf(l - m)) * a.part_o[prow * D + e];
       }

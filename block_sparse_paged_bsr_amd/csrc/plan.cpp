@@ -274,6 +274,7 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
   const int32_t NM = int32_t(p->merge_tiles.size());
   L.merge = off;    off = align256(off + sizeof(MergeRec) * std::max(NM, 1));
   L.mslots = off;   off = align256(off + sizeof(int32_t) * std::max<size_t>(p->merge_slots.size(), 1));
+  L.mroff = off;    off = align256(off + sizeof(int32_t));  // (no row offsets in a single-level plan)
   L.meta_bytes = off;
   const size_t rows_per_slot = size_t(p->Hk) * Tq;
   L.part_o = off;   off = align256(off + sizeof(float) * rows_per_slot * p->d * p->num_slots);
@@ -299,13 +300,13 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
   auto* qi = reinterpret_cast<ItemRec*>(p->meta.data() + L.items);
   for (int32_t k = 0; k < M; ++k) {
     const Item& it = items[p->queue_items[k]];
-    qi[k] = ItemRec{it.req, it.r0, it.r1, it.ks, it.ks + it.kl, it.slot, it.tile, 0};
+    qi[k] = ItemRec{it.req, it.r0, it.r1, it.ks, it.ks + it.kl, it.slot, req[it.req].q_start, req[it.req].page_start};
   }
   std::memcpy(p->meta.data() + L.qptr, p->queue_ptr.data(), sizeof(int32_t) * (p->C + 1));
   auto* mr = reinterpret_cast<MergeRec*>(p->meta.data() + L.merge);
   for (int32_t k = 0; k < NM; ++k) {
     const int32_t* tr = &p->tiles[5 * p->merge_tiles[k]];
-    mr[k] = MergeRec{tr[0], tr[1], tr[2], p->merge_ptr[k], p->merge_ptr[k + 1] - p->merge_ptr[k], {0, 0, 0}};
+    mr[k] = MergeRec{p->qo_indptr[tr[0]], tr[1], tr[2], p->merge_ptr[k], p->merge_ptr[k + 1] - p->merge_ptr[k], 0, {0, 0}};
   }
   if (!p->merge_slots.empty())
     std::memcpy(p->meta.data() + L.mslots, p->merge_slots.data(),

@@ -113,6 +113,32 @@ typedef struct bsr_plan_desc {
  */
 int bsr_plan_create(const bsr_plan_desc* desc, bsr_plan** out);
 
+/*
+ * Composable formats: attention of every query over the union of several BSR views ("levels") of
+ * one KV pool, the levels' states combined with the merge operator of eq. 6 ("FlashInfer:
+ * Engineering a Customizable, Block-Sparse Attention Engine for LLM Inference Serving" §IV.6 and
+ * "FlashInfer 原理" §⑤: a shared prefix stored once as a block row of several queries, B_r > 1,
+ * private suffixes as ordinary rows; "FlashInfer: Making Attention Fit the Serving Workload"
+ * §7.3, eq. 15).
+ *   levels[0 .. n_levels-1]: one description per view, over the same queries and the same pool:
+ *     equal num_qo_heads, num_kv_heads, head_dim, page_size, num_pages, logits_soft_cap, alpha,
+ *     beta; every level's query count (qo_indptr[B], or B when qo_indptr is NULL) is the same
+ *     total_q, and query q of a level is query q of Q/O.  Levels are non-causal (causal = 0,
+ *     window_size = 0); tile_q and num_workers of the descriptions are ignored.  The group size
+ *     H_qo / H_kv must divide 16.
+ *   num_workers: C for the whole plan (0 => default).
+ * Every level's block rows are cut into query tiles of 16 packed rows and the tiles of all levels
+ * are scheduled together by the partition of bsr_plan_create (W = the levels' summed eq. 10 work,
+ * one chunk limit, one sorted list, one heap).  Every chunk writes a partial state; the reduction
+ * map holds one entry per query that lists its partial rows in every level (levels in order,
+ * chunks in KV order), so one merge pass folds levels and chunks (bsr_plan_view: merge_tiles[k] =
+ * query k, merge_row_off = the row of that query inside each slot's tile).  Run with
+ * bsr_run_prefill (Q/O [total_q, H_qo, d]): one attention launch over all levels, one merge launch.
+ * Errors: BSR_INVALID_ARG for NULL pointers, n_levels outside 1 .. 16, a level that
+ * bsr_plan_create rejects (the message names the level) or levels that do not match.
+ */
+int bsr_plan_create_composable(const bsr_plan_desc* levels, int32_t n_levels, int32_t num_workers, bsr_plan** out);
+
 /* Release a plan.  Waits for an in-flight bsr_plan_upload copy of this plan first. */
 void bsr_plan_destroy(bsr_plan* plan);
 
@@ -187,6 +213,10 @@ typedef struct bsr_plan_view {
   float logits_soft_cap;
   const int32_t* tile_lo;
   int64_t custom_mask_bits;  /* sum_i l_qo(i) * l_kv(i): bits of a bsr_run_prefill_masked mask */
+  /* composable plans (bsr_plan_create_composable); a single-view plan has num_levels 1 */
+  int32_t num_levels;
+  const int32_t* level_req_start;  /* [num_levels+1]: first flattened request of each level */
+  const int32_t* merge_row_off;    /* per merge slot: partial-row offset (composable plans), else NULL */
 } bsr_plan_view;
 
 int bsr_plan_export(const bsr_plan* plan, bsr_plan_view* view);

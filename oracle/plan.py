@@ -215,3 +215,95 @@ def partial_capacity_bound(num_workers, tile_q, num_heads, head_dim):
     same count reads 2 C T_q H_kv (d + 1): pass the KV head count.
     """
     return 2 * num_workers * tile_q * num_heads * (head_dim + 1)
+
+
+@dataclass
+class ComposablePlan:
+    group_size: int
+    tile_q: int
+    total_work: int
+    chunk_limit: int
+    num_workers: int
+    level_req_start: List[int]  # first flattened request of each level (+ the total)
+    tiles: List[Tile]  # every level's tiles; Tile.req is the flattened request index
+    items: List[Item]
+    queues: List[List[int]]
+    worker_cost: List[int]
+    units: List[List[tuple]]  # per query: (slot, row offset inside the slot's tile), in fold order
+    num_slots: int
+
+
+def make_composable_plan(levels, num_qo_heads, num_kv_heads, num_workers, alpha=2, beta=1, tile_q=16):
+    """Partition of a composable format: several BSR views ("levels") of one KV pool over the
+    same queries, whose attention states are merged per query ("FlashInfer: Engineering a
+    Customizable, Block-Sparse Attention Engine for LLM Inference Serving" §IV.6; "FlashInfer
+    原理" §⑤; eq. 6 of "FlashInfer: Making Attention Fit the Serving Workload").
+
+    ``levels``: list of (kv_lens, qo_lens) per level, qo_lens None for one query per request;
+    every level holds the same queries, numbered in request order.  The pages leave the joint
+    schedule open; the reading taken here: each level's block rows are tiled exactly as
+    ``make_plan`` tiles a non-causal batch (tile_q packed rows), the tiles of all levels form one
+    batch (levels in order) for the partition steps of ``make_plan`` -- total work (the levels'
+    eq. 10 sums), one chunk limit, creation-order chunks, one stable descending sort, one heap --
+    and every chunk writes a partial state (slots in assignment order).  Query q's reduction list
+    walks the levels in order and, in each, the chunks of the tile holding q's rows in KV order;
+    a chunk's row offset is the tile row of q's first packed row.
+    """
+    g = num_qo_heads // num_kv_heads
+    assert tile_q % g == 0, "a query's packed rows must not straddle two tiles"
+    per_level = [make_plan(kv, qo, num_qo_heads, num_kv_heads, 1, tile_q=tile_q, alpha=alpha, beta=beta)
+                 for kv, qo in levels]
+    level_req_start = [0]
+    tiles: List[Tile] = []
+    W = 0
+    for lp, (kv, qo) in zip(per_level, levels):
+        base = level_req_start[-1]
+        for t in lp.tiles:
+            tiles.append(Tile(base + t.req, t.row_start, t.row_end, t.vis))
+        level_req_start.append(base + len(kv))
+        W += lp.total_work
+    L = max(1, ceil_div(W, num_workers)) if W > 0 else 0
+
+    items: List[Item] = []
+    if L > 0:
+        for t_id, t in enumerate(tiles):
+            s = 0
+            while s < t.vis:
+                t.items.append(len(items))
+                items.append(Item(t.req, t_id, t.row_start, t.row_end, s, min(L, t.vis - s)))
+                s += L
+    order = sorted(range(len(items)), key=lambda m: -items[m].kv_len)
+    heap = [(0, w) for w in range(num_workers)]
+    heapq.heapify(heap)
+    queues: List[List[int]] = [[] for _ in range(num_workers)]
+    cost = [0] * num_workers
+    for m in order:
+        c, w = heapq.heappop(heap)
+        queues[w].append(m)
+        items[m].worker = w
+        c += alpha * tile_positions(items[m], g) + beta * items[m].kv_len
+        cost[w] = c
+        heapq.heappush(heap, (c, w))
+    for slot, m in enumerate(order):
+        items[m].slot = slot
+
+    # per query: in every level, the tile that holds its rows
+    qo0 = levels[0][1]
+    total_q = len(levels[0][0]) if qo0 is None else int(sum(qo0))
+    units = [[] for _ in range(total_q)]
+    t_id = 0
+    for li, (kv, qo) in enumerate(levels):
+        qo = [1] * len(kv) if qo is None else [int(x) for x in qo]
+        q0 = 0
+        for i in range(len(kv)):
+            nt = ceil_div(qo[i] * g, tile_q)
+            for pos in range(qo[i]):
+                row = pos * g
+                t = tiles[t_id + row // tile_q]
+                for m in sorted(t.items, key=lambda m: items[m].kv_start):
+                    units[q0 + pos].append((items[m].slot, row - t.row_start))
+            t_id += nt
+            q0 += qo[i]
+        assert q0 == total_q, "every level must hold the same queries"
+    return ComposablePlan(g, tile_q, W, L, num_workers, level_req_start, tiles, items, queues, cost, units,
+                          len(order))

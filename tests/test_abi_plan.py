@@ -358,3 +358,87 @@ def test_prefill_lpt_hand_worked_example_in_the_library():
     assert e["merge_tiles"].tolist() == g["expected_merge_tiles"]
     mp = e["merge_ptr"]
     assert [e["merge_slots"][mp[k]:mp[k + 1]].tolist() for k in range(len(mp) - 1)] == g["expected_merge_slots"]
+
+
+def _composable_lib_and_oracle(levels, Hq, Hk, C_, P=16, seed=0):
+    """levels: list of (kv_lens, qo_lens or None).  Pages: one permutation of the pool shared by
+    the levels (only the lengths matter to the plan)."""
+    rng = np.random.default_rng(seed)
+    need = sum(int(((np.asarray(kv) + P - 1) // P).sum()) for kv, _ in levels)
+    pool = max(need, 1)
+    perm = rng.permutation(pool)
+    descs, off = [], 0
+    for kv, qo in levels:
+        kv = np.asarray(kv, dtype=np.int64)
+        n = int(((kv + P - 1) // P).sum())
+        ip, ix, la = I.page_table_from_lengths(kv, P, perm[off:off + n])
+        off += n
+        d = dict(kv_indptr=ip, kv_indices=ix, last_page_len=la)
+        if qo is not None:
+            d["qo_indptr"] = np.concatenate([[0], np.cumsum(qo)]).astype(np.int32)
+        descs.append(d)
+    lp = api.ComposablePlan(descs, num_pages=pool, num_qo_heads=Hq, num_kv_heads=Hk, head_dim=128, page_size=P,
+                            num_workers=C_)
+    op = PL.make_composable_plan(levels, Hq, Hk, C_)
+    return lp, op
+
+
+def _assert_composable_same(lp, op):
+    e = lp.export()
+    assert e["num_levels"] == len(op.level_req_start) - 1
+    assert e["level_req_start"].tolist() == op.level_req_start
+    assert (e["tile_q"], e["total_work"], e["chunk_limit"], e["num_slots"]) == \
+           (op.tile_q, op.total_work, op.chunk_limit, op.num_slots)
+    assert e["tiles"][:, :4].tolist() == [[t.req, t.row_start, t.row_end, t.vis] for t in op.tiles]
+    assert e["items"].tolist() == [[it.req, it.tile, it.row_start, it.row_end, it.kv_start, it.kv_len, it.worker,
+                                    it.slot] for it in op.items]
+    qp, qi = e["queue_ptr"], e["queue_items"]
+    assert [qi[qp[w]:qp[w + 1]].tolist() for w in range(op.num_workers)] == op.queues
+    assert e["worker_cost"].tolist() == op.worker_cost
+    mp = e["merge_ptr"]
+    assert e["merge_tiles"].tolist() == list(range(len(op.units)))
+    got = [list(zip(e["merge_slots"][mp[k]:mp[k + 1]].tolist(), e["merge_row_off"][mp[k]:mp[k + 1]].tolist()))
+           for k in range(len(mp) - 1)]
+    assert got == [list(u) for u in op.units]
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_composable_plans_bit_exact(seed):
+    rng = np.random.default_rng(100 + seed)
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    Hk = int(rng.choice([1, 2, 8]))
+    nq = int(rng.integers(1, 40))
+    levels = []
+    for _ in range(int(rng.integers(1, 4))):
+        # a random grouping of the nq queries into block rows (some possibly empty)
+        cuts = np.sort(rng.integers(0, nq + 1, size=int(rng.integers(0, 6))))
+        qo = np.diff(np.concatenate([[0], cuts, [nq]]))
+        kv = rng.integers(0, 3000, size=len(qo))
+        kv[rng.random(len(qo)) < 0.15] = 0
+        levels.append((kv, None if (rng.random() < 0.3 and np.all(qo == 1)) else qo))
+    if rng.random() < 0.5:
+        levels.append((rng.integers(0, 900, size=nq), None))  # private rows, one query each
+    C_ = int(rng.integers(1, 300))
+    lp, op = _composable_lib_and_oracle(levels, Hk * g, Hk, C_, P=int(rng.choice([1, 4, 16])), seed=seed)
+    _assert_composable_same(lp, op)
+
+
+def test_composable_shared_prefix_plan_bit_exact():
+    """The composable shared-prefix workload: 16 groups of 4 sharing a 2048-token prefix, private
+    suffixes U[128, 1024], at 256 workers."""
+    b = I.shared_prefix_decode(seed=0, poison=False)
+    levels = [(np.full(b.groups, b.prefix_len), np.full(b.groups, b.per_group)), (b.suffix_lens, None)]
+    lp, op = _composable_lib_and_oracle(levels, 32, 8, 256)
+    _assert_composable_same(lp, op)
+
+
+def test_composable_rejects_mismatched_levels():
+    base = dict(kv_indptr=[0, 1], kv_indices=[0], last_page_len=[3])
+    bad = [
+        [base, dict(kv_indptr=[0, 1, 2], kv_indices=[0, 1], last_page_len=[1, 1])],  # 1 query vs 2
+        [dict(base, qo_indptr=[0, 2]), dict(kv_indptr=[0, 1, 1], kv_indices=[1], last_page_len=[2, 0])],  # g = 3
+    ]
+    with pytest.raises(_lib.BsrError):
+        api.ComposablePlan(bad[0], num_pages=4, num_qo_heads=4, num_kv_heads=1, head_dim=128, page_size=4)
+    with pytest.raises(_lib.BsrError):
+        api.ComposablePlan(bad[1], num_pages=4, num_qo_heads=3, num_kv_heads=1, head_dim=128, page_size=4)

@@ -192,3 +192,46 @@ def test_prefill_lpt_golden_rejects_wrong_cost(variant, monkeypatch):
         tp = lambda it, g: qo[it.req]  # noqa: E731
     g, p = _prefill_hand_plan(tp, monkeypatch)
     assert not _matches_prefill_golden(g, p), variant
+
+
+def test_composable_plan_single_level_is_the_plain_schedule():
+    """One level: the same tiles, chunks, queues and costs as make_plan (non-causal, 16-row tiles);
+    only every chunk takes a slot, and each query's list is its tile's chunks in KV order."""
+    kv, qo = [70, 0, 300, 33], [5, 2, 9, 1]
+    cp = PL.make_composable_plan([(kv, qo)], 8, 2, 5)
+    p = PL.make_plan(kv, qo, 8, 2, 5, tile_q=16)
+    assert [(t.req, t.row_start, t.row_end, t.vis) for t in cp.tiles] == \
+           [(t.req, t.row_start, t.row_end, t.vis) for t in p.tiles]
+    assert [(it.tile, it.kv_start, it.kv_len, it.worker) for it in cp.items] == \
+           [(it.tile, it.kv_start, it.kv_len, it.worker) for it in p.items]
+    assert cp.queues == p.queues and cp.worker_cost == p.worker_cost
+    assert sorted(it.slot for it in cp.items) == list(range(len(cp.items)))
+    # g = 4; queries 0-4 are request 0, 5-6 request 1 (no keys), 7-15 request 2, 16 request 3.
+    # Query 8 = request 2, position 1: rows 4..7 of request 2's first tile
+    t = next(t for t in cp.tiles if t.req == 2 and t.row_start == 0)
+    assert [r for _, r in cp.units[8]] == [4] * len(t.items)
+    assert [s for s, _ in cp.units[8]] == [cp.items[m].slot for m in sorted(t.items, key=lambda m: cp.items[m].kv_start)]
+    # query 11 = request 2, position 4: rows 16..19 = row 0 of request 2's second tile
+    t2 = next(t for t in cp.tiles if t.req == 2 and t.row_start == 16)
+    assert [r for _, r in cp.units[11]] == [0] * len(t2.items)
+    assert cp.units[5] == [] and cp.units[6] == []  # request 1 has no keys
+
+
+def test_composable_plan_by_hand():
+    """Two levels over 4 queries (g = 2): level 0 is one block row of all 4 queries over 6 keys,
+    level 1 one row per query over 2, 0, 5 and 1 keys; 3 workers."""
+    cp = PL.make_composable_plan([([6], [4]), ([2, 0, 5, 1], None)], 4, 2, 3, alpha=2, beta=1)
+    # tiles: level 0 one tile of 8 rows (vis 6); level 1 four tiles of 2 rows (vis 2, 0, 5, 1)
+    assert [(t.req, t.row_start, t.row_end, t.vis) for t in cp.tiles] == \
+           [(0, 0, 8, 6), (1, 0, 2, 2), (2, 0, 2, 0), (3, 0, 2, 5), (4, 0, 2, 1)]
+    # W = 6 + (2 + 0 + 5 + 1) = 14, L = ceil(14 / 3) = 5
+    assert (cp.total_work, cp.chunk_limit) == (14, 5)
+    # chunks: m0 t0 [0,5), m1 t0 [5,6), m2 t1 [0,2), m3 t3 [0,5), m4 t4 [0,1)
+    assert [(it.tile, it.kv_start, it.kv_len) for it in cp.items] == [(0, 0, 5), (0, 5, 1), (1, 0, 2), (3, 0, 5), (4, 0, 1)]
+    # sorted: m0 (5), m3 (5), m2 (2), m1 (1), m4 (1); costs 2 * positions + length: m0 2*4+5 = 13,
+    # m3 2*1+5 = 7, m2 2+2 = 4, m1 8+1 = 9, m4 2+1 = 3
+    # heap: m0 -> w0 (13), m3 -> w1 (7), m2 -> w2 (4), m1 -> w2 (13), m4 -> w1 (10)
+    assert cp.queues == [[0], [3, 4], [2, 1]] and cp.worker_cost == [13, 10, 13]
+    assert [it.slot for it in cp.items] == [0, 3, 2, 1, 4]
+    # query 0: level 0 rows 0..1 (slots of m0, m1 in KV order, offset 0), level 1 request 0 (m2)
+    assert cp.units == [[(0, 0), (3, 0), (2, 0)], [(0, 2), (3, 2)], [(0, 4), (3, 4), (1, 0)], [(0, 6), (3, 6), (4, 0)]]
