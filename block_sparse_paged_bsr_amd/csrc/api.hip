@@ -97,6 +97,9 @@ RunArgs make_args(const bsr_plan* p, const void* ws) {
   a.merge = reinterpret_cast<const MergeRec*>(base + p->ws.merge);
   a.mslots = reinterpret_cast<const int32_t*>(base + p->ws.mslots);
   a.mroff = reinterpret_cast<const int32_t*>(base + p->ws.mroff);
+  a.lpt = reinterpret_cast<const int32_t*>(base + p->ws.lpt);
+  a.tickets = reinterpret_cast<int32_t*>(const_cast<char*>(base) + p->ws.tickets);
+  a.num_items = int32_t(p->items.size() / 8);
   a.part_o = reinterpret_cast<float*>(const_cast<char*>(base) + p->ws.part_o);
   a.part_lse = reinterpret_cast<float*>(const_cast<char*>(base) + p->ws.part_lse);
   a.B = p->B;

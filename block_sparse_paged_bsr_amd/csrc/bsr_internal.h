@@ -53,9 +53,14 @@ struct MergeRec {
 };
 static_assert(sizeof(MergeRec) == 32, "MergeRec layout");
 
+// Ticket counters in a workspace: one pair per group of workgroups that draw from the LPT list.
+constexpr int kTicketGroups = 64;
+
 // Byte offsets of the workspace sections (all 256-byte aligned).
 struct WsLayout {
   size_t req = 0, indices = 0, items = 0, qptr = 0, merge = 0, mslots = 0, mroff = 0;
+  size_t lpt = 0;      // [num_items]: position in `items` of the t-th item in the plan's LPT order
+  size_t tickets = 0;  // [kTicketGroups][2]: next ticket, finished workgroups (zero between calls)
   size_t meta_bytes = 0;  // end of metadata
   size_t part_o = 0, part_lse = 0;
   size_t total = 0;

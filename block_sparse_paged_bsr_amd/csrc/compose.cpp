@@ -234,6 +234,8 @@ int build_composable_plan(const bsr_plan_desc* levels, int32_t n_levels, int32_t
   L.merge = off;    off = al256(off + sizeof(MergeRec) * std::max(NM, 1));
   L.mslots = off;   off = al256(off + sizeof(int32_t) * std::max<size_t>(p->merge_slots.size(), 1));
   L.mroff = off;    off = al256(off + sizeof(int32_t) * std::max<size_t>(p->merge_roff.size(), 1));
+  L.lpt = off;      off = al256(off + sizeof(int32_t) * std::max(M, 1));
+  L.tickets = off;  off = al256(off + sizeof(int32_t) * 2 * kTicketGroups);
   L.meta_bytes = off;
   const size_t rows_per_slot = size_t(p->Hk) * p->Tq;
   L.part_o = off;   off = al256(off + sizeof(float) * rows_per_slot * p->d * p->num_slots);
@@ -258,6 +260,13 @@ int build_composable_plan(const bsr_plan_desc* levels, int32_t n_levels, int32_t
     qi[k] = ItemRec{it.req, it.r0, it.r1, it.ks, it.ks + it.kl, it.slot, req[it.req].q_start, req[it.req].page_start};
   }
   std::memcpy(p->meta.data() + L.qptr, p->queue_ptr.data(), sizeof(int32_t) * (p->C + 1));
+  // the items in the partition's LPT order (longest first), as positions in the queue-ordered list
+  {
+    std::vector<int32_t> pos(M);
+    for (int32_t k = 0; k < M; ++k) pos[p->queue_items[k]] = k;
+    auto* lpt = reinterpret_cast<int32_t*>(p->meta.data() + L.lpt);
+    for (int32_t t = 0; t < M; ++t) lpt[t] = pos[order[t]];
+  }
   auto* mr = reinterpret_cast<MergeRec*>(p->meta.data() + L.merge);
   for (int32_t k = 0; k < NM; ++k)
     mr[k] = MergeRec{p->merge_tiles[k], 0, g, p->merge_ptr[k], p->merge_ptr[k + 1] - p->merge_ptr[k], 1, {0, 0}};

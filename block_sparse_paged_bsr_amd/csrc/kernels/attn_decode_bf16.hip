@@ -33,6 +33,9 @@
 // scale is folded into the score scale and the V scale into the output normalisation, so the
 // loop does no extra multiplications; the bytes read per token are half of bf16's, and a step
 // covers 32 tokens (two 16-token halves loaded together) to keep a bf16 step's bytes in flight.
+#include <algorithm>
+#include <climits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -64,9 +67,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
   constexpr int PD = KV8 ? 2 : 1;  // 16-token halves per step (E4M3 rows are half as long)
   extern __shared__ __attribute__((aligned(16))) uint16_t decode_lds[];
 
+  __shared__ int s_ticket;
   const int wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
-  const int w = blockIdx.x, hk = blockIdx.y * waves + wave;
-  if (hk >= a.Hk) return;  // (no workgroup barrier below: every wave runs on its own)
+  const int hk = blockIdx.y * waves + wave;  // (waves divides H_kv: every wave has a head)
   // the wave's private V tile; LDS operations of one wave complete in order, so staging and the
   // transposing reads need no barrier
   uint16_t* Vs = decode_lds + wave * (16 * VS);
@@ -106,21 +109,41 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
     return a.indices[itm.page_start + (a.p_shift >= 0 ? (tc >> a.p_shift) : tc / a.P)];
   };
 
+  // Work distribution: the plan's items in its LPT order (longest first), taken by whichever
+  // workgroup is free through a ticket counter -- the order of the longest-processing-time
+  // partition, without binding an item to a worker in advance, so that compute units running at
+  // different clocks finish together.  Every item writes its own output or partial slot and the
+  // merge folds slots in the plan's order, so the results do not depend on which workgroup ran
+  // which item.  All waves of a workgroup (one per KV head) take the same item.  The last
+  // workgroup to find the list exhausted returns the counters to zero for the next call.
   // The work item record carries everything this kernel needs (rows, KV range, slot, query and
-  // page-list starts).  The next item's record is fetched when an item starts, and its queries and
-  // first page ids during the item's last step, so that a new item starts with only its first
-  // rows to wait for.
+  // page-list starts).  The next item is claimed and its record fetched in the second-to-last step
+  // of the current one, and its queries and first page ids issued in the last step, so that a new
+  // item starts with only its first rows to wait for.
+  int32_t* tk = a.tickets + 2 * blockIdx.y;
+  auto draw = [&]() -> int {
+    if (threadIdx.x == 0) s_ticket = __hip_atomic_fetch_add(tk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int t = s_ticket;
+    __syncthreads();  // every wave has read it before the next draw writes it
+    return t;
+  };
   constexpr int NPRE = KV8 ? 4 : 2;  // page ids of the first two steps (16 tokens each)
-  const int it_end = a.qptr[w + 1];
-  int it = a.qptr[w];
-  ItemRec next = a.items[it < it_end ? it : 0];
+  const int num_items = a.num_items;
+  int t = draw();
+  ItemRec next = a.items[a.lpt[t < num_items ? t : 0]];
   bf16x8 qb[KB], qn[KB];
   int32_t pre[NPRE];
   bool have_pre = false;
-  for (; it < it_end; ++it) {
+  while (t < num_items) {
     const ItemRec item = next;
-    if (it + 1 < it_end) next = a.items[it + 1];
-    const bool more = it + 1 < it_end;
+    bool claimed = false, more = false;
+    auto claim = [&]() {  // every wave of the workgroup reaches this at the same step of the item
+      t = draw();
+      more = t < num_items;
+      if (more) next = a.items[a.lpt[t]];
+      claimed = true;
+    };
     const int kv_end = item.kv_end;
     const int64_t orow = out_row(item);
     if (have_pre) {
@@ -241,7 +264,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
         // page ids) before touching this step's data
         u32x4 kn[NL], vn[NL];
         if (has_next) load_rows(kn, vn, t0 + 16 + n, pg_next);
-        else preload_next();
+        if (!claimed && t0 + 32 >= kv_end) claim();
+        if (!has_next) preload_next();
         pg_next = pg_after;
         compute(t0, kr, vr);
         if (has_next) {
@@ -266,6 +290,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
         u32x4 kn[2][NL], vn[2][NL];
         load_rows(kn[0], vn[0], t0 + 32 + n, pg_next0);
         load_rows(kn[1], vn[1], t0 + 48 + n, pg_next1);
+        if (!claimed && t0 + 64 >= kv_end) claim();
         if (!has_next) preload_next();
         compute(t0, kr[0], vr[0]);
         if (t0 + 16 < kv_end) compute(t0 + 16, kr[1], vr[1]);
@@ -282,6 +307,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
       }
     }
 
+    if (!claimed) claim();  // (an item always reaches its last step; kept for safety)
     // lane (n, j) summed tokens 4j..4j+3 of every step; add the four token groups
     l += shfl_xor(l, 16);
     l += shfl_xor(l, 32);
@@ -306,6 +332,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
       }
     }
   }
+  if (threadIdx.x == 0) {
+    const int done = __hip_atomic_fetch_add(tk + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == int(gridDim.x) - 1) {  // every workgroup has drawn its last ticket
+      __hip_atomic_store(tk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(tk + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 bool decode_bf16_supported(int d, int g, int Tq) {
@@ -314,7 +347,13 @@ bool decode_bf16_supported(int d, int g, int Tq) {
 
 bool decode_bf16_tiles(int d, int g, int Tq) { return (d == 64 || d == 128) && g >= 1 && Tq <= 16; }
 
-int decode_bf16_waves_per_block(int Hk) { return Hk < kDecodeWaves ? Hk : kDecodeWaves; }
+// waves per workgroup: the largest divisor of H_kv up to kDecodeWaves, so that every wave of a
+// workgroup has a KV head (they all join the ticket barriers)
+int decode_bf16_waves_per_block(int Hk) {
+  for (int wv = kDecodeWaves; wv > 1; --wv)
+    if (Hk % wv == 0) return wv;
+  return 1;
+}
 
 int decode_bf16_blocks_per_worker(int Hk) {
   const int wv = decode_bf16_waves_per_block(Hk);
@@ -341,9 +380,24 @@ static void launch_cap(const RunArgs& a, dim3 grid, int waves, hipStream_t s) {
   else hipLaunchKernelGGL((attn_decode_bf16_kernel<D, false, KV8>), grid, dim3(64 * waves), lds, s, a);
 }
 
+// Workgroups that stay resident together on the current device (per head group); items are taken
+// from the ticket list, so the grid needs no more workgroups than that, whatever the plan's C.
+static int decode_resident_blocks(int d, int Hk) {
+  static int cached[2][65] = {};
+  const int di = d == 64 ? 0 : 1, hi = Hk < 64 ? Hk : 64;
+  if (!cached[di][hi]) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return INT32_MAX;
+    cached[di][hi] = cus * decode_bf16_blocks_per_cu(d, Hk);
+  }
+  return cached[di][hi];
+}
+
 hipError_t launch_decode_bf16(const RunArgs& a, bool kv_e4m3, hipStream_t s) {
   const int waves = decode_bf16_waves_per_block(a.Hk);
-  const dim3 grid(a.C, decode_bf16_blocks_per_worker(a.Hk));
+  const dim3 grid(std::min(a.C, decode_resident_blocks(a.d, a.Hk)), decode_bf16_blocks_per_worker(a.Hk));
   if (a.d == 64 && kv_e4m3) launch_cap<64, true>(a, grid, waves, s);
   else if (a.d == 64) launch_cap<64, false>(a, grid, waves, s);
   else if (a.d == 128 && kv_e4m3) launch_cap<128, true>(a, grid, waves, s);

@@ -28,6 +28,9 @@ struct RunArgs {
   const MergeRec* merge;
   const int32_t* mslots;
   const int32_t* mroff;  // partial-row offset per merge slot (records with has_roff)
+  const int32_t* lpt;    // items in the plan's LPT order, as positions in `items`
+  int32_t* tickets;      // per workgroup group: next ticket, finished workgroups (zero between calls)
+  int32_t num_items;
   float* part_o;
   float* part_lse;
   const void* q;

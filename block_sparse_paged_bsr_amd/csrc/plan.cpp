@@ -275,6 +275,8 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
   L.merge = off;    off = align256(off + sizeof(MergeRec) * std::max(NM, 1));
   L.mslots = off;   off = align256(off + sizeof(int32_t) * std::max<size_t>(p->merge_slots.size(), 1));
   L.mroff = off;    off = align256(off + sizeof(int32_t));  // (no row offsets in a single-level plan)
+  L.lpt = off;      off = align256(off + sizeof(int32_t) * std::max(M, 1));
+  L.tickets = off;  off = align256(off + sizeof(int32_t) * 2 * kTicketGroups);
   L.meta_bytes = off;
   const size_t rows_per_slot = size_t(p->Hk) * Tq;
   L.part_o = off;   off = align256(off + sizeof(float) * rows_per_slot * p->d * p->num_slots);
@@ -303,6 +305,13 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
     qi[k] = ItemRec{it.req, it.r0, it.r1, it.ks, it.ks + it.kl, it.slot, req[it.req].q_start, req[it.req].page_start};
   }
   std::memcpy(p->meta.data() + L.qptr, p->queue_ptr.data(), sizeof(int32_t) * (p->C + 1));
+  // the items in the partition's LPT order (longest first), as positions in the queue-ordered list
+  {
+    std::vector<int32_t> pos(M);
+    for (int32_t k = 0; k < M; ++k) pos[p->queue_items[k]] = k;
+    auto* lpt = reinterpret_cast<int32_t*>(p->meta.data() + L.lpt);
+    for (int32_t t = 0; t < M; ++t) lpt[t] = pos[order[t]];
+  }
   auto* mr = reinterpret_cast<MergeRec*>(p->meta.data() + L.merge);
   for (int32_t k = 0; k < NM; ++k) {
     const int32_t* tr = &p->tiles[5 * p->merge_tiles[k]];
