@@ -1,9 +1,9 @@
 """Benchmark of the block-sparse paged attention path on one MI355X.
 
 One step = one bsr_run_decode call on the batch-64 paged decode workload (bf16,
-KV lengths U[512, 8192], page size 16, 32 query / 8 KV heads, head_dim 128): the
-attention kernel over the planned split-KV partition plus the merge of the partial
-states.  The plan is built once and reused by every step (one plan per generation
+KV lengths U[512, 8192], page size 16, 32 query / 8 KV heads, head_dim 128): one launch
+of the attention kernel over the planned split-KV partition, which also folds the split
+requests' partial states.  The plan is built once and reused by every step (one plan per generation
 step serves all layers).  Inputs are resident in HBM before timing; three copies of
 the KV pool are rotated so the last-level cache cannot serve a step from the previous
 one.  The same JSON line also reports
@@ -16,13 +16,17 @@ one.  The same JSON line also reports
   - a three-level cascade, and one prefix shared by a whole batch (batch 64 with a
     32,768-token prefix, batch 16 with 1,024; 128-token suffixes) composed and single-level,
   - the attention variants (soft cap, sliding window, tree masks) and E4M3 KV decode,
-  - the roofline of the decode call (its two launches timed together with HIP events over the
-    timed region, on the stream they run on) and of the prefill kernel, with per-kernel averages
-    and HBM counters from the committed rocprofv3 summaries while the kernel sources match,
+  - the roofline of the decode call (timed with HIP events over the timed region, on the stream
+    it runs on), next to the streaming-read ceiling of the same pages (libbsr_probe.so, measured
+    in the run), and of the prefill kernel, with per-kernel averages and HBM counters from the
+    committed rocprofv3 summaries while the kernel sources match,
   - the fp64 CPU oracle timed on the host cores as a baseline, for decode and for prefill.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--only NAME]
                        [--copy-calib]
+       python bench.py --profile-commands NAME   (the rocprofv3 runs behind profiles/NAME.*)
+       python bench.py --profile-case NAME       (one case's calls only, run under rocprofv3)
+       python bench.py --summarize NAME          (profiles/NAME.json and .md from their output)
 """
 from __future__ import annotations
 
@@ -140,8 +144,45 @@ def run_case(b, kind, steps, warmup, rotate=1, causal=False, **variant):
     res = {"ms": ms, "plan_us": plan_us, "upload_us": upload_us, "meta_bytes": int(p.workspace_bytes()),
            "num_workers": e["num_workers"],
            "items": int(e["items"].shape[0]), "slots": e["num_slots"], "step": step,
-           "out": (o, lse)}
+           "out": (o, lse), "pools": pools}
     return res
+
+
+def read_ceiling(pools, pages, steps, warmup, per_cu=(2, 4, 8, 16)):
+    """Streaming-read ceiling of the decode access shape on this device: libbsr_probe.so reads the
+    pages the call reads (every listed page of K and of V, in page-table order, whole pages, the
+    same rotated pools) and does nothing else with them.  Best of a few grid sizes, timed like the
+    call (events around back-to-back launches on the stream they run on)."""
+    import ctypes
+    import torch
+    from block_sparse_paged_bsr_amd import _lib
+
+    L = _lib.probe()
+    k0 = pools[0][0]
+    page_bytes = k0[0].numel() * k0.element_size()
+    pg = torch.from_numpy(np.ascontiguousarray(pages, dtype=np.int32)).to("cuda")
+    assert int(pg.min()) >= 0 and int(pg.max()) < k0.shape[0]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    best = None
+    for n in per_cu:
+        grid = cus * n
+        sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+
+        def step(s, grid=grid, sink=sink):
+            kk, vv = pools[s % len(pools)]
+            rc = L.bsr_probe_read_pages(ctypes.c_void_p(kk.data_ptr()), ctypes.c_void_p(vv.data_ptr()),
+                                        ctypes.c_void_p(pg.data_ptr()), int(pg.numel()), page_bytes, grid,
+                                        0x9E3779B9, ctypes.c_void_p(sink.data_ptr()),
+                                        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            assert rc == 0, rc
+
+        ms = time_calls(step, steps, warmup)
+        nbytes = 2 * int(pg.numel()) * page_bytes
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = {"gbs": round(gbs, 1), "us": round(ms * 1e3, 2), "grid": grid, "bytes": nbytes}
+    best["kernel"] = "bsr_probe_read_pages (libbsr_probe.so)"
+    return best
 
 
 def graph_replay_ms(step, steps, warmup, variants=3):
@@ -174,8 +215,9 @@ def bench_decode(args):
     med, mn, p90 = per_call_ms(r["step"], 50 if not args.quick else 10)
     graph_ms = graph_replay_ms(r["step"], args.steps, args.warmup)
     nbytes = decode_bytes(b.kv_lens, b.batch, len(b.kv_indices))
+    ceiling = read_ceiling(r.pop("pools"), b.kv_indices, args.steps, args.warmup)
     r.update({"gbs": nbytes / (r["ms"] * 1e-3) / 1e9, "bytes": nbytes, "median_ms": med, "min_ms": mn,
-              "p90_ms": p90, "graph_ms": graph_ms,
+              "p90_ms": p90, "graph_ms": graph_ms, "read_ceiling": ceiling,
               "tokens": int(b.kv_lens.sum()), "batch": b})
     return r
 
@@ -492,6 +534,259 @@ def copy_calibration():
     log(f"copy calibration: 3 x {n} bytes")
 
 
+# ---- rocprofv3 summaries (profiles/<name>.json, .md) ----
+# Each case runs one call of the path, warm-up and timed steps only, so that the kernel-trace
+# averages and the counters of its kernels belong to that call alone.
+SRC = "block_sparse_paged_bsr_amd/csrc/kernels/"
+PROFILE_CASES = {
+    "decode_batch64": {
+        "workload": "batched paged decode bf16: batch 64, KV lengths U[512,8192], page size 16, 32 query / "
+                    "8 KV heads, head_dim 128 (seed 0)",
+        "kernels": {"attn_decode_bf16_kernel": "attention, split requests folded in the kernel (the whole call)",
+                    "read_pages_kernel": "HBM read probe: the same K/V pages, page-table order, nothing else"},
+        "call": ["attn_decode_bf16_kernel"],
+        "sources": [SRC + "attn_decode_bf16.hip", SRC + "common.h", "block_sparse_paged_bsr_amd/csrc/hbm_probe.hip"],
+        "unit": "bytes"},
+    "prefill_ragged": {
+        "workload": "ragged causal prefill bf16: batch 16, q_len = kv_len U[256,4096], page size 16, 32 query / "
+                    "8 KV heads, head_dim 128 (seed 0)",
+        "kernels": {"attn_prefill128_bf16_kernel": "attention, 128-row query tiles"},
+        "call": ["attn_prefill128_bf16_kernel"],
+        "sources": [SRC + "attn_prefill_bf16.hip", SRC + "common.h"],
+        "unit": "flops", "sq": True},
+    "composable_shared_prefix": {
+        "workload": "composable shared-prefix decode bf16: 16 groups x 4 requests, 2048-token prefix per group, "
+                    "private suffixes U[128,1024], page size 16, 32/8 heads, head_dim 128 (seed 0), one plan",
+        "kernels": {"attn_decode_bf16_kernel": "attention over both levels' 16-row tiles",
+                    "merge_partials_kernel": "fold of each query's states over chunks and levels"},
+        "call": ["attn_decode_bf16_kernel", "merge_partials_kernel"],
+        "sources": [SRC + "attn_decode_bf16.hip", SRC + "merge.hip", SRC + "common.h",
+                    "block_sparse_paged_bsr_amd/csrc/compose.cpp"],
+        "unit": "bytes"},
+    "decode_page1": {
+        "workload": "batched paged decode bf16 at page size 1: the batch-64 decode's tokens scattered one per "
+                    "page over a 2^20-row pool (seed 0)",
+        "kernels": {"attn_decode_bf16_kernel": "attention, split requests folded in the kernel (the whole call)"},
+        "call": ["attn_decode_bf16_kernel"],
+        "sources": [SRC + "attn_decode_bf16.hip", SRC + "common.h"],
+        "unit": "bytes"},
+}
+SQ_COUNTERS = ("GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS "
+               "SQ_WAVE_CYCLES SQ_WAIT_INST_ANY")
+PROFILE_STEPS = "--steps 20 --warmup 5"
+
+
+def profile_commands(name):
+    """The rocprofv3 runs behind profiles/<name>.json, from the repository root: a kernel trace,
+    then FETCH_SIZE and WRITE_SIZE passes (each with the copy calibration) for the HBM-bound
+    cases, SQ counters for prefill."""
+    case = PROFILE_CASES[name]
+    run = f"python3 bench.py --profile-case {name} {PROFILE_STEPS}"
+    d = f"gpurun_out/prof/{name}"
+    cmds = [f"timeout -s KILL 300 rocprofv3 --kernel-trace --stats --output-format csv -d {d}_trace -o run -- {run} "
+            f"--profile-out {d}_event.json"]
+    if case["unit"] == "bytes":
+        cmds += [f"timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}_fetch -o run -- {run} "
+                 "--copy-calib",
+                 f"timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}_write -o run -- {run} "
+                 "--copy-calib"]
+    if case.get("sq"):
+        cmds.append(f"timeout -s KILL 300 rocprofv3 --pmc {SQ_COUNTERS} --output-format csv -d {d}_sq -o run -- {run}")
+    return cmds
+
+
+def profile_case_batch(name):
+    import workloads as inputs
+
+    if name == "decode_batch64":
+        return inputs.batched_decode_bf16(seed=0, poison=False)
+    if name == "prefill_ragged":
+        return inputs.ragged_prefill_bf16(seed=0, poison=False)
+    if name == "composable_shared_prefix":
+        return inputs.shared_prefix_decode(seed=0, poison=False)
+    if name == "decode_page1":
+        return inputs.vector_sparse_pair(0, inputs.decode_lengths(0), pool_rows=1 << 20)[0]
+    raise KeyError(name)
+
+
+def profile_algorithmic(name, b):
+    """Algorithmic bytes (or flops) of one call of the case."""
+    if name in ("decode_batch64", "decode_page1"):
+        return decode_bytes(b.kv_lens, b.batch, len(b.kv_indices))
+    if name == "prefill_ragged":
+        return prefill_flops(b.kv_lens)
+    per = H_KV * D * 2 * 2  # K and V of one token, all KV heads
+    R = int(b.q_f32.shape[0])  # one query per request
+    return b.groups * b.prefix_len * per + int(b.suffix_lens.sum()) * per + 2 * R * H_QO * D * 2 + R * H_QO * 4
+
+
+def run_profile_case(name, args):
+    """Warm-up and timed calls of one case and nothing else (plus the read probe for decode)."""
+    import torch
+    from block_sparse_paged_bsr_amd import api
+
+    b = profile_case_batch(name)
+    if name == "composable_shared_prefix":
+        q, k, v = b.torch_values("cuda")
+        cp = api.ComposablePlan([dict(kv_indptr=b.l1_kv_indptr, kv_indices=b.l1_kv_indices,
+                                      last_page_len=b.l1_last_page_len, qo_indptr=b.l1_qo_indptr),
+                                 dict(kv_indptr=b.l2_kv_indptr, kv_indices=b.l2_kv_indices,
+                                      last_page_len=b.l2_last_page_len)],
+                                num_pages=b.num_pages, num_qo_heads=H_QO, num_kv_heads=H_KV, head_dim=D,
+                                page_size=b.page_size, num_workers=api.query_num_workers("decode", H_QO, H_KV, D))
+        wc = api.alloc_workspace(cp)
+        cp.upload(wc)
+        o, l = torch.empty_like(q), torch.empty(q.shape[0], H_QO, dtype=torch.float32, device="cuda")
+        pools = [(k, v)] + [(k.clone(), v.clone()) for _ in range(2)]
+
+        def step(s):
+            kk, vv = pools[s % 3]
+            api.run_prefill(cp, wc, q, kk, vv, o=o, lse=l, sm_scale=SM)
+
+        ms = time_calls(step, args.steps, args.warmup)
+    elif name == "prefill_ragged":
+        ms = run_case(b, "prefill", args.steps, args.warmup, causal=True)["ms"]
+    else:
+        r = run_case(b, "decode", args.steps, args.warmup, rotate=3 if name == "decode_batch64" else 1)
+        ms = r["ms"]
+        if name == "decode_batch64":
+            log(f"read probe: {read_ceiling(r['pools'], b.kv_indices, args.steps, args.warmup, per_cu=(8,))}")
+    log(f"{name}: {ms * 1e3:.2f} us per call")
+    # the event-timed call average of this run, next to the trace (the summary compares the two)
+    if args.profile_out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.profile_out)), exist_ok=True)
+        with open(args.profile_out, "w") as f:
+            json.dump({"event_timed_us_per_call": round(ms * 1e3, 2), "steps": args.steps, "warmup": args.warmup}, f)
+
+
+def summarize_profile(name):
+    """profiles/<name>.json and .md from the rocprofv3 output of profile_commands(name)."""
+    import csv
+    import hashlib
+
+    case = PROFILE_CASES[name]
+    d = os.path.join(ROOT, "gpurun_out", "prof", name)
+    rows = list(csv.DictReader(open(os.path.join(d + "_trace", "run_kernel_stats.csv"))))
+    disp = list(csv.DictReader(open(os.path.join(d + "_trace", "run_kernel_trace.csv"))))
+    warm = int(PROFILE_STEPS.split("--warmup ")[1].split()[0])
+    kav, kall = {}, {}
+    md_rows = []
+    for key, what in case["kernels"].items():
+        hit = [r for r in rows if key in r["Name"]]
+        assert len(hit) == 1, (key, [r["Name"] for r in hit])
+        r = hit[0]
+        # the timed calls only: the dispatches after the warm-up ones, in dispatch order
+        durs = [(int(x["Dispatch_Id"]), (int(x["End_Timestamp"]) - int(x["Start_Timestamp"])) / 1e3)
+                for x in disp if key in x["Kernel_Name"]]
+        durs = [u for _, u in sorted(durs)][warm:]
+        kav[key] = round(sum(durs) / len(durs), 2)
+        kall[key] = round(float(r["AverageNs"]) / 1e3, 2)
+        md_rows.append(f"| `{r['Name'].replace('void ', '').replace('(bsr::RunArgs)', '')}` | {what} | {r['Calls']} | "
+                       f"{float(r['AverageNs']) / 1e3:,.2f} | {kav[key]:,.2f} | {float(r['MinNs']) / 1e3:,.2f} | "
+                       f"{float(r['MaxNs']) / 1e3:,.2f} |")
+
+    def counters(tag, counter):
+        rs = [r for r in csv.DictReader(open(os.path.join(d + "_" + tag, "run_counter_collection.csv")))
+              if r["Counter_Name"] == counter]
+        per = {}
+        for r in rs:
+            per.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], 0.0])[1] += float(r["Counter_Value"])
+        disp = sorted(per.items())
+        calib = [v for _, (n, v) in disp if "copyBuffer" in n][:3]
+        assert len(calib) == 3, "copy calibration dispatches missing"
+        scale = 524288.0 / (sum(calib) / 3)
+        out = {}
+        for key in case["kernels"]:
+            vals = [v for _, (n, v) in disp if key in n]
+            out[key] = (sum(vals) / len(vals), len(vals))
+        return scale, out
+
+    rec = {"name": name, "workload": case["workload"], "commands": profile_commands(name),
+           "sources": {p: hashlib.sha256(open(os.path.join(ROOT, p), "rb").read()).hexdigest()
+                       for p in case["sources"]},
+           "kernel_avg_us": kav, "kernel_avg_us_all_dispatches": kall}
+    ev = os.path.join(d + "_event.json")
+    if os.path.exists(ev):
+        rec["event_timed_us_per_call"] = json.load(open(ev))["event_timed_us_per_call"]
+    alg = profile_algorithmic(name, profile_case_batch(name))
+    rec["algorithmic_" + case["unit"] + "_per_call"] = alg
+    call_us = sum(kav[k] for k in case["call"])
+    rec["call_kernels_us"] = round(call_us, 2)
+    md = [f"# {name}: rocprofv3 summary", "", f"Workload: {case['workload']}.", "",
+          "Commands (from the repository root; library built in-tree; each pass in its own run):", ""]
+    md += ["    " + c for c in rec["commands"]]
+    md += ["", f"Kernel trace (`run_kernel_stats.csv` over all dispatches; `run_kernel_trace.csv` for the "
+           f"timed calls, i.e. the dispatches after the {warm} warm-up calls):", "",
+           "| Kernel | Role | Dispatches | Average, all (us) | Average, timed calls (us) | Min (us) | Max (us) |",
+           "|---|---|---|---|---|---|---|"]
+    md += md_rows
+    if "event_timed_us_per_call" in rec:
+        md += ["", f"The same traced run timed its calls with HIP events on their stream: "
+               f"{rec['event_timed_us_per_call']:.2f} us per call (the kernels of one call: "
+               f"{sum(kav[k] for k in case['call']):.2f} us in the trace).  Under the tracer every dispatch "
+               "runs somewhat slower than in an untraced run of bench.py."]
+    if case["unit"] == "bytes":
+        fs, fetch = counters("fetch", "FETCH_SIZE")
+        ws, write = counters("write", "WRITE_SIZE")
+        traffic = {k: int(round((fetch[k][0] * fs + write[k][0] * ws) * 1024)) for k in case["kernels"]}
+        rec.update({"fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+                    "fetch_kib_per_dispatch": {k: round(fetch[k][0], 1) for k in case["kernels"]},
+                    "write_kib_per_dispatch": {k: round(write[k][0], 1) for k in case["kernels"]},
+                    "traffic_bytes_per_dispatch": traffic,
+                    "traffic_bytes_per_call": sum(traffic[k] for k in case["call"])})
+        rec["traffic_over_algorithmic"] = round(rec["traffic_bytes_per_call"] / alg, 4)
+        rec["call_kernels_gbs"] = round(alg / (call_us * 1e-6) / 1e9, 1)
+        md += ["", "HBM counters per dispatch (FETCH_SIZE and WRITE_SIZE passes), scaled by what the same counters "
+               "read for the three 512 MiB device copies of `--copy-calib` (524,288 KiB read and written each): "
+               f"FETCH_SIZE x {fs:.4f}, WRITE_SIZE x {ws:.4f}.", "",
+               "| Kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes (scaled) |", "|---|---|---|---|"]
+        for k in case["kernels"]:
+            md.append(f"| `{k}` | {fetch[k][0]:,.1f} | {write[k][0]:,.1f} | {traffic[k]:,} |")
+        md += ["", f"Per call ({' + '.join(case['call'])}): {rec['traffic_bytes_per_call']:,} bytes of HBM traffic "
+               f"against {alg:,} algorithmic bytes (ratio {rec['traffic_over_algorithmic']:.4f}); the call's kernels "
+               f"take {call_us:.2f} us together = {rec['call_kernels_gbs']:,.1f} GB/s of algorithmic bytes "
+               f"({100 * rec['call_kernels_gbs'] / HBM_PEAK_GBS:.1f} % of 8 TB/s)."]
+        if "read_pages_kernel" in kav:
+            pb = traffic["read_pages_kernel"]
+            rec["read_probe_gbs"] = round(pb / (kav["read_pages_kernel"] * 1e-6) / 1e9, 1)
+            md += ["", f"Read probe: {pb:,} bytes counted per dispatch in {kav['read_pages_kernel']:.2f} us = "
+                   f"{rec['read_probe_gbs']:,.1f} GB/s, the streaming-read rate of this page-gather shape."]
+    else:
+        rs = list(csv.DictReader(open(os.path.join(d + "_sq", "run_counter_collection.csv"))))
+        key = case["call"][0]
+        per = {}
+        for r in rs:
+            if key in r["Kernel_Name"]:
+                per.setdefault(int(r["Dispatch_Id"]), {}).setdefault(r["Counter_Name"], 0.0)
+                per[int(r["Dispatch_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
+        names = SQ_COUNTERS.split()
+        mean = {c: sum(v[c] for v in per.values()) / len(per) for c in names}
+        simds, xcds = 1024, 8
+        busy = (mean["SQ_VALU_MFMA_BUSY_CYCLES"] / simds) / (mean["GRBM_GUI_ACTIVE"] / xcds)
+        rec.update({"sq_counters_mean_per_dispatch": {c: float(f"{mean[c]:.4g}") for c in names},
+                    "mfma_busy": round(busy, 4),
+                    "valu_per_mfma": round(mean["SQ_INSTS_VALU"] / mean["SQ_INSTS_MFMA"], 2),
+                    "lds_per_mfma": round(mean["SQ_INSTS_LDS"] / mean["SQ_INSTS_MFMA"], 2),
+                    "wait_inst_any_frac": round(mean["SQ_WAIT_INST_ANY"] / mean["SQ_WAVE_CYCLES"], 4)})
+        tf = alg / (kav[key] * 1e-6) / 1e12
+        rec["kernel_tflops"] = round(tf, 1)
+        md += ["", f"SQ counters, mean per dispatch over {len(per)} dispatches of `{key}`:", "",
+               "| Counter | Value |", "|---|---|"]
+        md += [f"| {c} | {mean[c]:.4g} |" for c in names]
+        md += ["", f"Matrix cores busy = (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs) / (GRBM_GUI_ACTIVE / 8 XCDs) = "
+               f"{100 * busy:.1f} %; vector instructions per matrix instruction {rec['valu_per_mfma']}; LDS "
+               f"instructions per matrix instruction {rec['lds_per_mfma']}; SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES = "
+               f"{100 * rec['wait_inst_any_frac']:.1f} %.", "",
+               f"Work per call: {alg:.4g} flops of unmasked QK^T + PV; at the trace's average "
+               f"{kav[key]:.1f} us the kernel runs at {tf:.1f} TFLOP/s ({100 * tf / BF16_PEAK_TFLOPS:.1f} % of "
+               f"2.5 PFLOP/s dense bf16)."]
+    md += ["", f"Kernel sources (SHA-256 in `{name}.json`; bench.py uses these figures only while they match): "
+           + ", ".join(f"`{p}`" for p in case["sources"]) + "."]
+    json.dump(rec, open(os.path.join(ROOT, "profiles", name + ".json"), "w"), indent=1)
+    open(os.path.join(ROOT, "profiles", name + ".md"), "w").write("\n".join(md) + "\n")
+    print(json.dumps(rec, indent=1))
+
+
 def bench_cascade(args):
     """Three BSR views (a prompt shared by all 64 requests, 16 group prefixes of 4, private
     suffixes) merged left to right, vs the single-level view over the same pages."""
@@ -677,7 +972,20 @@ def main():
                                        "variants", "e4m3"],
                     default=None)
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--profile-case", choices=sorted(PROFILE_CASES), default=None,
+                    help="run one case's calls only (for the rocprofv3 runs of profile_commands)")
+    ap.add_argument("--profile-out", default=None, help="with --profile-case: write the event-timed call average here")
+    ap.add_argument("--profile-commands", choices=sorted(PROFILE_CASES), default=None,
+                    help="print the rocprofv3 commands behind profiles/<name>.json")
+    ap.add_argument("--summarize", choices=sorted(PROFILE_CASES), default=None,
+                    help="write profiles/<name>.json and .md from gpurun_out/prof/<name>_* (no GPU)")
     args = ap.parse_args()
+    if args.profile_commands:
+        print("\n".join(profile_commands(args.profile_commands)))
+        return
+    if args.summarize:
+        summarize_profile(args.summarize)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: every GPU would run the same kernels on its own "
               "requests and KV heads, there is no cross-GPU step to time; use --gpus 1",
@@ -693,6 +1001,9 @@ def main():
     log(f"device: {device}")
     if args.copy_calib:
         copy_calibration()
+    if args.profile_case:
+        run_profile_case(args.profile_case, args)
+        return
     if args.only == "prefill":
         pf = bench_prefill(args)
         log(f"prefill: {pf['ms']*1e3:.1f} us, {pf['tflops']:.1f} TFLOP/s")
@@ -746,26 +1057,30 @@ def main():
             "device": device,
         },
     }
-    # Roofline of the decode call: one call = the attention kernel and the merge of the split
-    # requests' partial states, timed as a whole (events over the timed region, on the stream both
-    # kernels are launched on), so no per-kernel event overhead enters and no kernel can exceed its
-    # call.  The per-kernel split and the HBM counters come from the committed rocprofv3 summary
-    # (profiles/decode_batch64.json), reported only while the kernel sources are unchanged.
+    # Roofline of the decode call: one call = one launch of the attention kernel, which also folds
+    # the split requests' partial states, timed over the timed region with events on the stream it
+    # runs on (no per-launch events).  The kernel's rocprofv3 average and the HBM counters come
+    # from the committed summary (profiles/decode_batch64.json), reported only while the kernel
+    # sources are unchanged; the read ceiling is measured in this run.
     rec = profile_record("decode_batch64")
+    ceil = dec["read_ceiling"]
     out["roofline"] = {"bound": "hbm", "achieved": round(dec["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": round(dec["gbs"] / HBM_PEAK_GBS, 4),
                        "traffic": rec["traffic_bytes_per_call"] if rec else None,
-                       "kernel": "decode call: attn_decode_bf16_kernel<128, false, false> + "
-                                 "merge_partials_kernel<unsigned short>",
-                       "call_avg_us": round(dec["ms"] * 1e3, 2), "algorithmic_bytes": dec["bytes"]}
+                       # one launch: split requests are folded inside the attention kernel
+                       "kernel": "attn_decode_bf16_kernel<128, false, false>",
+                       "call_avg_us": round(dec["ms"] * 1e3, 2), "algorithmic_bytes": dec["bytes"],
+                       # the same pages read in the same order by a kernel that does nothing else
+                       "read_ceiling_gbs": ceil["gbs"], "read_ceiling": ceil,
+                       "frac_of_read_ceiling": round(dec["gbs"] / ceil["gbs"], 4)}
     if rec:
         kav = rec["kernel_avg_us"]
         out["roofline"].update({
-            "rocprof_kernel_avg_us": kav,
+            "rocprof_kernel_avg_us": kav["attn_decode_bf16_kernel"],
             "rocprof_attention_kernel_frac": round(dec["bytes"] / (kav["attn_decode_bf16_kernel"] * 1e-6) / 1e9
                                                    / HBM_PEAK_GBS, 4),
-            "traffic_over_algorithmic": round(rec["traffic_bytes_per_call"] / dec["bytes"], 4),
-            "streaming_read_ceiling_gbs": rec.get("streaming_read_ceiling_gbs")})
+            "traffic_over_algorithmic": rec["traffic_over_algorithmic"],
+            "rocprof_read_probe_gbs": rec.get("read_probe_gbs")})
     if not args.quick:
         del dec["step"], dec["out"]
         pf = bench_prefill(args)
@@ -783,7 +1098,9 @@ def main():
                                        "frac": round(pf["tflops"] / BF16_PEAK_TFLOPS, 4),
                                        "kernel": "attn_prefill128_bf16_kernel<128, 2, false>",
                                        "rocprof_kernel_avg_us": prec["kernel_avg_us"] if prec else None,
-                                       "mfma_busy": prec.get("mfma_busy") if prec else None}}
+                                       "rocprof_kernel_tflops": prec.get("kernel_tflops") if prec else None,
+                                       "mfma_busy": prec.get("mfma_busy") if prec else None,
+                                       "valu_per_mfma": prec.get("valu_per_mfma") if prec else None}}
         out["prefill"]["cpu_baseline"] = cpu_baseline_prefill(pf)
         torch.cuda.empty_cache()
         vs = bench_vector_sparse(args)

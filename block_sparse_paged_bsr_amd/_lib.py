@@ -9,6 +9,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbsr_attn.so")
+PROBE_PATH = os.path.join(HERE, "libbsr_probe.so")  # include/bsr_probe.h: HBM read probe
 
 BSR_OK = 0
 BSR_INVALID_ARG = -1
@@ -107,7 +108,29 @@ EXPORTED = [
     "bsr_version",
 ]
 
+PROBE_EXPORTED = ["bsr_probe_read_pages"]
+
 _lib = None
+_probe = None
+
+
+def probe():
+    """The HBM read probe library (raises if it was not built)."""
+    global _probe
+    if _probe is not None:
+        return _probe
+    if not os.path.exists(PROBE_PATH):
+        raise RuntimeError(f"{PROBE_PATH} is missing: build it with `python -m block_sparse_paged_bsr_amd.build`")
+    try:
+        import torch  # noqa: F401  (one HIP runtime per process, as in lib())
+    except ImportError:
+        pass
+    L = C.CDLL(PROBE_PATH)
+    vp = C.c_void_p
+    L.bsr_probe_read_pages.argtypes = [vp, vp, vp, C.c_int64, C.c_int64, C.c_int32, C.c_uint32, vp, vp]
+    L.bsr_probe_read_pages.restype = C.c_int
+    _probe = L
+    return L
 
 
 def lib():

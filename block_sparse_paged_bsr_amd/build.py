@@ -1,4 +1,5 @@
-"""Build libbsr_attn.so in-tree with hipcc for gfx950.
+"""Build libbsr_attn.so (the attention path) and libbsr_probe.so (the HBM read probe that
+bench.py prices the decode path against) in-tree with hipcc for gfx950.
 
 Usage: ``python -m block_sparse_paged_bsr_amd.build`` (or ``build()`` from Python).
 Every call recompiles every source; objects go to ``_build/`` next to this file.
@@ -15,6 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libbsr_attn.so")
+PROBE_OUT = os.path.join(HERE, "libbsr_probe.so")
 BUILD = os.path.join(HERE, "_build")
 
 SOURCES = [
@@ -26,6 +28,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "attn_decode_bf16.hip"),
     os.path.join(CSRC, "kernels", "merge.hip"),
 ]
+PROBE_SOURCES = [os.path.join(CSRC, "hbm_probe.hip")]
 
 ARCH = os.environ.get("BSR_OFFLOAD_ARCH", "gfx950")
 
@@ -72,18 +75,24 @@ def _compile(src):
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(out, objs):
+    tmp = out + ".tmp"
     cmd = [_hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(OUT, objs[:len(SOURCES)])
+    _link(PROBE_OUT, objs[len(SOURCES):])
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {PROBE_OUT}")
     return OUT
 
 

@@ -100,6 +100,9 @@ RunArgs make_args(const bsr_plan* p, const void* ws) {
   a.lpt = reinterpret_cast<const int32_t*>(base + p->ws.lpt);
   a.tickets = reinterpret_cast<int32_t*>(const_cast<char*>(base) + p->ws.tickets);
   a.num_items = int32_t(p->items.size() / 8);
+  a.imerge = reinterpret_cast<const int32_t*>(base + p->ws.imerge);
+  a.arrive = reinterpret_cast<int32_t*>(const_cast<char*>(base) + p->ws.arrive);
+  a.fold_in_kernel = 0;
   a.part_o = reinterpret_cast<float*>(const_cast<char*>(base) + p->ws.part_o);
   a.part_lse = reinterpret_cast<float*>(const_cast<char*>(base) + p->ws.part_lse);
   a.B = p->B;
@@ -159,6 +162,12 @@ int run_common(const bsr_plan* p, const void* ws, const void* q, const void* k, 
   hipError_t e = hipSuccess;
   if (!p->items.empty()) {
     hipEvent_t t0 = timing_start(s);
+    // split tiles of a plan on the bf16 decode kernel are folded by the wave that writes a tile's
+    // last partial state (partial states addressed with 32-bit offsets).  E4M3 items stream half
+    // the bytes per token, so the wait for each partial state's stores weighs twice as much there:
+    // measured 132.6-133.6 us against 127.7-131.1 us with the merge launch on the batch-64 decode,
+    // which E4M3 therefore keeps.
+    const bool fold_ok = p->item_folds && size_t(p->Hk) * p->Tq * (p->d + 1) * sizeof(float) * p->num_slots < (size_t(1) << 31);
     if (kv_e4m3) {
       e = launch_decode_bf16(a, true, s);
     } else if (dtype == BSR_DTYPE_F32) {
@@ -170,6 +179,7 @@ int run_common(const bsr_plan* p, const void* ws, const void* q, const void* k, 
       const bool dec_ok = !mask && ((p->decode && decode_bf16_supported(p->d, p->g, p->Tq)) ||
                                     (!p->causal && p->window_left < 0 && decode_bf16_tiles(p->d, p->g, p->Tq)));
       if (dec_ok) {
+        a.fold_in_kernel = fold_ok ? 1 : 0;
         e = launch_decode_bf16(a, false, s);
       } else {
         if (!prefill_bf16_supported(p->d, p->Tq)) return unsupported("bf16 head_dim must be 64 or 128");
@@ -184,7 +194,8 @@ int run_common(const bsr_plan* p, const void* ws, const void* q, const void* k, 
     return unsupported("fp32 head_dim must be one of 16, 32, 64, 128, 256");
   }
   (void)any_tokens;
-  if (a.num_merge > 0) {
+  const int32_t merge_left = a.fold_in_kernel ? p->num_empty_merge : a.num_merge;  // records for the merge pass
+  if (merge_left > 0) {
     hipEvent_t t1 = timing_start(s);
     e = launch_merge(a, dtype, s);
     timing_stop(t1, s, 1);

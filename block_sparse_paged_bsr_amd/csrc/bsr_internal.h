@@ -61,6 +61,8 @@ struct WsLayout {
   size_t req = 0, indices = 0, items = 0, qptr = 0, merge = 0, mslots = 0, mroff = 0;
   size_t lpt = 0;      // [num_items]: position in `items` of the t-th item in the plan's LPT order
   size_t tickets = 0;  // [kTicketGroups][2]: next ticket, finished workgroups (zero between calls)
+  size_t imerge = 0;   // [num_items], queue order: merge record of the item's split tile, or -1
+  size_t arrive = 0;   // [num_merge][H_kv]: partial states written so far (zero between calls)
   size_t meta_bytes = 0;  // end of metadata
   size_t part_o = 0, part_lse = 0;
   size_t total = 0;
@@ -91,6 +93,8 @@ struct bsr_plan {
   std::vector<int32_t> merge_tiles, merge_ptr, merge_slots;
   std::vector<int32_t> merge_roff;   // composable plans: partial-row offset of each merge slot
   int32_t num_slots = 0;
+  int32_t num_empty_merge = 0;  // merge records with no slot (tiles with nothing visible)
+  bool item_folds = false;      // every split tile's record is reachable from its items (imerge)
   // composable plans: number of levels and the first (flattened) request of each level
   int32_t num_levels = 1;
   std::vector<int32_t> level_req_start;

@@ -236,12 +236,20 @@ int build_composable_plan(const bsr_plan_desc* levels, int32_t n_levels, int32_t
   L.mroff = off;    off = al256(off + sizeof(int32_t) * std::max<size_t>(p->merge_roff.size(), 1));
   L.lpt = off;      off = al256(off + sizeof(int32_t) * std::max(M, 1));
   L.tickets = off;  off = al256(off + sizeof(int32_t) * 2 * kTicketGroups);
+  // (a query's states span several tiles: the merge pass folds them, never the attention kernel)
+  L.imerge = off;   off = al256(off + sizeof(int32_t) * std::max(M, 1));
+  L.arrive = off;   off = al256(off + sizeof(int32_t));
   L.meta_bytes = off;
   const size_t rows_per_slot = size_t(p->Hk) * p->Tq;
   L.part_o = off;   off = al256(off + sizeof(float) * rows_per_slot * p->d * p->num_slots);
   L.part_lse = off; off = al256(off + sizeof(float) * rows_per_slot * p->num_slots);
   L.total = off;
   p->meta.assign(L.meta_bytes, 0);
+  {
+    auto* im = reinterpret_cast<int32_t*>(p->meta.data() + L.imerge);
+    std::fill(im, im + std::max(M, 1), -1);
+    p->item_folds = false;
+  }
   auto* req = reinterpret_cast<ReqRec*>(p->meta.data() + L.req);
   int64_t tok = 0;
   for (int32_t i = 0; i < p->B; ++i) {

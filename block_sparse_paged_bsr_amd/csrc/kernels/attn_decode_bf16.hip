@@ -22,7 +22,9 @@
 //           converted to bf16 in place (B operand), V^T comes from the step's V rows
 //           staged in a wave-private LDS tile and read back with the transposing
 //           LDS read of gfx950 (ds_read_b64_tr_b16, A operand).
-// A work item writes the final (O, LSE) or a partial state folded by the merge pass.
+// A work item writes the final (O, LSE) or a partial state.  The partial states of a split tile
+// are folded by the workgroup that writes the tile's last one (see fold_tile below); the merge
+// pass then only writes tiles with nothing visible.
 // CAP: logits soft cap (eq. 8 of the review), each scaled score s becomes c tanh(s / c).  A
 // sliding window needs nothing here: all rows of a decode item share one query position, so
 // the planned chunks already start at the window.
@@ -57,6 +59,16 @@ constexpr int kDecodeWaves = 8;
 template <int D>
 constexpr int decode_vs_bytes() { return 16 * (D + 8) * 2; }  // one wave's V staging tile
 
+// Buffer resources over the partial states (raw, byte offsets; the host keeps them below 2 GiB)
+// and the cache policy of their accesses: agent scope (sc1), the encoding the compiler gives a
+// relaxed agent-scope atomic load or store, so that every access is coherent across the XCDs'
+// separate L2 caches without a whole-cache write-back or invalidation.
+constexpr int kAgentScope = 16;  // sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, 0x7fffffff, 0x00020000);
+}
+#define BSR_DECODE_WAIT_VMCNT0() __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8))
+
 template <int D, bool CAP, bool KV8>
 __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(RunArgs a) {
   constexpr int KB = D / 32;  // k-blocks of the score product
@@ -83,6 +95,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
   const uint8_t* __restrict__ K = static_cast<const uint8_t*>(a.k);
   const uint8_t* __restrict__ V = static_cast<const uint8_t*>(a.v);
   uint16_t* __restrict__ O = static_cast<uint16_t*>(a.o);
+  const __amdgpu_buffer_rsrc_t part_o_rs = raw_rsrc(a.part_o), part_lse_rs = raw_rsrc(a.part_lse);
 
   // Column n of an item serves packed row row_start + n of its tile (GQA packing, eq. 3 of the
   // review): query q_start + row / g, head g * h_kv + row % g.  A decode tile is the g heads of one
@@ -132,16 +145,21 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
   const int num_items = a.num_items;
   int t = draw();
   ItemRec next = a.items[a.lpt[t < num_items ? t : 0]];
+  int next_mi = a.imerge[a.lpt[t < num_items ? t : 0]];
   bf16x8 qb[KB], qn[KB];
   int32_t pre[NPRE];
   bool have_pre = false;
   while (t < num_items) {
     const ItemRec item = next;
+    const int item_mi = next_mi;
     bool claimed = false, more = false;
     auto claim = [&]() {  // every wave of the workgroup reaches this at the same step of the item
       t = draw();
       more = t < num_items;
-      if (more) next = a.items[a.lpt[t]];
+      if (more) {
+        next = a.items[a.lpt[t]];
+        next_mi = a.imerge[a.lpt[t]];
+      }
       claimed = true;
     };
     const int kv_end = item.kv_end;
@@ -325,10 +343,87 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
         if (j == 0) a.lse[orow] = lse;
       } else {
         const int64_t prow = (int64_t(item.slot) * a.Hk + hk) * a.Tq + n;  // row n of the tile
-        float* pp = a.part_o + prow * D + 4 * j;
+        if (a.fold_in_kernel) {  // read by whichever workgroup folds the tile: agent-scope stores
+          const int32_t ob = int32_t(prow * D + 4 * j) * 4;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(pp + db * 16) = oacc[db] * inv;
-        if (j == 0) a.part_lse[prow] = lse;
+          for (int db = 0; db < DB; ++db)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, oacc[db] * inv), part_o_rs,
+                                                   ob + 64 * db, 0, kAgentScope);
+          if (j == 0)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse), part_lse_rs, int32_t(prow) * 4, 0,
+                                                  kAgentScope);
+        } else {
+          float* pp = a.part_o + prow * D + 4 * j;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(pp + db * 16) = oacc[db] * inv;
+          if (j == 0) a.part_lse[prow] = lse;
+        }
+      }
+    }
+
+    // The last of a split tile's partial states folds the tile (the reduction of "FlashInfer:
+    // Engineering a Customizable, Block-Sparse Attention Engine for LLM Inference Serving" §VIII.3
+    // and §VIII.6, inside the attention kernel), per KV head: every wave that writes one of the
+    // tile's states for its head waits until its stores are complete at agent scope and then counts
+    // itself in; the wave that completes the count reads the tile's states in the plan's slot order
+    // (KV order) and writes the final output, so the result does not depend on which workgroup
+    // folded it, and returns the counter to zero for the next call.
+    if (a.fold_in_kernel && item_mi >= 0) {  // (uniform: all waves of the workgroup run the item)
+      const MergeRec mr = a.merge[item_mi];
+      const int ns = mr.slot_count;
+      const int* __restrict__ sl = a.mslots + mr.slot_begin;
+      const int sid0 = sl[0], sid1 = sl[ns > 1 ? 1 : 0];  // (fetched while the stores complete)
+      BSR_DECODE_WAIT_VMCNT0();
+      int32_t* ctr = a.arrive + int64_t(item_mi) * a.Hk + hk;
+      int arrived = 0;
+      if (lane == 0) arrived = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      arrived = __builtin_amdgcn_readfirstlane(arrived);
+      if (arrived == ns - 1) {
+        if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (n < item.row_end - item.row_start) {
+          // the states of this lane's row, two slots per round (loads issued together), folded
+          // with a running maximum: O = sum_k e^(lse_k - m) O_k / sum_k e^(lse_k - m)
+          float mrun = kNegInf, den = 0.f;
+          f32x4 acc[DB];
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int k0 = 0; k0 < ns; k0 += 2) {
+            float lk[2];
+            f32x4 ok[2][DB];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int k = min(k0 + u, ns - 1);  // (a repeated last slot is skipped below)
+              const int sid = k == 0 ? sid0 : k == 1 ? sid1 : sl[k];
+              const int64_t prow = (int64_t(sid) * a.Hk + hk) * a.Tq + n;
+              lk[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_lse_rs, int32_t(prow) * 4, 0,
+                                                                           kAgentScope));
+              const int32_t ob = int32_t(prow * D + 4 * j) * 4;
+#pragma unroll
+              for (int db = 0; db < DB; ++db)
+                ok[u][db] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(part_o_rs, ob + 64 * db, 0, kAgentScope));
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              if (k0 + u >= ns || lk[u] == kNegInf) continue;
+              const float mn = fmaxf(mrun, lk[u]);
+              const float so = expf(mrun - mn), w = expf(lk[u] - mn);
+              den = den * so + w;
+#pragma unroll
+              for (int db = 0; db < DB; ++db) acc[db] = acc[db] * so + ok[u][db] * w;
+              mrun = mn;
+            }
+          }
+          const bool empty = !(den > 0.f);
+          const float inv = empty ? 0.f : 1.f / den;
+          uint16_t* op = O + orow * D + 4 * j;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const f32x4 v = acc[db] * inv;
+            *reinterpret_cast<u32x2*>(op + db * 16) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          }
+          if (j == 0) a.lse[orow] = empty ? kNegInf : mrun + logf(den);
+        }
       }
     }
   }

@@ -31,6 +31,9 @@ struct RunArgs {
   const int32_t* lpt;    // items in the plan's LPT order, as positions in `items`
   int32_t* tickets;      // per workgroup group: next ticket, finished workgroups (zero between calls)
   int32_t num_items;
+  const int32_t* imerge;  // per item (queue order): merge record of its split tile, or -1
+  int32_t* arrive;        // [num_merge][H_kv]: partial states written (zero between calls)
+  int32_t fold_in_kernel; // 1: the decode kernel folds split tiles; the merge pass writes empty tiles
   float* part_o;
   float* part_lse;
   const void* q;

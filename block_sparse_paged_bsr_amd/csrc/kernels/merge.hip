@@ -54,6 +54,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_partials_kernel(RunArgs a
   const int hk = blockIdx.y, tid = threadIdx.x;
   const int mi = blockIdx.x / row_chunks, r0 = (blockIdx.x % row_chunks) * kRowChunk;
   const MergeRec mr = a.merge[mi];
+  if (a.fold_in_kernel && mr.slot_count > 0) return;  // folded by the attention kernel
   const int nrows = min(kRowChunk, mr.row_end - mr.row_start - r0);  // rows r0 .. r0 + nrows - 1
   if (nrows <= 0) return;  // uniform: a chunk past the tile's last row
   const int ns = mr.slot_count;

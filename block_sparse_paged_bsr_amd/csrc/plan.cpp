@@ -277,6 +277,8 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
   L.mroff = off;    off = align256(off + sizeof(int32_t));  // (no row offsets in a single-level plan)
   L.lpt = off;      off = align256(off + sizeof(int32_t) * std::max(M, 1));
   L.tickets = off;  off = align256(off + sizeof(int32_t) * 2 * kTicketGroups);
+  L.imerge = off;   off = align256(off + sizeof(int32_t) * std::max(M, 1));
+  L.arrive = off;   off = align256(off + sizeof(int32_t) * std::max<int64_t>(int64_t(NM) * p->Hk, 1));
   L.meta_bytes = off;
   const size_t rows_per_slot = size_t(p->Hk) * Tq;
   L.part_o = off;   off = align256(off + sizeof(float) * rows_per_slot * p->d * p->num_slots);
@@ -320,6 +322,22 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
   if (!p->merge_slots.empty())
     std::memcpy(p->meta.data() + L.mslots, p->merge_slots.data(),
                 sizeof(int32_t) * p->merge_slots.size());
+  // each item's merge record (its tile is split), so that the workgroup completing a split tile
+  // can fold it; arrival counters start at zero
+  {
+    std::vector<int32_t> tile_merge(p->tiles.size() / 5, -1);
+    p->num_empty_merge = 0;
+    for (int32_t k = 0; k < NM; ++k) {
+      tile_merge[p->merge_tiles[k]] = k;
+      if (p->merge_ptr[k + 1] == p->merge_ptr[k]) ++p->num_empty_merge;
+    }
+    auto* im = reinterpret_cast<int32_t*>(p->meta.data() + L.imerge);
+    for (int32_t k = 0; k < M; ++k) {
+      const Item& it = items[p->queue_items[k]];
+      im[k] = it.slot >= 0 ? tile_merge[it.tile] : -1;
+    }
+    p->item_folds = true;
+  }
   return BSR_OK;
 }
 

@@ -231,9 +231,15 @@ int bsr_plan_export(const bsr_plan* plan, bsr_plan_view* view);
  *           the request's keys; -inf (with O = 0) for a request without keys.
  * Exact attention, eq. 1 of "FlashInfer: Making Attention Fit the Serving Workload"
  * (§2.1), computed tile by tile with the online-softmax recurrence and split across
- * workers as planned; partial states are combined with the merge of eq. 6.  Runs the
- * attention kernel and, if the plan split any request, the merge kernel.  sm_scale must
- * be positive and finite (1/sqrt(d) for the standard operator).
+ * workers as planned; partial states are combined with the merge of eq. 6.  With bf16 on the
+ * decode kernel (head_dim 64 or 128, at most 16 query heads per KV head) this is one launch:
+ * the wave that writes the last partial state of a split request folds the request's states
+ * in the plan's slot order ("FlashInfer: Engineering a Customizable, Block-Sparse Attention
+ * Engine for LLM Inference Serving" §VIII.3, §VIII.6), and a merge launch follows only if a
+ * request has no keys (its empty state).  Otherwise (fp32, or the tiled kernel) the attention
+ * launch is followed by the merge launch whenever the plan split a request.  The result does
+ * not depend on which workgroup ran which work item.  sm_scale must be positive and finite
+ * (1/sqrt(d) for the standard operator).
  */
 int bsr_run_decode(const bsr_plan* plan, const void* ws, const void* q, const void* k_cache,
                    const void* v_cache, void* o, float* lse, int32_t dtype, float sm_scale,

@@ -40,6 +40,25 @@ def test_header_symbols_exported():
     assert "gfx950" in api.version()
 
 
+def test_probe_header_symbols_exported():
+    """include/bsr_probe.h against libbsr_probe.so (the HBM read probe bench.py uses)."""
+    if not os.path.exists(_lib.PROBE_PATH):
+        pytest.skip("libbsr_probe.so not built")
+    src = open(os.path.join(ROOT, "include", "bsr_probe.h")).read()
+    names = sorted(set(re.findall(r"^\s*int\s+(bsr_\w+)\s*\(", src, re.M)))
+    assert names == sorted(_lib.PROBE_EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.PROBE_PATH], capture_output=True, text=True).stdout
+    assert set(names) <= set(re.findall(r"\b(bsr_\w+)\b", out))
+    L = _lib.probe()
+    # argument checks happen on the host, before any launch
+    one = C.c_void_p(16)
+    assert L.bsr_probe_read_pages(None, one, one, 1, 4096, 1, 0, one, None) == -1
+    assert L.bsr_probe_read_pages(one, one, one, 1, 4000, 1, 0, one, None) == -1
+    assert L.bsr_probe_read_pages(one, one, one, 1, 4096, 0, 0, one, None) == -1
+    assert L.bsr_probe_read_pages(one, one, one, -1, 4096, 1, 0, one, None) == -1
+    assert L.bsr_probe_read_pages(one, one, one, 0, 4096, 1, 0, one, None) == 0
+
+
 def _oracle_as_export(p):
     tiles = np.array([[t.req, t.row_start, t.row_end, t.vis, len(t.items)] for t in p.tiles], dtype=np.int32).reshape(-1, 5)
     items = np.array([[it.req, it.tile, it.row_start, it.row_end, it.kv_start, it.kv_len, it.worker, it.slot]
