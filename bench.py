@@ -553,7 +553,7 @@ PROFILE_CASES = {
         "kernels": {"attn_prefill128_bf16_kernel": "attention, 128-row query tiles"},
         "call": ["attn_prefill128_bf16_kernel"],
         "sources": [SRC + "attn_prefill_bf16.hip", SRC + "common.h"],
-        "unit": "flops", "sq": True},
+        "unit": "flops", "sq": True, "traffic": True},
     "composable_shared_prefix": {
         "workload": "composable shared-prefix decode bf16: 16 groups x 4 requests, 2048-token prefix per group, "
                     "private suffixes U[128,1024], page size 16, 32/8 heads, head_dim 128 (seed 0), one plan",
@@ -585,7 +585,7 @@ def profile_commands(name):
     d = f"gpurun_out/prof/{name}"
     cmds = [f"timeout -s KILL 300 rocprofv3 --kernel-trace --stats --output-format csv -d {d}_trace -o run -- {run} "
             f"--profile-out {d}_event.json"]
-    if case["unit"] == "bytes":
+    if case["unit"] == "bytes" or case.get("traffic"):
         cmds += [f"timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}_fetch -o run -- {run} "
                  "--copy-calib",
                  f"timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}_write -o run -- {run} "

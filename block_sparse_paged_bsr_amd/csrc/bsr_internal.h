@@ -33,10 +33,13 @@ struct ItemRec {
   int32_t kv_start;   // logical tokens [kv_start, kv_end) of the request
   int32_t kv_end;
   int32_t slot;       // partial slot, or -1: write the final output
-  int32_t q_start;    // the request's first query row and first page-list entry, copied from its
-  int32_t page_start; //   request record so that the decode kernel needs only this record
+  int32_t q_start;    // the request's first query row, first page-list entry, query and KV
+  int32_t page_start; //   lengths, copied from its request record so that the attention kernels
+  int32_t q_len;      //   need only this record (the custom-mask offset stays in the request
+  int32_t kv_len;     //   record)
+  int32_t pad[6];
 };
-static_assert(sizeof(ItemRec) == 32, "ItemRec layout");
+static_assert(sizeof(ItemRec) == 64, "ItemRec layout");
 
 // Per block of output rows written by the merge pass: a split or empty tile of a plan, or one
 // query (all of its GQA rows) of a composable plan.  Slot k of the list holds the partial state of

@@ -265,7 +265,8 @@ int build_composable_plan(const bsr_plan_desc* levels, int32_t n_levels, int32_t
   auto* qi = reinterpret_cast<ItemRec*>(p->meta.data() + L.items);
   for (int32_t k = 0; k < M; ++k) {
     const Item& it = items[p->queue_items[k]];
-    qi[k] = ItemRec{it.req, it.r0, it.r1, it.ks, it.ks + it.kl, it.slot, req[it.req].q_start, req[it.req].page_start};
+    qi[k] = ItemRec{it.req, it.r0, it.r1, it.ks, it.ks + it.kl, it.slot, req[it.req].q_start, req[it.req].page_start,
+                    req[it.req].q_len, req[it.req].kv_len, {0, 0, 0, 0}};
   }
   std::memcpy(p->meta.data() + L.qptr, p->queue_ptr.data(), sizeof(int32_t) * (p->C + 1));
   // the items in the partition's LPT order (longest first), as positions in the queue-ordered list

@@ -107,8 +107,40 @@ struct Slots {
   __device__ __forceinline__ lds_u8* v0() const { return base + 2 * PF<D>::SLOT; }
   __device__ __forceinline__ lds_u8* v1() const { return base + 3 * PF<D>::SLOT; }
   __device__ __forceinline__ lds_i32* table() const { return reinterpret_cast<lds_i32*>(base + 4 * PF<D>::SLOT); }
-  static constexpr int BYTES = 4 * PF<D>::SLOT + 4 * kPageWindow;
+  // the next work item's record, fetched during the current item
+  __device__ __forceinline__ lds_i32* rec() const {
+    return reinterpret_cast<lds_i32*>(base + 4 * PF<D>::SLOT + 4 * kPageWindow);
+  }
+  static constexpr int BYTES = 4 * PF<D>::SLOT + 4 * kPageWindow + sizeof(ItemRec);
 };
+
+// The next work item's record, fetched while the current item starts: lane l of the first
+// kRecWords threads loads word l before the current item issues its first tile loads, and
+// stores it to the record slot in LDS once the item's prologue has waited for its own loads, so
+// a new item starts with an LDS read instead of dependent global loads.
+constexpr int kRecWords = int(sizeof(ItemRec) / 4);
+struct RecFetch {
+  int32_t word = 0;
+  bool valid = false;  // uniform: there is a next item
+  __device__ __forceinline__ void load(const ItemRec* next, bool has_next) {
+    valid = has_next;
+    if (has_next && threadIdx.x < kRecWords) word = reinterpret_cast<const int32_t*>(next)[threadIdx.x];
+  }
+  __device__ __forceinline__ void store(lds_i32* rec) const {
+    if (valid && threadIdx.x < kRecWords) rec[threadIdx.x] = word;
+  }
+};
+__device__ __forceinline__ ItemRec read_rec(const lds_i32* rec) {
+  int32_t w[kRecWords];
+#pragma unroll
+  for (int i = 0; i < kRecWords; ++i) w[i] = __builtin_amdgcn_readfirstlane(rec[i]);
+  ItemRec r;
+  __builtin_memcpy(&r, w, sizeof(ItemRec));
+  return r;
+}
+// The request fields the kernels use, from the item record (the custom-mask offset, needed only
+// with a mask, from the request record)
+__device__ __forceinline__ ReqRec req_of(const RunArgs& a, const ItemRec& it);
 
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
   bf16x2 r;
@@ -186,6 +218,18 @@ __device__ __forceinline__ T uniform_load(const T* p) {
   return v;
 }
 
+__device__ __forceinline__ ReqRec req_of(const RunArgs& a, const ItemRec& it) {
+  ReqRec r;
+  r.q_start = it.q_start;
+  r.q_len = it.q_len;
+  r.page_start = it.page_start;
+  r.kv_len = it.kv_len;
+  r.tok_start = 0;
+  r.pad = 0;
+  r.mask_off = a.mask ? uniform_load(a.req + it.req).mask_off : 0;
+  return r;
+}
+
 // Page-size classes the kernels are compiled for: any size (division), a power of two (shift
 // and mask), or a power of two that divides 32 (then a token's offset inside its page is the
 // same in every 32-token tile of an item, and its page number advances by 32 / P per tile).
@@ -195,6 +239,8 @@ constexpr int kPageAny = 0, kPagePow2 = 1, kPageDiv32 = 2;
 // A window of up to kPageWindow entries of the request's page list is staged in LDS, so the
 // lookups inside the tile loops are LDS reads and the only vector-memory loads in flight there
 // are the tile DMAs.  POW2: the page size is a power of two (shift and mask).
+constexpr int kRefillBatch = 4;  // page-id loads in flight per thread during a window refill
+
 template <bool POW2>
 struct Paging {
   const int32_t* indices;  // the request's page list starts at indices + page_start
@@ -218,14 +264,36 @@ struct Paging {
   // (Re)fill the window so it holds the pages of tokens [lo, hi]; lo and hi are uniform and
   // every thread of the workgroup (NTH of them) calls this (it synchronises the workgroup
   // when it refills).
-  template <int NTH = kThreads>
+  // At an item's start (START) the loads of the refill are issued kRefillBatch per thread before
+  // their values are stored, so a window of up to NTH * kRefillBatch entries costs one memory
+  // round trip there; inside the tile loops, where a refill is rare (an item longer than the
+  // window) and registers are scarce, one entry per thread at a time.
+  template <int NTH = kThreads, bool START = false>
   __device__ __forceinline__ void cover(int lo, int hi) {
     const int plo = page_no(lo), phi = page_no(hi);
     if (plo >= base && phi < base + kPageWindow) return;
     __syncthreads();  // nobody reads the old window any more
     base = plo;
     const int cnt = min(kPageWindow, page_no(kv_end - 1) - plo + 1);
-    for (int j = threadIdx.x; j < cnt; j += NTH) table[j] = indices[page_start + plo + j];
+    const int32_t* __restrict__ src = indices + page_start + plo;
+    if constexpr (START) {
+      // (cnt >= 1: page_no clamps to the chunk's last token; a load past cnt re-reads entry
+      // cnt - 1, so the first batch is straight-line code and none of its loads waits for another)
+      auto batch = [&](int j0) {
+        int32_t v[kRefillBatch];
+#pragma unroll
+        for (int u = 0; u < kRefillBatch; ++u) v[u] = src[min(j0 + u * NTH + int(threadIdx.x), cnt - 1)];
+#pragma unroll
+        for (int u = 0; u < kRefillBatch; ++u) {
+          const int j = j0 + u * NTH + int(threadIdx.x);
+          if (j < cnt) table[j] = v[u];
+        }
+      };
+      batch(0);
+      for (int j0 = NTH * kRefillBatch; j0 < cnt; j0 += NTH * kRefillBatch) batch(j0);
+    } else {
+      for (int j = threadIdx.x; j < cnt; j += NTH) table[j] = src[j];
+    }
     __syncthreads();
   }
 };
@@ -366,10 +434,10 @@ __device__ __forceinline__ void sched_mfma_interleave() {
 // instruction of the wave, in issue order; nothing else in the step loop touches vector memory
 // (page ids come from the LDS window, and a window refill waits for its own loads, hence for every
 // older load too), so the limits below count exactly these batches.
-constexpr int kKAhead = 4, kVAhead = 2;
 constexpr int kIssueToUseSteps = 3;
+constexpr int kKAhead = kIssueToUseSteps + 1, kVAhead = kIssueToUseSteps - 1;
 constexpr int kDmaBatchesPerStep = 2;
-constexpr int kMaxBatchesInFlight = 4;
+constexpr int kMaxBatchesInFlight = kDmaBatchesPerStep * (kIssueToUseSteps - 1);
 static_assert(kKAhead - 1 == kIssueToUseSteps && kVAhead + 1 == kIssueToUseSteps,
               "step j reads K(j+1) and V(j-1): both issued kIssueToUseSteps steps earlier");
 static_assert(kMaxBatchesInFlight == kDmaBatchesPerStep * (kIssueToUseSteps - 1),
@@ -388,7 +456,7 @@ __device__ __forceinline__ int batches_in_between(int j, int n) {
 template <int NF>
 __device__ __forceinline__ void wait_dma_batches(int nb) {
   static_assert(kMaxBatchesInFlight * NF <= 63, "the vmcnt field holds 0 .. 63");
-  static_assert(kMaxBatchesInFlight == 4, "one case per batch count");
+  static_assert(kMaxBatchesInFlight <= 4, "one case per batch count");
   switch (nb) {
     case 4: BSR_WAIT_VMCNT(4 * NF); break;
     case 3: BSR_WAIT_VMCNT(3 * NF); break;
@@ -406,7 +474,7 @@ __device__ __forceinline__ void tile_loop(PG& pgn, int kv_start, int kv_end, con
   const int ntiles = (kv_end - kv_start + kTileKV - 1) / kTileKV;
   __syncthreads();  // LDS free (previous item finished, including its combine)
   pgn.base = -kPageWindow;  // nothing staged for this item yet
-  pgn.cover(kv_start, kv_start + 2 * kTileKV - 1);
+  pgn.template cover<kThreads, true>(kv_start, kv_start + 2 * kTileKV - 1);
   int32_t pk = k_page(pgn, kv_start), pv = v_page(pgn, kv_start);
   issue_k<D>(s.k0(), pgn, kv_start, pk, K);
   issue_v<D>(s.v0(), pgn, kv_start, pv, V);
@@ -805,21 +873,24 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
     u32x4 pa[2], pb[2];
     __syncthreads();  // LDS free (previous item finished)
     pgn.base = -kPageWindow;  // nothing staged for this item yet
-    pgn.cover(T(0), T(6) - 1);
+    pgn.template cover<kThreads, true>(T(0), T(kKAhead + 2) - 1);
+    const bool window_holds_item = pgn.page_no(kv_end - 1) - pgn.base < kPageWindow;  // (uniform)
     {
-      const int32_t k0 = page_k(0), k1 = page_k(1), k2 = page_k(2), k3 = page_k(3);
-      const int32_t v0 = page_v(0), v1 = page_v(1);
-      dma_k(0, k0);
-      if (n > 1) dma_k(1, k1);
-      if (n > 2) dma_k(2, k2);
-      if (n > 3) dma_k(3, k3);
-      dma_v(0, v0);
-      if (n > 1) dma_v(1, v1);
+      int32_t kp[kKAhead], vp[kVAhead];
+#pragma unroll
+      for (int i = 0; i < kKAhead; ++i) kp[i] = page_k(i);
+#pragma unroll
+      for (int i = 0; i < kVAhead; ++i) vp[i] = page_v(i);
+#pragma unroll
+      for (int i = 0; i < kKAhead; ++i)
+        if (i == 0 || n > i) dma_k(i, kp[i]);
+#pragma unroll
+      for (int i = 0; i < kVAhead; ++i)
+        if (i == 0 || n > i) dma_v(i, vp[i]);
     }
-    static_assert(kKAhead == 4 && kVAhead == 2, "the prologue stages K(0..3) and V(0..1)");
     int32_t nk = page_k(kKAhead), nv = page_v(kVAhead);  // for step 0's loads
     BSR_WAIT_VMCNT(0);
-    __syncthreads();  // K(0..3), V(0..1) staged
+    __syncthreads();  // K(0 .. kKAhead-1), V(0 .. kVAhead-1) staged
     qk(k_slot(0), Sa);
     mask(Sa, T(0));
 
@@ -833,7 +904,9 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
     // step j with S(j) in Scur and P(j-1) in pprev; writes S(j+1) to Snext and P(j) to pcur
     auto step = [&](int j, f32x16& Scur, f32x16& Snext, const u32x4 (&pprev)[2], u32x4 (&pcur)[2]) {
       const bool fast = PG == kPageDiv32 && j >= 1 && j + kKAhead + 1 < n_full;
-      pgn.cover(T(j + kVAhead + 1), T(j + kKAhead + 2) - 1);  // this step's lookups: K(j+5), V(j+3)
+      // this step's lookups: K(j + kKAhead + 1), V(j + kVAhead + 1) (the window filled at the
+      // item's start holds all of its pages unless the item spans more than kPageWindow)
+      if (!window_holds_item) pgn.cover(T(j + kVAhead + 1), T(j + kKAhead + 2) - 1);
       wait_dma_batches<NF>(fast ? kMaxBatchesInFlight : batches_in_between(j, n));
       __builtin_amdgcn_s_barrier();
       if (fast) {
@@ -1148,7 +1221,7 @@ __device__ __forceinline__ void prefill_item16(const RunArgs& a, const ItemRec& 
 // ---------------------------------------------------------------------------------
 template <int D, int PG, bool VAR>
 __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec& item, const ReqRec& rq, int hk,
-                                                const Slots<D>& sl) {
+                                                const Slots<D>& sl, const RecFetch& nf) {
   constexpr int KB = PF<D>::KB, FRAG = PF<D>::FRAG;
   constexpr int KS16 = D / 16;  // 16-deep k-steps of the score product
   constexpr bool POW2 = PG != kPageAny;
@@ -1396,21 +1469,25 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
   f32x16 Sa[2], Sb[2];
   u32x4 pa[2][2], pb[2][2];
   __syncthreads();  // LDS free (previous item finished)
-  pgn.template cover<kThreads2>(T(0), T(6) - 1);
+  pgn.template cover<kThreads2, true>(T(0), T(kKAhead + 2) - 1);
+  const bool window_holds_item = pgn.page_no(kv_end - 1) - pgn.base < kPageWindow;  // (uniform)
   {
-    const int32_t k0 = page_k(0), k1 = page_k(1), k2 = page_k(2), k3 = page_k(3);
-    const int32_t v0 = page_v(0), v1 = page_v(1);
-    dma_k(0, k0);
-    if (n > 1) dma_k(1, k1);
-    if (n > 2) dma_k(2, k2);
-    if (n > 3) dma_k(3, k3);
-    dma_v(0, v0);
-    if (n > 1) dma_v(1, v1);
+    int32_t kp[kKAhead], vp[kVAhead];
+#pragma unroll
+    for (int i = 0; i < kKAhead; ++i) kp[i] = page_k(i);
+#pragma unroll
+    for (int i = 0; i < kVAhead; ++i) vp[i] = page_v(i);
+#pragma unroll
+    for (int i = 0; i < kKAhead; ++i)
+      if (i == 0 || n > i) dma_k(i, kp[i]);
+#pragma unroll
+    for (int i = 0; i < kVAhead; ++i)
+      if (i == 0 || n > i) dma_v(i, vp[i]);
   }
-  static_assert(kKAhead == 4 && kVAhead == 2, "the prologue stages K(0..3) and V(0..1)");
   int32_t nk = page_k(kKAhead), nv = page_v(kVAhead);  // for step 0's loads
   BSR_WAIT_VMCNT(0);
-  __syncthreads();  // K(0..3), V(0..1) staged
+  nf.store(sl.rec());  // (its load was issued before this item's)
+  __syncthreads();  // K(0 .. kKAhead-1), V(0 .. kVAhead-1) staged
   qk(k_slot(0), Sa);
   mask(Sa, T(0));
 
@@ -1419,7 +1496,9 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
   const int n_full = PG == kPageDiv32 ? (kv_end - kv0) / 32 : 0;
   auto step = [&](int j, f32x16 (&Scur)[2], f32x16 (&Snext)[2], const u32x4 (&pprev)[2][2], u32x4 (&pcur)[2][2]) {
     const bool fast = PG == kPageDiv32 && j >= 1 && j + kKAhead + 1 < n_full;
-    pgn.template cover<kThreads2>(T(j + kVAhead + 1), T(j + kKAhead + 2) - 1);  // lookups: K(j+5), V(j+3)
+    // lookups: K(j + kKAhead + 1), V(j + kVAhead + 1); the window filled at the item's start holds
+    // all of its pages unless the item spans more than kPageWindow of them
+    if (!window_holds_item) pgn.template cover<kThreads2>(T(j + kVAhead + 1), T(j + kKAhead + 2) - 1);
     wait_dma_batches<NF>(fast ? kMaxBatchesInFlight : batches_in_between(j, n));
     __builtin_amdgcn_s_barrier();
     if (fast) {
@@ -1453,26 +1532,54 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
 
   // ---- epilogue: final output or partial state, per block ----
   acc_settle();
+  float inv[2], lse[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const float lb = pair_sum(l[b]);  // the two halves of a row held different tokens
-    if (!row_ok[b]) continue;
     const bool empty = !(lb > 0.f);
-    const float inv = empty ? 0.f : 1.f / lb;
-    const float lse = empty ? kNegInf : (m[b] + log2f(lb)) * kLn2;
-    const int r = item.row_start + 64 * wave + 32 * b + r32;
-    if (item.slot < 0) {
-      const int64_t orow = int64_t(rq.q_start + row_pos[b]) * a.Hq + row_hq[b];
-      uint16_t* op = static_cast<uint16_t*>(a.o) + orow * D + 4 * h;
+    inv[b] = empty ? 0.f : 1.f / lb;
+    lse[b] = empty ? kNegInf : (m[b] + log2f(lb)) * kLn2;
+  }
+  if (item.slot < 0) {
+    // The final rows go out through LDS: a lane of the product layout holds 8-byte pieces of 32
+    // rows, so stored directly every store instruction would touch 32 partial lines; staged in the
+    // (now idle) tile slots, each wave writes its 64 rows back as whole 16-byte row pieces, D / 8
+    // lanes per row (for g = 4 one instruction covers the four heads of a query: one contiguous
+    // 1 KB run of O).  Rows are padded by 16 bytes against bank conflicts.
+    constexpr int RS = 2 * D + 16;  // staging row stride, bytes
+    static_assert(128 * RS <= 4 * PF<D>::SLOT, "the staged tile fits in the tile slots");
+    lds_u8* st = sl.k0();
+    __syncthreads();  // both waves are done with the tile slots
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      lds_u8* rowp = st + (64 * wave + 32 * b + r32) * RS + 8 * h;
 #pragma unroll
       for (int cb = 0; cb < KB; ++cb)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<u32x2*>(op + 32 * cb + 8 * q4) =
-              u32x2{cvt_pk_bf16(oacc[b][cb][4 * q4] * inv, oacc[b][cb][4 * q4 + 1] * inv),
-                    cvt_pk_bf16(oacc[b][cb][4 * q4 + 2] * inv, oacc[b][cb][4 * q4 + 3] * inv)};
-      if (h == 0) a.lse[orow] = lse;
-    } else {
+          *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(rowp + 2 * (32 * cb + 8 * q4)) =
+              u32x2{cvt_pk_bf16(oacc[b][cb][4 * q4] * inv[b], oacc[b][cb][4 * q4 + 1] * inv[b]),
+                    cvt_pk_bf16(oacc[b][cb][4 * q4 + 2] * inv[b], oacc[b][cb][4 * q4 + 3] * inv[b])};
+      if (h == 0 && row_ok[b]) a.lse[int64_t(rq.q_start + row_pos[b]) * a.Hq + row_hq[b]] = lse[b];
+    }
+    __syncthreads();  // (each wave reads back only its own rows; the barrier orders the LDS traffic)
+    constexpr int LPR = D / 8, RPI = 64 / LPR;  // lanes per row (16 bytes each), rows per store
+    const int sub = lane / LPR, col = 8 * (lane % LPR);
+#pragma unroll
+    for (int i = 0; i < 64 / RPI; ++i) {
+      const int lr = 64 * wave + RPI * i + sub;  // row of the tile
+      const int r = item.row_start + lr;
+      const u32x4 v = *reinterpret_cast<__attribute__((address_space(3))) const u32x4*>(st + lr * RS + 2 * col);
+      if (r < item.row_end) {
+        const int64_t orow = int64_t(rq.q_start + r / a.g) * a.Hq + hk * a.g + r % a.g;
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) + orow * D + col) = v;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      if (!row_ok[b]) continue;
+      const int r = item.row_start + 64 * wave + 32 * b + r32;
       const int64_t prow = (int64_t(item.slot) * a.Hk + hk) * a.Tq + (r - item.row_start);
       float* pp = a.part_o + prow * D + 4 * h;
 #pragma unroll
@@ -1481,8 +1588,8 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
         for (int q4 = 0; q4 < 4; ++q4)
           *reinterpret_cast<f32x4*>(pp + 32 * cb + 8 * q4) =
               f32x4{oacc[b][cb][4 * q4], oacc[b][cb][4 * q4 + 1], oacc[b][cb][4 * q4 + 2], oacc[b][cb][4 * q4 + 3]} *
-              inv;
-      if (h == 0) a.part_lse[prow] = lse;
+              inv[b];
+      if (h == 0) a.part_lse[prow] = lse[b];
     }
   }
 }
@@ -1501,15 +1608,23 @@ void attn_prefill_bf16_kernel(RunArgs a) {
   const int bid = blockIdx.x + gridDim.x * blockIdx.y;
   // (the division runs on the vector ALU; the results are uniform, so read them back as scalars)
   const int hk = __builtin_amdgcn_readfirstlane(bid % a.Hk), w = __builtin_amdgcn_readfirstlane(bid / a.Hk);
-  const int it_end = uniform_load(a.qptr + w + 1);
-  for (int it = uniform_load(a.qptr + w); it < it_end; ++it) {
-    const ItemRec item = uniform_load(a.items + it);
-    const ReqRec rq = uniform_load(a.req + item.req);
+  const int it0 = uniform_load(a.qptr + w), it_end = uniform_load(a.qptr + w + 1);
+  if (it0 >= it_end) return;
+  ItemRec item = uniform_load(a.items + it0);
+  for (int it = it0; it < it_end; ++it) {
+    RecFetch nf;  // the next item's record, loaded before this item's first tile loads
+    nf.load(a.items + it + 1, it + 1 < it_end);
+    const ReqRec rq = req_of(a, item);
     const int rows = item.row_end - item.row_start;
     if (rows > 64) prefill_item32<D, true, PG, VAR>(a, item, rq, hk, sl);        // 3-4 blocks of 32 rows, pipelined
     else if (rows > 32) prefill_item32<D, false, PG, VAR>(a, item, rq, hk, sl);  // 2 blocks, tokens split
     else if (rows > 16) prefill_item16<D, 2, POW2, VAR>(a, item, rq, hk, sl);  // 2 blocks of 16 rows
     else prefill_item16<D, 1, POW2, VAR>(a, item, rq, hk, sl);                 // 1 block, tokens split 4 ways
+    if (it + 1 < it_end) {
+      nf.store(sl.rec());
+      __syncthreads();
+      item = read_rec(sl.rec());
+    }
   }
 }
 
@@ -1521,11 +1636,14 @@ void attn_prefill128_bf16_kernel(RunArgs a) {
   const Slots<D> sl{(lds_u8*)lds};
   const int bid = blockIdx.x + gridDim.x * blockIdx.y;  // KV-head-minor: see attn_prefill_bf16_kernel
   const int hk = __builtin_amdgcn_readfirstlane(bid % a.Hk), w = __builtin_amdgcn_readfirstlane(bid / a.Hk);
-  const int it_end = uniform_load(a.qptr + w + 1);
-  for (int it = uniform_load(a.qptr + w); it < it_end; ++it) {
-    const ItemRec item = uniform_load(a.items + it);
-    const ReqRec rq = uniform_load(a.req + item.req);
-    prefill_item128<D, PG, VAR>(a, item, rq, hk, sl);
+  const int it0 = uniform_load(a.qptr + w), it_end = uniform_load(a.qptr + w + 1);
+  if (it0 >= it_end) return;
+  ItemRec item = uniform_load(a.items + it0);
+  for (int it = it0; it < it_end; ++it) {
+    RecFetch nf;
+    nf.load(a.items + it + 1, it + 1 < it_end);
+    prefill_item128<D, PG, VAR>(a, item, req_of(a, item), hk, sl, nf);
+    if (it + 1 < it_end) item = read_rec(sl.rec());
   }
 }
 

@@ -48,8 +48,9 @@ def _kernel_constant(name):
 PAGE_WINDOW = _kernel_constant("kPageWindow")
 TILE_KV = _kernel_constant("kTileKV")
 BATCHES_PER_STEP = _kernel_constant("kDmaBatchesPerStep")
-MAX_IN_FLIGHT = _kernel_constant("kMaxBatchesInFlight")
-K_AHEAD = _kernel_constant("kKAhead")
+ISSUE_TO_USE = _kernel_constant("kIssueToUseSteps")  # steps between a tile's loads and its first read
+K_AHEAD, V_AHEAD = ISSUE_TO_USE + 1, ISSUE_TO_USE - 1  # step j loads K(j + K_AHEAD), V(j + V_AHEAD)
+MAX_IN_FLIGHT = BATCHES_PER_STEP * (ISSUE_TO_USE - 1)
 
 
 def _page_no(t, kv_end, P):
@@ -124,11 +125,12 @@ def replay_rings(n, n_full, loose=0):
             assert holds[ring].get(slot) == tile, f"{ring}({tile}) not staged when read"
         last_read[ring][slot] = epoch[0]
 
-    # prologue: K(0..3), V(0..1), then a full wait and a barrier; the first scores read K(0)
-    for t in range(4):
+    # prologue: K(0 .. K_AHEAD-1), V(0 .. V_AHEAD-1), then a full wait and a barrier; the first
+    # scores read K(0)
+    for t in range(K_AHEAD):
         if t < n:
             issue("K", t)
-    for t in range(2):
+    for t in range(V_AHEAD):
         if t < n:
             issue("V", t)
     wait(0)
@@ -136,21 +138,23 @@ def replay_rings(n, n_full, loose=0):
     read("K", 0)
     fast_steps = 0
     for j in range(n + 1):
-        fast = j >= 1 and j + 5 < n_full
-        nb = MAX_IN_FLIGHT if fast else (j + 2 < n) + (j < n) + (j + 3 < n) + (j + 1 < n)
+        fast = j >= 1 and j + K_AHEAD + 1 < n_full
+        # batches issued in the steps after the ones this step needs, that exist in the item
+        nb = MAX_IN_FLIGHT if fast else sum((j - s + K_AHEAD < n) + (j - s + V_AHEAD < n)
+                                            for s in range(1, ISSUE_TO_USE))
         assert nb <= MAX_IN_FLIGHT
         wait(nb + loose)
         barrier()
         if fast:
             fast_steps += 1
-            issue("K", j + 4)
-            issue("V", j + 2)
+            issue("K", j + K_AHEAD)
+            issue("V", j + V_AHEAD)
             assert issued[0] == BATCHES_PER_STEP
         else:
-            if j + 4 < n:
-                issue("K", j + 4)
-            if j + 2 < n:
-                issue("V", j + 2)
+            if j + K_AHEAD < n:
+                issue("K", j + K_AHEAD)
+            if j + V_AHEAD < n:
+                issue("V", j + V_AHEAD)
             assert issued[0] <= BATCHES_PER_STEP
         # the stream: scores of tile j+1 (masked out entirely when it does not exist), P.V of j-1
         read("K", j + 1, must_hold=j + 1 < n)
@@ -161,25 +165,27 @@ def replay_rings(n, n_full, loose=0):
 
 def model_pipelined(kv0, kv_end, P, div32, rings=True):
     """prefill_item128 and the pipelined prefill_item32: one 32-token tile per step, K loaded
-    four tiles ahead and V two, lookups of K(j+5) and V(j+3) after cover(T(j+3), T(j+6) - 1).
-    Every lane of either shape loads one of a tile's 32 tokens.  Returns (refills, fast steps)."""
+    K_AHEAD tiles ahead and V V_AHEAD, lookups of K(j + K_AHEAD + 1) and V(j + V_AHEAD + 1) after
+    cover(T(j + V_AHEAD + 1), T(j + K_AHEAD + 2) - 1).  Every lane of either shape loads one of a
+    tile's 32 tokens.  Returns (refills, fast steps)."""
     n = (kv_end - kv0 + 31) // 32
     T = lambda j: kv0 + 32 * np.asarray(j)  # noqa: E731
     js = np.arange(n + 1)
-    covers = [(kv0, kv0 + 6 * 32 - 1)] + [(kv0 + 32 * (j + 3), kv0 + 32 * (j + 6) - 1) for j in range(n + 1)]
+    covers = [(kv0, kv0 + (K_AHEAD + 2) * 32 - 1)] + [(kv0 + 32 * (j + V_AHEAD + 1), kv0 + 32 * (j + K_AHEAD + 2) - 1)
+                                                      for j in range(n + 1)]
     base, cnt, refills = window_states(kv_end, P, covers)
-    # prologue lookups K(0..4), V(0..2) under the first window
-    check_lookups(T(np.arange(5)), base[0], cnt[0], kv_end, P, 32)
-    # step j looks up K(j+5) and V(j+3) under the window after its cover()
-    check_lookups(T(js + 5), base[1:], cnt[1:], kv_end, P, 32)
-    check_lookups(T(js + 3), base[1:], cnt[1:], kv_end, P, 32)
+    # prologue lookups K(0 .. K_AHEAD), V(0 .. V_AHEAD) under the first window
+    check_lookups(T(np.arange(K_AHEAD + 1)), base[0], cnt[0], kv_end, P, 32)
+    # step j looks up K(j + K_AHEAD + 1) and V(j + V_AHEAD + 1) under the window after its cover()
+    check_lookups(T(js + K_AHEAD + 1), base[1:], cnt[1:], kv_end, P, 32)
+    check_lookups(T(js + V_AHEAD + 1), base[1:], cnt[1:], kv_end, P, 32)
     n_full = (kv_end - kv0) // 32 if div32 else 0
-    fast = (js >= 1) & (js + 5 < n_full)
+    fast = (js >= 1) & (js + K_AHEAD + 1 < n_full)
     if div32 and fast.any():
         # fast lookups: table[(kv0 + tok) / P + (j + ahead) (32 / P) - base], every token offset
         jf, tok = js[fast][:, None], np.arange(32)[None, :]
         bf, cf = base[1:][fast][:, None], cnt[1:][fast][:, None]
-        for ahead in (5, 3):
+        for ahead in (K_AHEAD + 1, V_AHEAD + 1):
             idx = (kv0 + tok) // P + (jf + ahead) * (32 // P) - bf
             want = _page_no(kv0 + 32 * (jf + ahead) + tok, kv_end, P) - bf
             assert np.array_equal(idx, want) and idx.min() >= 0 and (idx - cf).max() < 0
@@ -235,7 +241,11 @@ def _qo(lens):
 
 
 def test_constants_agree_with_the_kernel():
-    assert BATCHES_PER_STEP == 2 and MAX_IN_FLIGHT == 2 * BATCHES_PER_STEP and K_AHEAD == 4
+    """The kernel derives its lookahead from kIssueToUseSteps in the same way as this model."""
+    src = open(SRC).read()
+    assert re.search(r"constexpr int kKAhead = kIssueToUseSteps \+ 1, kVAhead = kIssueToUseSteps - 1;", src)
+    assert re.search(r"constexpr int kMaxBatchesInFlight = kDmaBatchesPerStep \* \(kIssueToUseSteps - 1\);", src)
+    assert BATCHES_PER_STEP == 2 and ISSUE_TO_USE >= 2 and MAX_IN_FLIGHT <= 4
 
 
 @pytest.mark.parametrize("n", range(1, 80))
@@ -289,10 +299,11 @@ def test_model_catches_planted_mistakes():
     with pytest.raises(AssertionError, match="outside the filled window"):
         kv_end = 3000
         n = (kv_end + 31) // 32
-        covers = [(0, 191)] + [(32 * (j + 3), 32 * (j + 6) - 1) for j in range(n + 1)]
+        covers = [(0, 32 * (K_AHEAD + 2) - 1)] + [(32 * (j + V_AHEAD + 1), 32 * (j + K_AHEAD + 2) - 1)
+                                                  for j in range(n + 1)]
         base, cnt, _ = window_states(kv_end, 1, covers, fill_short=1)
         js = np.arange(n + 1)
-        check_lookups(32 * (js + 5), base[1:], cnt[1:], kv_end, 1, 32)
+        check_lookups(32 * (js + K_AHEAD + 1), base[1:], cnt[1:], kv_end, 1, 32)
 
 
 @pytest.mark.parametrize("tile_q", [128, 64, 32])
