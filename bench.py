@@ -725,7 +725,7 @@ def summarize_profile(name):
                f"{rec['event_timed_us_per_call']:.2f} us per call (the kernels of one call: "
                f"{sum(kav[k] for k in case['call']):.2f} us in the trace).  Under the tracer every dispatch "
                "runs somewhat slower than in an untraced run of bench.py."]
-    if case["unit"] == "bytes":
+    if case["unit"] == "bytes" or case.get("traffic"):
         fs, fetch = counters("fetch", "FETCH_SIZE")
         ws, write = counters("write", "WRITE_SIZE")
         traffic = {k: int(round((fetch[k][0] * fs + write[k][0] * ws) * 1024)) for k in case["kernels"]}
@@ -734,24 +734,32 @@ def summarize_profile(name):
                     "write_kib_per_dispatch": {k: round(write[k][0], 1) for k in case["kernels"]},
                     "traffic_bytes_per_dispatch": traffic,
                     "traffic_bytes_per_call": sum(traffic[k] for k in case["call"])})
-        rec["traffic_over_algorithmic"] = round(rec["traffic_bytes_per_call"] / alg, 4)
-        rec["call_kernels_gbs"] = round(alg / (call_us * 1e-6) / 1e9, 1)
+        if case["unit"] == "bytes":
+            rec["traffic_over_algorithmic"] = round(rec["traffic_bytes_per_call"] / alg, 4)
+            rec["call_kernels_gbs"] = round(alg / (call_us * 1e-6) / 1e9, 1)
+        else:
+            rec["hbm_gbs"] = round(rec["traffic_bytes_per_call"] / (call_us * 1e-6) / 1e9, 1)
         md += ["", "HBM counters per dispatch (FETCH_SIZE and WRITE_SIZE passes), scaled by what the same counters "
                "read for the three 512 MiB device copies of `--copy-calib` (524,288 KiB read and written each): "
                f"FETCH_SIZE x {fs:.4f}, WRITE_SIZE x {ws:.4f}.", "",
                "| Kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes (scaled) |", "|---|---|---|---|"]
         for k in case["kernels"]:
             md.append(f"| `{k}` | {fetch[k][0]:,.1f} | {write[k][0]:,.1f} | {traffic[k]:,} |")
-        md += ["", f"Per call ({' + '.join(case['call'])}): {rec['traffic_bytes_per_call']:,} bytes of HBM traffic "
-               f"against {alg:,} algorithmic bytes (ratio {rec['traffic_over_algorithmic']:.4f}); the call's kernels "
-               f"take {call_us:.2f} us together = {rec['call_kernels_gbs']:,.1f} GB/s of algorithmic bytes "
-               f"({100 * rec['call_kernels_gbs'] / HBM_PEAK_GBS:.1f} % of 8 TB/s)."]
+        if case["unit"] == "bytes":
+            md += ["", f"Per call ({' + '.join(case['call'])}): {rec['traffic_bytes_per_call']:,} bytes of HBM traffic "
+                   f"against {alg:,} algorithmic bytes (ratio {rec['traffic_over_algorithmic']:.4f}); the call's "
+                   f"kernels take {call_us:.2f} us together = {rec['call_kernels_gbs']:,.1f} GB/s of algorithmic bytes "
+                   f"({100 * rec['call_kernels_gbs'] / HBM_PEAK_GBS:.1f} % of 8 TB/s)."]
+        else:
+            md += ["", f"Per call: {rec['traffic_bytes_per_call']:,} bytes of HBM traffic in {call_us:.2f} us = "
+                   f"{rec['hbm_gbs']:,.1f} GB/s ({100 * rec['hbm_gbs'] / HBM_PEAK_GBS:.1f} % of 8 TB/s): the K/V "
+                   "re-reads of the query tiles of one request are served by the L2 caches."]
         if "read_pages_kernel" in kav:
             pb = traffic["read_pages_kernel"]
             rec["read_probe_gbs"] = round(pb / (kav["read_pages_kernel"] * 1e-6) / 1e9, 1)
             md += ["", f"Read probe: {pb:,} bytes counted per dispatch in {kav['read_pages_kernel']:.2f} us = "
                    f"{rec['read_probe_gbs']:,.1f} GB/s, the streaming-read rate of this page-gather shape."]
-    else:
+    if case.get("sq"):
         rs = list(csv.DictReader(open(os.path.join(d + "_sq", "run_counter_collection.csv"))))
         key = case["call"][0]
         per = {}
@@ -937,15 +945,32 @@ def bench_shared_prefix(args):
         def single(s):
             api.run_decode(pf, wf, q, k, v, o=of, lse=lf, sm_scale=SM)
 
+        # the same two views as one composable plan (16-row tiles of 4 queries on the decode kernel:
+        # every tile reads the whole prefix, so this suits short prefixes)
+        cp = api.ComposablePlan([dict(kv_indptr=ip, kv_indices=ix, last_page_len=la, qo_indptr=qo),
+                                 dict(kv_indptr=sip, kv_indices=six, last_page_len=sla)],
+                                num_pages=b.num_pages, num_qo_heads=H_QO, num_kv_heads=H_KV, head_dim=D,
+                                page_size=b.page_size, num_workers=C2)
+        wc = api.alloc_workspace(cp)
+        cp.upload(wc)
+        oc, lc = torch.empty_like(q), torch.empty(R, H_QO, dtype=torch.float32, device="cuda")
+
+        def one_plan(s):
+            api.run_prefill(cp, wc, q, k, v, o=oc, lse=lc, sm_scale=SM)
+
         steps = max(10, args.steps // 2)
+        ms_p = time_calls(one_plan, steps, args.warmup)
+        ms_pg = graph_replay_ms(one_plan, steps, args.warmup)
         ms_c = time_calls(composed, steps, args.warmup)
         ms_s = time_calls(single, steps, args.warmup)
         ms_cg = graph_replay_ms(composed, steps, args.warmup)
         ms_sg = graph_replay_ms(single, steps, args.warmup)
         composed(0)
         single(0)
+        one_plan(0)
         torch.cuda.synchronize()
         diff = float((o.float() - of.float()).abs().max())
+        diff_p = float((oc.float() - of.float()).abs().max())
         per = H_KV * D * 2 * 2
         out[f"batch{R}_prefix{P}"] = {
             "composed_us": round(ms_c * 1e3, 2), "composed_graph_us": round(ms_cg * 1e3, 2),
@@ -954,10 +979,13 @@ def bench_shared_prefix(args):
             # (the small shape's eager calls are bound by the host's per-call cost: compare graphs)
             "graph_speedup": round(ms_sg / ms_cg, 2),
             "composed_bytes": (P + R * 128) * per, "single_level_bytes": R * (P + 128) * per,
-            "max_abs_diff_O_composed_vs_single": round(diff, 5)}
+            "max_abs_diff_O_composed_vs_single": round(diff, 5),
+            "composable_plan_us": round(ms_p * 1e3, 2), "composable_plan_graph_us": round(ms_pg * 1e3, 2),
+            "composable_plan_speedup": round(ms_s / ms_p, 2),
+            "max_abs_diff_O_composable_plan_vs_single": round(diff_p, 5)}
         log(f"shared prefix batch {R}, prefix {P}: composed {ms_c * 1e3:.1f} us (graph {ms_cg * 1e3:.1f}), "
             f"single level {ms_s * 1e3:.1f} us, max|O composed - O single| {diff:.2e}")
-        del q, k, v, o1, o2, o, of, w1, w2, wf
+        del q, k, v, o1, o2, o, of, oc, w1, w2, wf, wc
         torch.cuda.empty_cache()
     return out
 
@@ -1043,7 +1071,7 @@ def main():
         "data": "synthetic (seeded N(0,1) Q/K/V, random page permutation)",
         "config": {
             "workload": "batched paged decode bf16: batch 64, KV lengths U[512,8192], page size 16, "
-                        "32 query / 8 KV heads, head_dim 128, split-KV + merge",
+                        "32 query / 8 KV heads, head_dim 128, split-KV with the split requests folded in the kernel",
             "tokens": dec["tokens"], "algorithmic_bytes": dec["bytes"],
             "num_workers": dec["num_workers"], "work_items": dec["items"],
             "partial_slots": dec["slots"], "plan_host_us": round(dec["plan_us"], 1),

@@ -2,7 +2,8 @@
 Workload" §7.3 (Appendix Table 5 shapes: batch 64 with a 32,768-token prefix, batch 16 with a
 1,024-token prefix, 128-token suffixes), in the launch configuration bench.py times: the prefix
 view (one block row of all queries, non-causal, chunks of >= 256 keys), the suffix view (decode),
-their merge, and the single-level view, against the fp64 oracle.  Batch 16 is compared on every
+their merge, the two views as one composable plan, and the single-level view, against the fp64
+oracle.  Batch 16 is compared on every
 row; batch 64 on every fourth request, 16 of them (the oracle evaluates them one by one).
 
 Tolerances: bf16 inputs with fp32 accumulation -> O max-abs 2e-2, LSE max-abs 1e-2.
@@ -72,3 +73,15 @@ def test_shared_prefix_table5_shapes(R, P):
     compare(*cpu(states[1]), ro2, rl2, "bf16", "suffix view")
     compare(*cpu(states[2]), ruo, rul, "bf16", "single-level view")
     compare(*cpu((o, l)), ruo, rul, "bf16", "prefix (+) suffix vs union")
+
+    # the same two views as one composable plan (one attention and one merge launch)
+    cp = api.ComposablePlan([dict(kv_indptr=ip, kv_indices=ix, last_page_len=la, qo_indptr=qo),
+                             dict(kv_indptr=sip, kv_indices=six, last_page_len=sla)],
+                            num_pages=b.num_pages, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                            page_size=b.page_size, num_workers=C2)
+    wc = api.alloc_workspace(cp)
+    cp.upload(wc)
+    log(f"    composable plan: {cp.export()['num_slots']} partial slots")
+    oc, lc = api.run_prefill(cp, wc, q, k, v, sm_scale=sm)
+    torch.cuda.synchronize()
+    compare(*cpu((oc, lc)), ruo, rul, "bf16", "composable plan vs union")
