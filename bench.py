@@ -574,6 +574,7 @@ PROFILE_CASES = {
 SQ_COUNTERS = ("GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS "
                "SQ_WAVE_CYCLES SQ_WAIT_INST_ANY")
 PROFILE_STEPS = "--steps 20 --warmup 5"
+PROFILE_RAW = "rocprof_out"  # rocprofv3 output of the profile runs, relative to the repository root
 
 
 def profile_commands(name):
@@ -582,7 +583,7 @@ def profile_commands(name):
     cases, SQ counters for prefill."""
     case = PROFILE_CASES[name]
     run = f"python3 bench.py --profile-case {name} {PROFILE_STEPS}"
-    d = f"gpurun_out/prof/{name}"
+    d = f"{PROFILE_RAW}/{name}"
     cmds = [f"timeout -s KILL 300 rocprofv3 --kernel-trace --stats --output-format csv -d {d}_trace -o run -- {run} "
             f"--profile-out {d}_event.json"]
     if case["unit"] == "bytes" or case.get("traffic"):
@@ -665,7 +666,7 @@ def summarize_profile(name):
     import hashlib
 
     case = PROFILE_CASES[name]
-    d = os.path.join(ROOT, "gpurun_out", "prof", name)
+    d = os.path.join(ROOT, PROFILE_RAW, name)
     rows = list(csv.DictReader(open(os.path.join(d + "_trace", "run_kernel_stats.csv"))))
     disp = list(csv.DictReader(open(os.path.join(d + "_trace", "run_kernel_trace.csv"))))
     warm = int(PROFILE_STEPS.split("--warmup ")[1].split()[0])
@@ -1006,7 +1007,7 @@ def main():
     ap.add_argument("--profile-commands", choices=sorted(PROFILE_CASES), default=None,
                     help="print the rocprofv3 commands behind profiles/<name>.json")
     ap.add_argument("--summarize", choices=sorted(PROFILE_CASES), default=None,
-                    help="write profiles/<name>.json and .md from gpurun_out/prof/<name>_* (no GPU)")
+                    help="write profiles/<name>.json and .md from rocprof_out/<name>_* (no GPU)")
     args = ap.parse_args()
     if args.profile_commands:
         print("\n".join(profile_commands(args.profile_commands)))

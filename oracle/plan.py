@@ -18,7 +18,7 @@ scheduler as the pages describe it:
   eq. 11 linear cost) and §6.2 (integer chunk limit max(1, ceil(W / C)), ties broken
   by a stable id, heap of (cost, CTA id), ordered partial list per output tile).
 
-Readings taken where the pages leave a detail open (each is listed in the design doc):
+Readings taken where the pages leave a detail open:
 the query-tile set is {16, 32, 64, 128} (a tile is a multiple of the 16-row matrix
 instruction; 128 when the average exceeds 64); the per-item cost charges the query
 positions of the item's own tile (one for a decode request, at most T_q / g for a
