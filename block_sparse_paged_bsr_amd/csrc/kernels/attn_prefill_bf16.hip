@@ -1572,7 +1572,8 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
       const u32x4 v = *reinterpret_cast<__attribute__((address_space(3))) const u32x4*>(st + lr * RS + 2 * col);
       if (r < item.row_end) {
         const int64_t orow = int64_t(rq.q_start + r / a.g) * a.Hq + hk * a.g + r % a.g;
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) + orow * D + col) = v;
+        // (streaming: this kernel never reads the rows back)
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.o) + orow * D + col));
       }
     }
   } else {
