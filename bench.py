@@ -660,13 +660,15 @@ def run_profile_case(name, args):
             json.dump({"event_timed_us_per_call": round(ms * 1e3, 2), "steps": args.steps, "warmup": args.warmup}, f)
 
 
-def summarize_profile(name):
-    """profiles/<name>.json and .md from the rocprofv3 output of profile_commands(name)."""
+def summarize_profile(name, raw_dir=None, out_dir=None):
+    """profiles/<name>.json and .md from the rocprofv3 output of profile_commands(name) (raw_dir
+    and out_dir default to rocprof_out/ and profiles/ under the repository root)."""
     import csv
     import hashlib
 
     case = PROFILE_CASES[name]
-    d = os.path.join(ROOT, PROFILE_RAW, name)
+    d = os.path.join(raw_dir or os.path.join(ROOT, PROFILE_RAW), name)
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
     rows = list(csv.DictReader(open(os.path.join(d + "_trace", "run_kernel_stats.csv"))))
     disp = list(csv.DictReader(open(os.path.join(d + "_trace", "run_kernel_trace.csv"))))
     warm = int(PROFILE_STEPS.split("--warmup ")[1].split()[0])
@@ -791,9 +793,10 @@ def summarize_profile(name):
                f"2.5 PFLOP/s dense bf16)."]
     md += ["", f"Kernel sources (SHA-256 in `{name}.json`; bench.py uses these figures only while they match): "
            + ", ".join(f"`{p}`" for p in case["sources"]) + "."]
-    json.dump(rec, open(os.path.join(ROOT, "profiles", name + ".json"), "w"), indent=1)
-    open(os.path.join(ROOT, "profiles", name + ".md"), "w").write("\n".join(md) + "\n")
+    json.dump(rec, open(os.path.join(out_dir, name + ".json"), "w"), indent=1)
+    open(os.path.join(out_dir, name + ".md"), "w").write("\n".join(md) + "\n")
     print(json.dumps(rec, indent=1))
+    return rec
 
 
 def bench_cascade(args):
