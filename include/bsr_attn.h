@@ -106,8 +106,9 @@ typedef struct bsr_plan_desc {
  *   chunks are stably sorted by length, descending, and each goes to the worker of
  *   least accumulated cost (ties: lower worker id); an item costs alpha times the query
  *   positions of its tile (1 in decode) plus beta times its chunk length (eq. 11).  A tile with one chunk writes its
- *   final output; chunks of split tiles get partial slots, folded by the merge pass in
- *   KV order (deterministic, no atomics).
+ *   final output; chunks of split tiles get partial slots, folded in KV order
+ *   (deterministic; no atomics in the arithmetic) by the wave that writes a tile's last
+ *   slot on the bf16 decode kernel, otherwise by the merge pass.
  * Copies every host array, so the caller may free them on return.  Pure host code:
  * never touches the GPU.  *out receives the plan (NULL on error).
  */
@@ -239,7 +240,9 @@ int bsr_plan_export(const bsr_plan* plan, bsr_plan_view* view);
  * request has no keys (its empty state).  Otherwise (fp32, or the tiled kernel) the attention
  * launch is followed by the merge launch whenever the plan split a request.  The result does
  * not depend on which workgroup ran which work item.  sm_scale must be positive and finite
- * (1/sqrt(d) for the standard operator).
+ * (1/sqrt(d) for the standard operator).  The workspace holds the counters the kernels use to
+ * hand out work items and to count arrivals (zero between calls, reset by the kernels), so run
+ * calls on one workspace must not overlap; calls on different workspaces may.
  */
 int bsr_run_decode(const bsr_plan* plan, const void* ws, const void* q, const void* k_cache,
                    const void* v_cache, void* o, float* lse, int32_t dtype, float sm_scale,
@@ -272,6 +275,7 @@ int bsr_run_decode_scratch(const bsr_plan* plan, const void* q, const void* k_ca
  * open, and this is the OCP format with per-tensor scales.  k_scale and v_scale must be
  * positive and finite.  Supported where the bf16 decode kernel is (head_dim 64 or 128, at
  * most 16 query heads per KV head), else BSR_UNSUPPORTED.  Reads half the KV bytes of bf16.
+ * Split requests are combined by the merge launch (not inside the attention kernel).
  */
 int bsr_run_decode_e4m3(const bsr_plan* plan, const void* ws, const void* q, const void* k_cache,
                         const void* v_cache, void* o, float* lse, float sm_scale, float k_scale,
