@@ -185,6 +185,77 @@ def read_ceiling(pools, pages, steps, warmup, per_cu=(2, 4, 8, 16)):
     return best
 
 
+ISA_MIX_MODES = ["MFMA", "MFMA + 6 FMA", "MFMA + 8 FMA", "MFMA + 3 EXP", "MFMA + 4 EXP", "8 FMA", "8 EXP",
+                 "MFMA + 2 FMA + 2 EXP"]  # the slots of bsr_probe_issue_mix (include/bsr_probe.h)
+
+
+def isa_rates(out_md=None, iters=4096):
+    """Execution rates of the device behind the kernels' design (libbsr_probe.so execution-rate
+    probes): cycles per slot of the one-wave instruction mixes, LDS read rates of the prefill
+    kernel's operand patterns, and the L2-to-LDS copy rate of a CU.  Returns a dict; with out_md,
+    also writes it as a markdown table with the command that produced it."""
+    import ctypes
+    import torch
+    from block_sparse_paged_bsr_amd import _lib
+
+    L = _lib.probe()
+    st = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)  # noqa: E731
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    cyc = torch.zeros(4 * 1024, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
+    res = {"issue_mix_cycles_per_slot": {}, "lds_read": {}, "l2_to_lds": {}}
+    for mode, name in enumerate(ISA_MIX_MODES):
+        for n in (16, iters):  # the first launch warms the code up
+            assert L.bsr_probe_issue_mix(mode, n, vp(cyc), vp(sink), st()) == 0
+        torch.cuda.synchronize()
+        c = cyc[:2].cpu().tolist()
+        res["issue_mix_cycles_per_slot"][name] = round(c[0] / (8.0 * iters), 2)
+        res["clock_ghz"] = round(c[0] / (c[1] * 10.0), 3)
+    for pattern, (pname, per, nbytes) in enumerate((("ds_read_b128 (K pattern)", 8, 1024),
+                                                    ("ds_read_b64_tr_b16 (V pattern)", 16, 512))):
+        for waves in (1, 2, 4):
+            for n in (8, iters // 4):
+                assert L.bsr_probe_lds_read(pattern, waves, n, vp(cyc), vp(sink), st()) == 0
+            torch.cuda.synchronize()
+            mx = max(cyc[:waves].cpu().tolist())
+            n = iters // 4
+            res["lds_read"][f"{pname}, {waves} wave(s)"] = {
+                "cycles_per_instruction": round(mx / (n * per), 2),
+                "bytes_per_cycle_per_cu": round(n * per * nbytes * waves / mx, 1)}
+    src = torch.ones(1 << 16, dtype=torch.int32, device="cuda")  # 256 KB, L2-resident
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for waves, blocks in ((1, 1), (4, 1), (4, cus), (4, 2 * cus)):
+        for n in (8, iters // 4):
+            assert L.bsr_probe_l2_to_lds(vp(src), waves, blocks, n, vp(cyc), vp(sink), st()) == 0
+        torch.cuda.synchronize()
+        c = cyc[:4 * blocks].view(blocks, 4)[:, :waves]
+        mx = int(c.max())
+        n = iters // 4
+        per_cu = max(1, blocks // cus)  # workgroups sharing a CU
+        res["l2_to_lds"][f"{waves} wave(s) x {blocks} workgroup(s)"] = {
+            "cycles_per_8kb": round(mx / n, 1),
+            "bytes_per_cycle_per_cu": round(8192.0 * n * waves * per_cu / mx, 1)}
+    if out_md:
+        cmd = "python3 bench.py --isa-rates " + os.path.basename(out_md)
+        lines = ["# Execution rates of the device (libbsr_probe.so execution-rate probes)", "",
+                 f"Command: `{cmd}` (shader-clock cycles from s_memtime; clock {res['clock_ghz']} GHz "
+                 "from the same loop's real-time counter).", "",
+                 "One wave, cycles per slot (a slot = at most one `v_mfma_f32_32x32x16_bf16` and the vector "
+                 "instructions listed; each vector instruction reads a value written two slots earlier):", "",
+                 "| Slot | Cycles |", "|---|---|"]
+        lines += [f"| {k} | {v} |" for k, v in res["issue_mix_cycles_per_slot"].items()]
+        lines += ["", "LDS reads of the 128-row prefill kernel's operand patterns (one workgroup):", "",
+                  "| Pattern | Cycles per instruction per wave | Bytes per cycle per CU |", "|---|---|---|"]
+        lines += [f"| {k} | {v['cycles_per_instruction']} | {v['bytes_per_cycle_per_cu']} |"
+                  for k, v in res["lds_read"].items()]
+        lines += ["", "L2 to LDS (eight 1 KB `global_load_lds_dwordx4` per wave, then a wait; source L2-resident):", "",
+                  "| Waves x workgroups | Cycles per 8 KB per wave | Bytes per cycle per CU |", "|---|---|---|"]
+        lines += [f"| {k} | {v['cycles_per_8kb']} | {v['bytes_per_cycle_per_cu']} |" for k, v in res["l2_to_lds"].items()]
+        with open(out_md, "w") as f:
+            f.write("\n".join(lines) + "\n")
+    return res
+
+
 def graph_replay_ms(step, steps, warmup, variants=3):
     """Per-step time when each step is a captured HIP graph replayed (one graph per KV pool
     of the rotation): the plan-once, replay-per-step loop of a serving engine."""
@@ -1011,6 +1082,8 @@ def main():
                     help="print the rocprofv3 commands behind profiles/<name>.json")
     ap.add_argument("--summarize", choices=sorted(PROFILE_CASES), default=None,
                     help="write profiles/<name>.json and .md from rocprof_out/<name>_* (no GPU)")
+    ap.add_argument("--isa-rates", default=None, metavar="OUT.md",
+                    help="run the execution-rate probes of libbsr_probe.so, print them and write OUT.md")
     args = ap.parse_args()
     if args.profile_commands:
         print("\n".join(profile_commands(args.profile_commands)))
@@ -1031,6 +1104,9 @@ def main():
               "hbm_gib": round(props.total_memory / 2**30, 1), "torch": torch.__version__,
               "hip": getattr(torch.version, "hip", None)}
     log(f"device: {device}")
+    if args.isa_rates:
+        print(json.dumps(isa_rates(args.isa_rates)), flush=True)
+        return
     if args.copy_calib:
         copy_calibration()
     if args.profile_case:

@@ -9,7 +9,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbsr_attn.so")
-PROBE_PATH = os.path.join(HERE, "libbsr_probe.so")  # include/bsr_probe.h: HBM read probe
+PROBE_PATH = os.path.join(HERE, "libbsr_probe.so")  # include/bsr_probe.h: HBM read and rate probes
 
 BSR_OK = 0
 BSR_INVALID_ARG = -1
@@ -108,14 +108,14 @@ EXPORTED = [
     "bsr_version",
 ]
 
-PROBE_EXPORTED = ["bsr_probe_read_pages"]
+PROBE_EXPORTED = ["bsr_probe_read_pages", "bsr_probe_issue_mix", "bsr_probe_lds_read", "bsr_probe_l2_to_lds"]
 
 _lib = None
 _probe = None
 
 
 def probe():
-    """The HBM read probe library (raises if it was not built)."""
+    """The probe library (raises if it was not built)."""
     global _probe
     if _probe is not None:
         return _probe
@@ -129,6 +129,13 @@ def probe():
     vp = C.c_void_p
     L.bsr_probe_read_pages.argtypes = [vp, vp, vp, C.c_int64, C.c_int64, C.c_int32, C.c_uint32, vp, vp]
     L.bsr_probe_read_pages.restype = C.c_int
+    i32 = C.c_int32
+    L.bsr_probe_issue_mix.argtypes = [i32, i32, vp, vp, vp]
+    L.bsr_probe_issue_mix.restype = C.c_int
+    L.bsr_probe_lds_read.argtypes = [i32, i32, i32, vp, vp, vp]
+    L.bsr_probe_lds_read.restype = C.c_int
+    L.bsr_probe_l2_to_lds.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+    L.bsr_probe_l2_to_lds.restype = C.c_int
     _probe = L
     return L
 

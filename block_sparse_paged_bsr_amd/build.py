@@ -28,7 +28,7 @@ SOURCES = [
     os.path.join(CSRC, "kernels", "attn_decode_bf16.hip"),
     os.path.join(CSRC, "kernels", "merge.hip"),
 ]
-PROBE_SOURCES = [os.path.join(CSRC, "hbm_probe.hip")]
+PROBE_SOURCES = [os.path.join(CSRC, "hbm_probe.hip"), os.path.join(CSRC, "isa_probes.hip")]
 
 ARCH = os.environ.get("BSR_OFFLOAD_ARCH", "gfx950")
 

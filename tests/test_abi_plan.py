@@ -41,7 +41,8 @@ def test_header_symbols_exported():
 
 
 def test_probe_header_symbols_exported():
-    """include/bsr_probe.h against libbsr_probe.so (the HBM read probe bench.py uses)."""
+    """include/bsr_probe.h against libbsr_probe.so (the HBM read and execution-rate probes
+    bench.py uses): every declaration exported, arguments checked on the host before a launch."""
     if not os.path.exists(_lib.PROBE_PATH):
         pytest.skip("libbsr_probe.so not built")
     src = open(os.path.join(ROOT, "include", "bsr_probe.h")).read()
@@ -57,6 +58,16 @@ def test_probe_header_symbols_exported():
     assert L.bsr_probe_read_pages(one, one, one, 1, 4096, 0, 0, one, None) == -1
     assert L.bsr_probe_read_pages(one, one, one, -1, 4096, 1, 0, one, None) == -1
     assert L.bsr_probe_read_pages(one, one, one, 0, 4096, 1, 0, one, None) == 0
+    assert L.bsr_probe_issue_mix(-1, 1, one, one, None) == -1
+    assert L.bsr_probe_issue_mix(8, 1, one, one, None) == -1
+    assert L.bsr_probe_issue_mix(0, 0, one, one, None) == -1
+    assert L.bsr_probe_issue_mix(0, 1, None, one, None) == -1
+    assert L.bsr_probe_lds_read(2, 1, 1, one, one, None) == -1
+    assert L.bsr_probe_lds_read(0, 5, 1, one, one, None) == -1
+    assert L.bsr_probe_lds_read(0, 1, 1, one, None, None) == -1
+    assert L.bsr_probe_l2_to_lds(None, 1, 1, 1, one, one, None) == -1
+    assert L.bsr_probe_l2_to_lds(one, 0, 1, 1, one, one, None) == -1
+    assert L.bsr_probe_l2_to_lds(one, 1, 0, 1, one, one, None) == -1
 
 
 def _oracle_as_export(p):
