@@ -371,6 +371,40 @@ __device__ __forceinline__ void dma_fragments(const uint16_t* src, const lds_u8*
   }
 }
 
+// The K and V batches of one steady pipeline step in one asm block (NF = 2 or 4 fragments each):
+// ksrc / vsrc are this lane's 16-byte sources of fragment 0, kdst / vdst the wave's first LDS
+// fragments (uniform).  M0 is written straight from the base plus the fragment's offset
+// b (1024 - 64), and saved and restored once for the whole block.  Same loads, in the same order,
+// as dma_fragments<NF> for K followed by dma_fragments<NF> for V.
+#define BSR_DMA_FRAG(src, base, b) \
+  "s_add_u32 m0, " base ", " #b " * 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 " src ", off offset:" #b " * 64\n\t"
+template <int NF>
+__device__ __forceinline__ void dma_kv(const uint16_t* ksrc, uint32_t kdst, const uint16_t* vsrc, uint32_t vdst) {
+  static_assert(NF == 2 || NF == 4, "two or four fragments per batch");
+  static_assert(1024 - 64 == 960, "M0 step between fragments");
+  uint32_t saved;
+  if constexpr (NF == 4) {
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 BSR_DMA_FRAG("%1", "%3", 0) BSR_DMA_FRAG("%1", "%3", 1) BSR_DMA_FRAG("%1", "%3", 2)
+                 BSR_DMA_FRAG("%1", "%3", 3) BSR_DMA_FRAG("%2", "%4", 0) BSR_DMA_FRAG("%2", "%4", 1)
+                 BSR_DMA_FRAG("%2", "%4", 2) BSR_DMA_FRAG("%2", "%4", 3)
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(ksrc), "v"(vsrc), "s"(kdst), "s"(vdst)
+                 : "memory", "scc");
+  } else {
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 BSR_DMA_FRAG("%1", "%3", 0) BSR_DMA_FRAG("%1", "%3", 1)
+                 BSR_DMA_FRAG("%2", "%4", 0) BSR_DMA_FRAG("%2", "%4", 1)
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(ksrc), "v"(vsrc), "s"(kdst), "s"(vdst)
+                 : "memory", "scc");
+  }
+}
+#undef BSR_DMA_FRAG
+
+
 // LDS-DMA loads of the K (V) half of the 64-token tile at t0 into one array: wave w loads
 // token group w, D/32 fragments; `page` comes from k_page (v_page) one step earlier
 template <int D, class PG>
@@ -1450,6 +1484,7 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
     pin(pcur[1]);
     pin(Snext[0]);
     pin(Snext[1]);
+    asm volatile("" : "+v"(lsum[0]), "+v"(lsum[1]));  // (the row sums too)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int b = 0; b < 2; ++b) l[b] += lsum[b];
@@ -1519,11 +1554,65 @@ __device__ __forceinline__ void prefill_item128(const RunArgs& a, const ItemRec&
     rescale(any);
     mask(Snext, T(j + 1));
   };
+  // Steady steps: the steps j (from a multiple of 4 on) for which every test of step() comes out
+  // the same way: no window refill (the window holds the item), a full lookahead tile in the fast
+  // page class, a wait for kMaxBatchesInFlight batches, and a next score tile that needs no mask.
+  // They run as straight-line code, four per loop trip, so that j mod 4 and with it every LDS slot
+  // is known at compile time; loads, waits and barriers are those step() would issue.
+  int j_fast = -1, n_quads = 0;  // (uniform)
+  if constexpr (PG == kPageDiv32) {
+    if (window_holds_item) {
+      int hi = n_full - kKAhead - 2;                // j + kKAhead + 1 < n_full
+      hi = min(hi, (min_lim - kv0) / 32 - 2);       // T(j + 1) + 32 <= min_lim
+      int lo = 1;                                   // V(j - 1) exists
+      if constexpr (VAR) {
+        if (var[0].max_lo > kv0) lo = max(lo, (var[0].max_lo - kv0 + 31) / 32 - 1);  // T(j + 1) >= max_lo
+      }
+      lo = (lo + 3) & ~3;
+      if (hi >= lo) {
+        j_fast = lo;
+        n_quads = (hi - lo + 1) / 4;
+      }
+    }
+  }
+  const uint32_t lds_k = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sl.k0() + wave * KB * FRAG)));
+  const uint32_t lds_v = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sl.v0() + wave * KB * FRAG)));
+  auto slot_off = [](int j) { return ((j >> 1) & 1) * PF<D>::SLOT + (j & 1) * HALF; };
+  auto fast_step = [&](auto qc, int j, f32x16 (&Scur)[2], f32x16 (&Snext)[2], const u32x4 (&pprev)[2][2],
+                       u32x4 (&pcur)[2][2]) {
+    constexpr int q = decltype(qc)::value;  // j mod 4
+    BSR_WAIT_VMCNT(kMaxBatchesInFlight * NF);
+    __builtin_amdgcn_s_barrier();
+    const int32_t nk2 = page_k_fast(j + kKAhead + 1), nv2 = page_v_fast(j + kVAhead + 1);
+    dma_kv<NF>(reinterpret_cast<const uint16_t*>(uint64_t(uint32_t(nk)) * page_bytes + k_add),
+            lds_k + slot_off((q + kKAhead) & 3),
+            reinterpret_cast<const uint16_t*>(uint64_t(uint32_t(nv)) * page_bytes + v_add),
+            lds_v + slot_off((q + kVAhead) & 3));
+    nk = nk2;
+    nv = nv2;
+    __builtin_amdgcn_sched_barrier(0);
+    const bool any = fused(sl.k0() + slot_off((q + 1) & 3), sl.v0() + slot_off((q + 3) & 3), Snext, Scur, pprev, pcur);
+    rescale(any);
+  };
+  using Q0 = std::integral_constant<int, 0>;
+  using Q1 = std::integral_constant<int, 1>;
+  using Q2 = std::integral_constant<int, 2>;
+  using Q3 = std::integral_constant<int, 3>;
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int i = 0; i < 2; ++i) pb[b][i] = u32x4{0u, 0u, 0u, 0u};  // P(-1)
   for (int j = 0;; j += 2) {
+    if (j == j_fast) {
+      for (int i = 0; i < n_quads; ++i, j += 4) {
+        fast_step(Q0{}, j, Sa, Sb, pb, pa);
+        fast_step(Q1{}, j + 1, Sb, Sa, pa, pb);
+        fast_step(Q2{}, j + 2, Sa, Sb, pb, pa);
+        fast_step(Q3{}, j + 3, Sb, Sa, pa, pb);
+      }
+    }
     step(j, Sa, Sb, pb, pa);
     if (j + 1 > n) break;
     step(j + 1, Sb, Sa, pa, pb);
