@@ -380,7 +380,7 @@ __device__ __forceinline__ void dma_fragments(const uint16_t* src, const lds_u8*
   "s_add_u32 m0, " base ", " #b " * 960\n\ts_nop 0\n\tglobal_load_lds_dwordx4 " src ", off offset:" #b " * 64\n\t"
 template <int NF>
 __device__ __forceinline__ void dma_kv(const uint16_t* ksrc, uint32_t kdst, const uint16_t* vsrc, uint32_t vdst) {
-  static_assert(NF == 2 || NF == 4, "two or four fragments per batch");
+  static_assert(NF == 1 || NF == 2 || NF == 4, "one, two or four fragments per batch");
   static_assert(1024 - 64 == 960, "M0 step between fragments");
   uint32_t saved;
   if constexpr (NF == 4) {
@@ -392,10 +392,17 @@ __device__ __forceinline__ void dma_kv(const uint16_t* ksrc, uint32_t kdst, cons
                  : "=&s"(saved)
                  : "v"(ksrc), "v"(vsrc), "s"(kdst), "s"(vdst)
                  : "memory", "scc");
-  } else {
+  } else if constexpr (NF == 2) {
     asm volatile("s_mov_b32 %0, m0\n\t"
                  BSR_DMA_FRAG("%1", "%3", 0) BSR_DMA_FRAG("%1", "%3", 1)
                  BSR_DMA_FRAG("%2", "%4", 0) BSR_DMA_FRAG("%2", "%4", 1)
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(ksrc), "v"(vsrc), "s"(kdst), "s"(vdst)
+                 : "memory", "scc");
+  } else {
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 BSR_DMA_FRAG("%1", "%3", 0) BSR_DMA_FRAG("%2", "%4", 0)
                  "s_mov_b32 m0, %0"
                  : "=&s"(saved)
                  : "v"(ksrc), "v"(vsrc), "s"(kdst), "s"(vdst)
@@ -898,6 +905,7 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
       // to their first use, after the rescale branch
       pin(pcur);
       pin(Snext);
+      asm volatile("" : "+v"(lsum));  // (the row sum too)
       __builtin_amdgcn_sched_barrier(0);
       l += lsum;
       return any;
@@ -961,10 +969,60 @@ __device__ __forceinline__ void prefill_item32(const RunArgs& a, const ItemRec& 
       rescale(any);
       mask(Snext, T(j + 1));
     };
+    // Steady steps, as in the 128-row shape: the steps j (from a multiple of 4 on) for which the
+    // window holds the item, the lookahead tiles are full tiles of the fast page class, the wait
+    // is for kMaxBatchesInFlight batches and (without VAR) the next score tile needs no mask run
+    // as straight-line code, four per loop trip, with every LDS slot known at compile time.  With
+    // VAR the mask (which also applies the soft cap and the custom mask) runs in every step.
+    int j_fast = -1, n_quads = 0;  // (uniform)
+    if constexpr (PG == kPageDiv32) {
+      if (window_holds_item) {
+        int hi = n_full - kKAhead - 2;                                    // j + kKAhead + 1 < n_full
+        if constexpr (!VAR) hi = min(hi, (min_lim - kv0) / 32 - 2);       // T(j + 1) + 32 <= min_lim
+        constexpr int lo = 4;                                             // (V(j - 1) exists from j = 1)
+        if (hi >= lo) {
+          j_fast = lo;
+          n_quads = (hi - lo + 1) / 4;
+        }
+      }
+    }
+    const uint32_t lds_k = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sl.k0() + f0 * FRAG)));
+    const uint32_t lds_v = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sl.v0() + f0 * FRAG)));
+    auto slot_off = [](int j) { return ((j >> 1) & 1) * PF<D>::SLOT + (j & 1) * HALF; };
+    auto fast_step = [&](auto qc, int j, f32x16& Scur, f32x16& Snext, const u32x4 (&pprev)[2], u32x4 (&pcur)[2]) {
+      constexpr int q = decltype(qc)::value;  // j mod 4
+      BSR_WAIT_VMCNT(kMaxBatchesInFlight * NF);
+      __builtin_amdgcn_s_barrier();
+      const int32_t nk2 = page_k_fast(j + kKAhead + 1), nv2 = page_v_fast(j + kVAhead + 1);
+      dma_kv<NF>(reinterpret_cast<const uint16_t*>(uint64_t(uint32_t(nk)) * page_bytes + k_add),
+                 lds_k + slot_off((q + kKAhead) & 3),
+                 reinterpret_cast<const uint16_t*>(uint64_t(uint32_t(nv)) * page_bytes + v_add),
+                 lds_v + slot_off((q + kVAhead) & 3));
+      nk = nk2;
+      nv = nv2;
+      __builtin_amdgcn_sched_barrier(0);
+      const bool any = fused(sl.k0() + slot_off((q + 1) & 3), sl.v0() + slot_off((q + 3) & 3), Snext, Scur, pprev, pcur);
+      rescale(any);
+      if constexpr (VAR) mask(Snext, T(j + 1));
+    };
+    using Q0 = std::integral_constant<int, 0>;
+    using Q1 = std::integral_constant<int, 1>;
+    using Q2 = std::integral_constant<int, 2>;
+    using Q3 = std::integral_constant<int, 3>;
 #pragma unroll
     for (int i = 0; i < 2; ++i) pb[i] = u32x4{0u, 0u, 0u, 0u};  // P(-1)
     // two steps per iteration so that the register roles alternate without copies
     for (int j = 0;; j += 2) {
+      if (j == j_fast) {
+        for (int i = 0; i < n_quads; ++i, j += 4) {
+          fast_step(Q0{}, j, Sa, Sb, pb, pa);
+          fast_step(Q1{}, j + 1, Sb, Sa, pa, pb);
+          fast_step(Q2{}, j + 2, Sa, Sb, pb, pa);
+          fast_step(Q3{}, j + 3, Sb, Sa, pa, pb);
+        }
+      }
       step(j, Sa, Sb, pb, pa);
       if (j + 1 > n) break;
       step(j + 1, Sb, Sa, pa, pb);
