@@ -132,10 +132,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
   // The work item record carries everything this kernel needs (rows, KV range, slot, query and
   // page-list starts).  The next item is claimed and its record fetched in the second-to-last step
   // of the current one, and its queries and first page ids issued in the last step, so that a new
-  // item starts with only its first rows to wait for.
+  // item starts with only its first rows to wait for.  The grid's workgroups are all resident and
+  // start together, so the first round needs no counter: workgroup b takes ticket b, and the
+  // counter hands out tickets gridDim.x, gridDim.x + 1, ... to the workgroups that finish first
+  // (no burst of atomics on one address at the start of every call).
   int32_t* tk = a.tickets + 2 * blockIdx.y;
   auto draw = [&]() -> int {
-    if (threadIdx.x == 0) s_ticket = __hip_atomic_fetch_add(tk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0)
+      s_ticket = int(gridDim.x) + __hip_atomic_fetch_add(tk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     const int t = s_ticket;
     __syncthreads();  // every wave has read it before the next draw writes it
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
   };
   constexpr int NPRE = KV8 ? 4 : 2;  // page ids of the first two steps (16 tokens each)
   const int num_items = a.num_items;
-  int t = draw();
+  int t = blockIdx.x;
   ItemRec next = a.items[a.lpt[t < num_items ? t : 0]];
   int next_mi = a.imerge[a.lpt[t < num_items ? t : 0]];
   bf16x8 qb[KB], qn[KB];
