@@ -200,12 +200,28 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
       const int off = a.p_shift >= 0 ? (tc & ((1 << a.p_shift) - 1)) : tc - (tc / a.P) * a.P;
       return ((int64_t(page) * a.P + off) * a.Hk + hk) * (D * ES) + j * 16;
     };
+    // bf16 V rows go through LDS anyway, so their loads read whole pieces of the token slices:
+    // load i of a step reads tokens TPI i .. TPI i + TPI - 1 of the step, lane (vt, vc) the
+    // 16-byte chunk vc of token TPI i + vt (one instruction covers whole 128-byte lines), with
+    // that token's page taken from the lane that looked it up
+    constexpr int CPT = D / 8, TPI = 64 / CPT;  // 16-byte chunks per slice, tokens per load
+    static_assert(KV8 || TPI * NL == 16, "one step's 16 tokens in NL loads");
+    const int vt = lane / CPT, vc = lane % CPT;
     auto load_rows = [&](u32x4 (&kd)[NL], u32x4 (&vd)[NL], int t, int32_t page) {
       const int64_t base = row_base(t, page);
 #pragma unroll
-      for (int l = 0; l < NL; ++l) {
-        kd[l] = *reinterpret_cast<const u32x4*>(K + base + 64 * l);
-        vd[l] = *reinterpret_cast<const u32x4*>(V + base + 64 * l);
+      for (int l = 0; l < NL; ++l) kd[l] = *reinterpret_cast<const u32x4*>(K + base + 64 * l);
+      if constexpr (KV8) {
+#pragma unroll
+        for (int l = 0; l < NL; ++l) vd[l] = *reinterpret_cast<const u32x4*>(V + base + 64 * l);
+      } else {
+        const int ts = t - n;  // the step's first token (lane n carries token ts + n)
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          const int tok = TPI * i + vt;
+          const int32_t pg = __shfl(page, tok, 64);
+          vd[i] = *reinterpret_cast<const u32x4*>(V + row_base(ts + tok, pg) - j * 16 + vc * 16);
+        }
       }
     };
     // one step: tokens t0 .. t0 + 15 (lane n: token t0 + n) from the rows in kr / vr
@@ -236,7 +252,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
             *reinterpret_cast<u32x4*>(Vs + n * VS + 64 * l + 16 * j + 8 * hb) = u32x4{x0[0], x0[1], x1[0], x1[1]};
           }
         } else {
-          *reinterpret_cast<u32x4*>(Vs + n * VS + 32 * l + 8 * j) = vr[l];
+          *reinterpret_cast<u32x4*>(Vs + (TPI * l + vt) * VS + 8 * vc) = vr[l];
         }
       }
 
