@@ -313,3 +313,104 @@ def test_page_window_refill_gpu_case(tile_q):
     r = _run_plan([5000], _qo([5000]), 1, 1, True, tile_q=tile_q, shapes=("pipelined", "loop"), Hq=8, Hk=2,
                   pool=5300, seed=11)
     assert r["refills"] > 0
+
+
+# ---- steady steps: the straight-line steps of the pipelined shapes ----
+# The kernels run a subset of an item's steps as straight-line code (four per loop trip, LDS
+# slots fixed at compile time, a fixed wait, no window test and, without VAR in the 128-row
+# shape, no mask).  The bounds below are the kernels' (C++ integer division truncates toward
+# zero); the checks are the conditions under which those steps may skip the tests.
+
+def _trunc_div(a, b):
+    q = abs(a) // b
+    return q if a >= 0 else -q
+
+
+def steady_steps(kv0, kv_end, min_lim, window_holds, div32, max_lo=None, mask_every_step=False, hi_slack=0):
+    """Steps j of one item that run as steady steps: from j_fast (a multiple of 4) n_quads
+    quads.  max_lo: the sliding window's largest lower bound over the tile's rows (128-row shape
+    with VAR); mask_every_step: the 4-wave shape with VAR, whose steady steps apply the mask.
+    (hi_slack plants a mistake: a last steady step that many steps too late.)"""
+    if not (div32 and window_holds):
+        return []
+    n_full = (kv_end - kv0) // 32
+    hi = n_full - K_AHEAD - 2 + hi_slack
+    if not mask_every_step:
+        hi = min(hi, _trunc_div(min_lim - kv0, 32) - 2 + hi_slack)
+    lo = 1
+    if max_lo is not None and max_lo > kv0:
+        lo = max(lo, (max_lo - kv0 + 31) // 32 - 1)
+    lo = (lo + 3) & ~3
+    if hi < lo:
+        return []
+    return list(range(lo, lo + 4 * ((hi - lo + 1) // 4)))
+
+
+def check_steady(kv0, kv_end, min_lim, steps, max_lo=None, mask_every_step=False):
+    n = (kv_end - kv0 + 31) // 32
+    n_full = (kv_end - kv0) // 32
+    for j in steps:
+        assert 1 <= j <= n, "a steady step outside the item"
+        # the model's fast-step condition: lookups and loads of full tiles of the fast page class
+        assert j + K_AHEAD + 1 < n_full, f"steady step {j} of {n_full} full tiles loads a partial tile"
+        t1 = kv0 + 32 * (j + 1)  # first key of the score tile the step computes
+        if not mask_every_step:
+            assert t1 + 32 <= min_lim, f"steady step {j} skips the causal mask of tile {j + 1}"
+            if max_lo is not None:
+                assert t1 >= max_lo, f"steady step {j} skips the window mask of tile {j + 1}"
+    assert steps == sorted(steps) and (not steps or steps[0] % 4 == 0), "steady steps start at a multiple of 4"
+    assert len(steps) % 4 == 0
+
+
+def _steady_over_plan(kv_lens, qo_lens, P, C, causal, window_left=-1, shape="128", hi_slack=0, pool=None):
+    ip, ix, last = _tables(kv_lens, P, 0, pool)
+    qo = _qo(qo_lens)
+    p = api.Plan(ip, ix, last, num_pages=pool or max(len(ix), 1), num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                 page_size=P, qo_indptr=qo, causal=causal, num_workers=C, tile_q=128, window_left=window_left)
+    e = p.export()
+    g = 4
+    div32 = P <= 32 and (P & (P - 1)) == 0
+    total = 0
+    for it in e["items"]:
+        req, r0, r1, kv0, kl = int(it[0]), int(it[2]), int(it[3]), int(it[4]), int(it[5])
+        kv_end = kv0 + kl
+        lq, lk = int(qo[req + 1] - qo[req]), int(kv_lens[req])
+        min_lim = min(kv_end, lk - lq + r0 // g + 1) if causal else kv_end
+        window_holds = _page_no(kv_end - 1, kv_end, P) - _page_no(kv0, kv_end, P) < PAGE_WINDOW
+        max_lo = (lk - lq - window_left + (r1 - 1) // g) if window_left >= 0 else None
+        var = window_left >= 0
+        if shape == "128":
+            steps = steady_steps(kv0, kv_end, min_lim, window_holds, div32, max_lo if var else None,
+                                 hi_slack=hi_slack)
+            check_steady(kv0, kv_end, min_lim, steps, max_lo if var else None)
+        else:  # the 4-wave shape (128-row tiles of soft-capped plans): with VAR the mask runs in every step
+            steps = steady_steps(kv0, kv_end, min_lim, window_holds, div32, mask_every_step=var, hi_slack=hi_slack)
+            check_steady(kv0, kv_end, min_lim, steps, mask_every_step=var)
+        total += len(steps)
+    return total
+
+
+@pytest.mark.parametrize("shape", ["128", "32"])
+def test_steady_steps_ragged_and_uniform_plans(shape):
+    """The ragged causal prefill and uniform batches (causal and not), page sizes 16 and 1."""
+    lens = I.prefill_lengths(0)
+    assert _steady_over_plan(lens, lens, 16, 64, True, shape=shape) > 0
+    assert _steady_over_plan([4096] * 4, [4096] * 4, 16, 64, True, shape=shape) > 0
+    assert _steady_over_plan([3000, 700, 45], [3000, 700, 45], 1, 16, False, shape=shape, pool=1 << 14) > 0
+    assert _steady_over_plan([2048] * 2, [300, 2048], 8, 8, True, shape=shape) > 0
+
+
+@pytest.mark.parametrize("shape", ["128", "32"])
+def test_steady_steps_sliding_window(shape):
+    """Windowed causal prefill (the VAR instantiations): windows of 1024 and 100 keys."""
+    lens = I.prefill_lengths(0)
+    for w in (1023, 99):
+        _steady_over_plan(lens, lens, 16, 64, True, window_left=w, shape=shape)
+
+
+def test_steady_steps_planted_mistake():
+    """A last steady step one step too late is caught (it would load a partial tile or skip a
+    mask)."""
+    lens = I.prefill_lengths(0)
+    with pytest.raises(AssertionError, match="partial tile|skips the"):
+        _steady_over_plan(lens, lens, 16, 64, True, hi_slack=1)
