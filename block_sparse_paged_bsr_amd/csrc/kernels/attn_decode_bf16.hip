@@ -64,13 +64,18 @@ constexpr int decode_vs_bytes() { return 16 * (D + 8) * 2; }  // one wave's V st
 // relaxed agent-scope atomic load or store, so that every access is coherent across the XCDs'
 // separate L2 caches without a whole-cache write-back or invalidation.
 constexpr int kAgentScope = 16;  // sc1
+// partial states whose loads a folding lane issues together
+constexpr int kFoldSlots = 8;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(void* p) {
   return __builtin_amdgcn_make_buffer_rsrc(p, 0, 0x7fffffff, 0x00020000);
 }
 #define BSR_DECODE_WAIT_VMCNT0() __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8))
 
-template <int D, bool CAP, bool KV8>
+// FOLD: the plan's split tiles are folded inside this kernel (RunArgs::fold_in_kernel); without
+// it the kernel carries no fold code, and the merge pass folds them.
+template <int D, bool CAP, bool KV8, bool FOLD>
 __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(RunArgs a) {
+  static_assert(!(KV8 && FOLD), "E4M3 decode keeps the merge launch");
   constexpr int KB = D / 32;  // k-blocks of the score product
   constexpr int DB = D / 16;  // d-blocks of the output product
   constexpr int VS = D + 8;   // LDS row stride (elements); 16-byte aligned rows
@@ -149,7 +154,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
   const int num_items = a.num_items;
   int t = blockIdx.x;
   ItemRec next = a.items[a.lpt[t < num_items ? t : 0]];
-  int next_mi = a.imerge[a.lpt[t < num_items ? t : 0]];
+  int next_mi = FOLD ? a.imerge[a.lpt[t < num_items ? t : 0]] : -1;
   bf16x8 qb[KB], qn[KB];
   int32_t pre[NPRE];
   bool have_pre = false;
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
       more = t < num_items;
       if (more) {
         next = a.items[a.lpt[t]];
-        next_mi = a.imerge[a.lpt[t]];
+        if constexpr (FOLD) next_mi = a.imerge[a.lpt[t]];
       }
       claimed = true;
     };
@@ -363,7 +368,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
         if (j == 0) a.lse[orow] = lse;
       } else {
         const int64_t prow = (int64_t(item.slot) * a.Hk + hk) * a.Tq + n;  // row n of the tile
-        if (a.fold_in_kernel) {  // read by whichever workgroup folds the tile: agent-scope stores
+        if constexpr (FOLD) {  // read by whichever workgroup folds the tile: agent-scope stores
           const int32_t ob = int32_t(prow * D + 4 * j) * 4;
 #pragma unroll
           for (int db = 0; db < DB; ++db)
@@ -388,61 +393,71 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
     // itself in; the wave that completes the count reads the tile's states in the plan's slot order
     // (KV order) and writes the final output, so the result does not depend on which workgroup
     // folded it, and returns the counter to zero for the next call.
-    if (a.fold_in_kernel && item_mi >= 0) {  // (uniform: all waves of the workgroup run the item)
-      const MergeRec mr = a.merge[item_mi];
-      const int ns = mr.slot_count;
-      const int* __restrict__ sl = a.mslots + mr.slot_begin;
-      const int sid0 = sl[0], sid1 = sl[ns > 1 ? 1 : 0];  // (fetched while the stores complete)
-      BSR_DECODE_WAIT_VMCNT0();
-      int32_t* ctr = a.arrive + int64_t(item_mi) * a.Hk + hk;
-      int arrived = 0;
-      if (lane == 0) arrived = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      arrived = __builtin_amdgcn_readfirstlane(arrived);
-      if (arrived == ns - 1) {
-        if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (n < item.row_end - item.row_start) {
-          // the states of this lane's row, two slots per round (loads issued together), folded
+    if constexpr (FOLD) {
+      if (item_mi >= 0) {  // (uniform: all waves of the workgroup run the item)
+        const MergeRec mr = a.merge[item_mi];
+        const int ns = mr.slot_count;
+        const int* __restrict__ sl = a.mslots + mr.slot_begin;
+        // lane u < kFoldSlots holds slot id u of the tile (fetched while the stores complete)
+        const int sid_lane = sl[min(lane % kFoldSlots, ns - 1)];
+        BSR_DECODE_WAIT_VMCNT0();
+        int32_t* ctr = a.arrive + int64_t(item_mi) * a.Hk + hk;
+        int arrived = 0;
+        if (lane == 0) arrived = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        arrived = __builtin_amdgcn_readfirstlane(arrived);
+        if (arrived == ns - 1) {
+          if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          // every lane folds 8 values of one row: lane c of a pass takes row c / (D / 8), values
+          // 8 (c % (D / 8)) .. + 7, and issues the loads of kFoldSlots slots together, folded
           // with a running maximum: O = sum_k e^(lse_k - m) O_k / sum_k e^(lse_k - m)
-          float mrun = kNegInf, den = 0.f;
-          f32x4 acc[DB];
+          constexpr int CPR = D / 8;
+          const int rows = item.row_end - item.row_start;
+          for (int c0 = 0; c0 < rows * CPR; c0 += 64) {
+            const int c = c0 + lane;
+            const bool live = c < rows * CPR;
+            const int r = live ? c / CPR : 0, col = 8 * (c % CPR);
+            float mrun = kNegInf, den = 0.f;
+            f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            for (int k0 = 0; k0 < ns; k0 += kFoldSlots) {
+              // slot ids k0 .. k0 + kFoldSlots - 1 in lanes 0 .. kFoldSlots - 1 (the last id repeats
+              // past the tile's end; those slots are skipped below)
+              const int sid_k = k0 == 0 ? sid_lane : sl[min(k0 + lane % kFoldSlots, ns - 1)];
+              float lk[kFoldSlots];
+              f32x4 ok[kFoldSlots][2];
 #pragma unroll
-          for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-          for (int k0 = 0; k0 < ns; k0 += 2) {
-            float lk[2];
-            f32x4 ok[2][DB];
+              for (int u = 0; u < kFoldSlots; ++u) {
+                const int id = __shfl(sid_k, u, 64);
+                const int32_t prow = (id * a.Hk + hk) * a.Tq + r;
+                lk[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_lse_rs, prow * 4, 0, kAgentScope));
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int k = min(k0 + u, ns - 1);  // (a repeated last slot is skipped below)
-              const int sid = k == 0 ? sid0 : k == 1 ? sid1 : sl[k];
-              const int64_t prow = (int64_t(sid) * a.Hk + hk) * a.Tq + n;
-              lk[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part_lse_rs, int32_t(prow) * 4, 0,
-                                                                           kAgentScope));
-              const int32_t ob = int32_t(prow * D + 4 * j) * 4;
+                for (int h2 = 0; h2 < 2; ++h2)
+                  ok[u][h2] = __builtin_bit_cast(
+                      f32x4, __builtin_amdgcn_raw_buffer_load_b128(part_o_rs, (prow * D + col + 4 * h2) * 4, 0,
+                                                                   kAgentScope));
+              }
 #pragma unroll
-              for (int db = 0; db < DB; ++db)
-                ok[u][db] = __builtin_bit_cast(
-                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(part_o_rs, ob + 64 * db, 0, kAgentScope));
+              for (int u = 0; u < kFoldSlots; ++u) {
+                if (k0 + u >= ns || lk[u] == kNegInf) continue;
+                const float mn = fmaxf(mrun, lk[u]);
+                const float so = expf(mrun - mn), w = expf(lk[u] - mn);
+                den = den * so + w;
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) acc[h2] = acc[h2] * so + ok[u][h2] * w;
+                mrun = mn;
+              }
             }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              if (k0 + u >= ns || lk[u] == kNegInf) continue;
-              const float mn = fmaxf(mrun, lk[u]);
-              const float so = expf(mrun - mn), w = expf(lk[u] - mn);
-              den = den * so + w;
-#pragma unroll
-              for (int db = 0; db < DB; ++db) acc[db] = acc[db] * so + ok[u][db] * w;
-              mrun = mn;
+            if (live) {
+              const bool empty = !(den > 0.f);
+              const float inv = empty ? 0.f : 1.f / den;
+              const int row = item.row_start + r;
+              const int64_t orow_r = int64_t(item.q_start + row / g) * a.Hq + hk * g + row % g;
+              const f32x4 v0 = acc[0] * inv, v1 = acc[1] * inv;
+              *reinterpret_cast<u32x4*>(O + orow_r * D + col) =
+                  u32x4{pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]), pack_bf16x2(v1[0], v1[1]),
+                        pack_bf16x2(v1[2], v1[3])};
+              if (col == 0) a.lse[orow_r] = empty ? kNegInf : mrun + logf(den);
             }
           }
-          const bool empty = !(den > 0.f);
-          const float inv = empty ? 0.f : 1.f / den;
-          uint16_t* op = O + orow * D + 4 * j;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const f32x4 v = acc[db] * inv;
-            *reinterpret_cast<u32x2*>(op + db * 16) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          }
-          if (j == 0) a.lse[orow] = empty ? kNegInf : mrun + logf(den);
         }
       }
     }
@@ -480,19 +495,21 @@ int decode_bf16_blocks_per_cu(int d, int Hk) {
   int nb = 1;
   hipError_t e = hipErrorInvalidValue;
   if (d == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<64, false, false>, 64 * wv,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<64, false, false, true>, 64 * wv,
                                                      wv * decode_vs_bytes<64>());
   if (d == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<128, false, false>, 64 * wv,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<128, false, false, true>, 64 * wv,
                                                      wv * decode_vs_bytes<128>());
   return (e == hipSuccess && nb > 0) ? nb : 1;
 }
 
-template <int D, bool KV8>
+template <int D, bool KV8, bool FOLD>
 static void launch_cap(const RunArgs& a, dim3 grid, int waves, hipStream_t s) {
   const size_t lds = size_t(waves) * decode_vs_bytes<D>();
-  if (a.soft_cap > 0.f) hipLaunchKernelGGL((attn_decode_bf16_kernel<D, true, KV8>), grid, dim3(64 * waves), lds, s, a);
-  else hipLaunchKernelGGL((attn_decode_bf16_kernel<D, false, KV8>), grid, dim3(64 * waves), lds, s, a);
+  if (a.soft_cap > 0.f)
+    hipLaunchKernelGGL((attn_decode_bf16_kernel<D, true, KV8, FOLD>), grid, dim3(64 * waves), lds, s, a);
+  else
+    hipLaunchKernelGGL((attn_decode_bf16_kernel<D, false, KV8, FOLD>), grid, dim3(64 * waves), lds, s, a);
 }
 
 // Workgroups that stay resident together on the current device (per head group); items are taken
@@ -513,10 +530,13 @@ static int decode_resident_blocks(int d, int Hk) {
 hipError_t launch_decode_bf16(const RunArgs& a, bool kv_e4m3, hipStream_t s) {
   const int waves = decode_bf16_waves_per_block(a.Hk);
   const dim3 grid(std::min(a.C, decode_resident_blocks(a.d, a.Hk)), decode_bf16_blocks_per_worker(a.Hk));
-  if (a.d == 64 && kv_e4m3) launch_cap<64, true>(a, grid, waves, s);
-  else if (a.d == 64) launch_cap<64, false>(a, grid, waves, s);
-  else if (a.d == 128 && kv_e4m3) launch_cap<128, true>(a, grid, waves, s);
-  else if (a.d == 128) launch_cap<128, false>(a, grid, waves, s);
+  if (kv_e4m3 && a.fold_in_kernel) return hipErrorInvalidValue;  // (E4M3 keeps the merge launch)
+  if (a.d == 64 && kv_e4m3) launch_cap<64, true, false>(a, grid, waves, s);
+  else if (a.d == 64 && a.fold_in_kernel) launch_cap<64, false, true>(a, grid, waves, s);
+  else if (a.d == 64) launch_cap<64, false, false>(a, grid, waves, s);
+  else if (a.d == 128 && kv_e4m3) launch_cap<128, true, false>(a, grid, waves, s);
+  else if (a.d == 128 && a.fold_in_kernel) launch_cap<128, false, true>(a, grid, waves, s);
+  else if (a.d == 128) launch_cap<128, false, false>(a, grid, waves, s);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
