@@ -1183,7 +1183,7 @@ def main():
                        "frac": round(dec["gbs"] / HBM_PEAK_GBS, 4),
                        "traffic": rec["traffic_bytes_per_call"] if rec else None,
                        # one launch: split requests are folded inside the attention kernel
-                       "kernel": "attn_decode_bf16_kernel<128, false, false>",
+                       "kernel": "attn_decode_bf16_kernel<128, false, false, true>",
                        "call_avg_us": round(dec["ms"] * 1e3, 2), "algorithmic_bytes": dec["bytes"],
                        # the same pages read in the same order by a kernel that does nothing else
                        "read_ceiling_gbs": ceil["gbs"], "read_ceiling": ceil,

@@ -13,7 +13,7 @@ import bench
 
 WARM = int(bench.PROFILE_STEPS.split("--warmup ")[1].split()[0])
 STEPS = int(bench.PROFILE_STEPS.split("--steps ")[1].split()[0])
-KNAME = "void bsr::attn_decode_bf16_kernel<128, false, false>(bsr::RunArgs)"
+KNAME = "void bsr::attn_decode_bf16_kernel<128, false, false, true>(bsr::RunArgs)"
 PNAME = "(anonymous namespace)::read_pages_kernel(unsigned int const*, int)"
 COPY = "__amd_rocclr_copyBuffer"
 
