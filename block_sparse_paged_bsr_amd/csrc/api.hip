@@ -162,13 +162,11 @@ int run_common(const bsr_plan* p, const void* ws, const void* q, const void* k, 
   hipError_t e = hipSuccess;
   if (!p->items.empty()) {
     hipEvent_t t0 = timing_start(s);
-    // split tiles of a plan on the bf16 decode kernel are folded by the wave that writes a tile's
-    // last partial state (partial states addressed with 32-bit offsets).  E4M3 items stream half
-    // the bytes per token, so the wait for each partial state's stores weighs twice as much there:
-    // measured 132.6-133.6 us against 127.7-131.1 us with the merge launch on the batch-64 decode,
-    // which E4M3 therefore keeps.
+    // split tiles of a plan on the decode kernel (bf16 or E4M3 KV) are folded by the wave that
+    // writes a tile's last partial state (partial states addressed with 32-bit offsets)
     const bool fold_ok = p->item_folds && size_t(p->Hk) * p->Tq * (p->d + 1) * sizeof(float) * p->num_slots < (size_t(1) << 31);
     if (kv_e4m3) {
+      a.fold_in_kernel = fold_ok ? 1 : 0;
       e = launch_decode_bf16(a, true, s);
     } else if (dtype == BSR_DTYPE_F32) {
       if (!attn_f32_supported(p->d)) return unsupported("fp32 head_dim must be one of 16, 32, 64, 128, 256");

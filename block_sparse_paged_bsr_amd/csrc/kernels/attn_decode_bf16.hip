@@ -75,7 +75,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(void* p) {
 // it the kernel carries no fold code, and the merge pass folds them.
 template <int D, bool CAP, bool KV8, bool FOLD>
 __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(RunArgs a) {
-  static_assert(!(KV8 && FOLD), "E4M3 decode keeps the merge launch");
   constexpr int KB = D / 32;  // k-blocks of the score product
   constexpr int DB = D / 16;  // d-blocks of the output product
   constexpr int VS = D + 8;   // LDS row stride (elements); 16-byte aligned rows
@@ -530,10 +529,11 @@ static int decode_resident_blocks(int d, int Hk) {
 hipError_t launch_decode_bf16(const RunArgs& a, bool kv_e4m3, hipStream_t s) {
   const int waves = decode_bf16_waves_per_block(a.Hk);
   const dim3 grid(std::min(a.C, decode_resident_blocks(a.d, a.Hk)), decode_bf16_blocks_per_worker(a.Hk));
-  if (kv_e4m3 && a.fold_in_kernel) return hipErrorInvalidValue;  // (E4M3 keeps the merge launch)
-  if (a.d == 64 && kv_e4m3) launch_cap<64, true, false>(a, grid, waves, s);
+  if (a.d == 64 && kv_e4m3 && a.fold_in_kernel) launch_cap<64, true, true>(a, grid, waves, s);
+  else if (a.d == 64 && kv_e4m3) launch_cap<64, true, false>(a, grid, waves, s);
   else if (a.d == 64 && a.fold_in_kernel) launch_cap<64, false, true>(a, grid, waves, s);
   else if (a.d == 64) launch_cap<64, false, false>(a, grid, waves, s);
+  else if (a.d == 128 && kv_e4m3 && a.fold_in_kernel) launch_cap<128, true, true>(a, grid, waves, s);
   else if (a.d == 128 && kv_e4m3) launch_cap<128, true, false>(a, grid, waves, s);
   else if (a.d == 128 && a.fold_in_kernel) launch_cap<128, false, true>(a, grid, waves, s);
   else if (a.d == 128) launch_cap<128, false, false>(a, grid, waves, s);

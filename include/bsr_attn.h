@@ -108,7 +108,7 @@ typedef struct bsr_plan_desc {
  *   positions of its tile (1 in decode) plus beta times its chunk length (eq. 11).  A tile with one chunk writes its
  *   final output; chunks of split tiles get partial slots, folded in KV order
  *   (deterministic; no atomics in the arithmetic) by the wave that writes a tile's last
- *   slot on the bf16 decode kernel, otherwise by the merge pass.
+ *   slot on the decode kernel (bf16 or E4M3 KV), otherwise by the merge pass.
  * Copies every host array, so the caller may free them on return.  Pure host code:
  * never touches the GPU.  *out receives the plan (NULL on error).
  */
@@ -275,7 +275,8 @@ int bsr_run_decode_scratch(const bsr_plan* plan, const void* q, const void* k_ca
  * open, and this is the OCP format with per-tensor scales.  k_scale and v_scale must be
  * positive and finite.  Supported where the bf16 decode kernel is (head_dim 64 or 128, at
  * most 16 query heads per KV head), else BSR_UNSUPPORTED.  Reads half the KV bytes of bf16.
- * Split requests are combined by the merge launch (not inside the attention kernel).
+ * As with bsr_run_decode, split requests are folded inside the attention kernel, so the call
+ * is one launch unless a request has no keys.
  */
 int bsr_run_decode_e4m3(const bsr_plan* plan, const void* ws, const void* q, const void* k_cache,
                         const void* v_cache, void* o, float* lse, float sm_scale, float k_scale,

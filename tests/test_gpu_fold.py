@@ -1,4 +1,4 @@
-"""GPU tests of the split-request fold inside the bf16 decode kernel: the wave that writes the
+"""GPU tests of the split-request fold inside the decode kernel: the wave that writes the
 last partial state of a split request folds that request's states in the plan's slot order
 ("FlashInfer: Engineering a Customizable, Block-Sparse Attention Engine for LLM Inference Serving"
 §VIII.3 and §VIII.6), so a decode call is one launch unless a request has no keys.
@@ -88,7 +88,7 @@ def test_empty_request_adds_the_merge_launch():
 
 @pytest.mark.parametrize("seed,workers", [(31, 40), (32, 97), (33, 256)])
 def test_many_splits_per_request(seed, workers):
-    """Up to dozens of partial states per request, so the fold runs many rounds of two slots,
+    """Up to dozens of partial states per request, so the fold runs several rounds of eight slots,
     and counters of one plan are reused by the next call of another plan."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(1, 3000, size=12)

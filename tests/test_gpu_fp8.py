@@ -91,7 +91,8 @@ def test_decode_e4m3_with_window_and_cap():
 
 def test_decode_e4m3_batch64_full():
     """Batch-64 paged decode at its full size over E4M3 K/V: every request against the oracle,
-    and two runs bitwise equal."""
+    two runs bitwise equal, and each call one launch (its 55 split requests folded inside the
+    attention kernel, no merge launch)."""
     import torch
     from block_sparse_paged_bsr_amd import api
 
@@ -101,10 +102,16 @@ def test_decode_e4m3_batch64_full():
     log(f"[decode_e4m3_batch64_full] tokens={int(b.kv_lens.sum())} workers={C_} scales={e.k_scale:.4g},{e.v_scale:.4g}")
     p = make_plan(b, num_workers=C_)
     tens = e.torch_values("cuda")
-    o, l = _run(e, p, tens)
+    api.timing_enable(True)
+    try:
+        o, l = _run(e, p, tens)
+        o2, l2 = _run(e, p, tens)
+        t = api.timing_read()
+    finally:
+        api.timing_enable(False)
+    assert t["attn_launches"] == 2 and t["merge_launches"] == 0, t
     ro, rl = _oracle(e)
     compare(o, l, ro, rl, "bf16", "decode e4m3 batch64")
-    o2, l2 = _run(e, p, tens)
     assert np.array_equal(o, o2) and np.array_equal(l, l2)
     torch.cuda.synchronize()
 
