@@ -97,11 +97,14 @@ def per_call_ms(fn, n):
     return float(np.median(ts)), float(ts.min()), float(np.percentile(ts, 90))
 
 
-def make_plan(b, kind, causal=False, **variant):
+def make_plan(b, kind, causal=False, affine=False, **variant):
+    """affine: plan the batch as a contiguous cache (no page table; its table must be the identity)."""
     from block_sparse_paged_bsr_amd import api
 
     C = api.query_num_workers(kind, H_QO, H_KV, D)
-    return api.Plan(b.kv_indptr, b.kv_indices, b.last_page_len, num_pages=b.num_pages,
+    if affine:
+        assert np.array_equal(b.kv_indices, np.arange(len(b.kv_indices)))
+    return api.Plan(b.kv_indptr, None if affine else b.kv_indices, b.last_page_len, num_pages=b.num_pages,
                     num_qo_heads=H_QO, num_kv_heads=H_KV, head_dim=D, page_size=b.page_size,
                     qo_indptr=b.qo_indptr, causal=causal, num_workers=C, **variant)
 
@@ -413,7 +416,9 @@ def bench_e4m3(args, num_workers=None):
 
 
 def bench_vector_sparse(args):
-    """Page size 1 over a 2^20-row pool vs the same contents contiguous."""
+    """Page size 1 over a 2^20-row pool vs the same contents contiguous: through the identity
+    page table (same loader, row locality only) and, for decode, planned as a contiguous cache
+    (page ids computed: the cost of indexed addressing)."""
     import workloads as inputs
 
     out = {}
@@ -422,11 +427,16 @@ def bench_vector_sparse(args):
     nbytes = decode_bytes(lens, len(lens), len(a.kv_indices))
     ra = run_case(a, "decode", args.steps, args.warmup)
     rc = run_case(c, "decode", args.steps, args.warmup)
+    # the contiguous twin once more, planned without a page table: page ids computed, not loaded
+    rf = run_case(c, "decode", args.steps, args.warmup, affine=True)
     out["decode"] = {"paged_us": round(ra["ms"] * 1e3, 2), "contiguous_us": round(rc["ms"] * 1e3, 2),
+                     "contiguous_affine_us": round(rf["ms"] * 1e3, 2),
                      "paged_gbs": round(nbytes / (ra["ms"] * 1e-3) / 1e9, 1),
                      "contiguous_gbs": round(nbytes / (rc["ms"] * 1e-3) / 1e9, 1),
-                     "paged_over_contiguous_time": round(ra["ms"] / rc["ms"], 4)}
-    del a, c, ra, rc
+                     "contiguous_affine_gbs": round(nbytes / (rf["ms"] * 1e-3) / 1e9, 1),
+                     "paged_over_contiguous_time": round(ra["ms"] / rc["ms"], 4),
+                     "paged_over_affine_time": round(ra["ms"] / rf["ms"], 4)}
+    del a, c, ra, rc, rf
     plens = [2048] * 8
     a, c = inputs.vector_sparse_pair(1, plens, plens, pool_rows=1 << 20, causal=True)
     fl = prefill_flops(plens)

@@ -41,9 +41,13 @@ def _dtype_code(t):
 def _plan_desc(kv_indptr, kv_indices, last_page_len, *, num_pages, num_qo_heads, num_kv_heads, head_dim, page_size,
                qo_indptr=None, causal=False, num_workers=0, tile_q=0, alpha=2, beta=1, window_left=-1,
                logits_soft_cap=0.0):
-    """A bsr_plan_desc and the int32 arrays it points to (keep them alive while it is used)."""
+    """A bsr_plan_desc and the int32 arrays it points to (keep them alive while it is used).
+    kv_indices None: a contiguous cache (request i's pages are kv_indptr[i] .. kv_indptr[i+1] - 1)."""
     kv_indptr, p_ip = _i32(kv_indptr)
-    kv_indices, p_ix = _i32(kv_indices)
+    if kv_indices is None:
+        p_ix = C.cast(None, _lib.i32p)
+    else:
+        kv_indices, p_ix = _i32(kv_indices)
     last_page_len, p_last = _i32(last_page_len)
     if qo_indptr is not None:
         qo_indptr, p_qo = _i32(qo_indptr)
@@ -74,7 +78,8 @@ def _plan_desc(kv_indptr, kv_indices, last_page_len, *, num_pages, num_qo_heads,
 
 
 class Plan:
-    """Host plan: the load-balanced split-KV partition of one batch (bsr_plan_create)."""
+    """Host plan: the load-balanced split-KV partition of one batch (bsr_plan_create).
+    kv_indices=None plans a contiguous cache (the identity page table)."""
 
     def __init__(
         self,

@@ -103,6 +103,7 @@ RunArgs make_args(const bsr_plan* p, const void* ws) {
   a.imerge = reinterpret_cast<const int32_t*>(base + p->ws.imerge);
   a.arrive = reinterpret_cast<int32_t*>(const_cast<char*>(base) + p->ws.arrive);
   a.fold_in_kernel = 0;
+  a.affine = p->affine ? 1 : 0;
   a.part_o = reinterpret_cast<float*>(const_cast<char*>(base) + p->ws.part_o);
   a.part_lse = reinterpret_cast<float*>(const_cast<char*>(base) + p->ws.part_lse);
   a.B = p->B;

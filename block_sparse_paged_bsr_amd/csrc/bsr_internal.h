@@ -98,6 +98,7 @@ struct bsr_plan {
   int32_t num_slots = 0;
   int32_t num_empty_merge = 0;  // merge records with no slot (tiles with nothing visible)
   bool item_folds = false;      // every split tile's record is reachable from its items (imerge)
+  bool affine = false;          // kv_indices was NULL: the identity page table (contiguous KV)
   // composable plans: number of levels and the first (flattened) request of each level
   int32_t num_levels = 1;
   std::vector<int32_t> level_req_start;

@@ -72,8 +72,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(void* p) {
 #define BSR_DECODE_WAIT_VMCNT0() __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8))
 
 // FOLD: the plan's split tiles are folded inside this kernel (RunArgs::fold_in_kernel); without
-// it the kernel carries no fold code, and the merge pass folds them.
-template <int D, bool CAP, bool KV8, bool FOLD>
+// it the kernel carries no fold code, and the merge pass folds them.  AFF: the cache is
+// contiguous (RunArgs::affine), so page ids are computed instead of loaded from the table.
+template <int D, bool CAP, bool KV8, bool FOLD, bool AFF>
 __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(RunArgs a) {
   constexpr int KB = D / 32;  // k-blocks of the score product
   constexpr int DB = D / 16;  // d-blocks of the output product
@@ -120,10 +121,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
       dst[kb] = *reinterpret_cast<const bf16x8*>(qp + col);
     }
   };
-  // page of token t of an item (eq. 7), t clamped to the item's last token
+  // page of token t of an item (eq. 7), t clamped to the item's last token; a contiguous cache
+  // (identity page table) computes it without the table's load, the affine addressing of
+  // "FlashInfer: Engineering a Customizable, Block-Sparse Attention Engine for LLM Inference
+  // Serving" §V.4
   auto page_in = [&](const ItemRec& itm, int t) -> int32_t {
     const int tc = min(t, itm.kv_end - 1);
-    return a.indices[itm.page_start + (a.p_shift >= 0 ? (tc >> a.p_shift) : tc / a.P)];
+    const int32_t x = itm.page_start + (a.p_shift >= 0 ? (tc >> a.p_shift) : tc / a.P);
+    return AFF ? x : a.indices[x];
   };
 
   // Work distribution: the plan's items in its LPT order (longest first), taken by whichever
@@ -494,21 +499,25 @@ int decode_bf16_blocks_per_cu(int d, int Hk) {
   int nb = 1;
   hipError_t e = hipErrorInvalidValue;
   if (d == 64)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<64, false, false, true>, 64 * wv,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<64, false, false, true, false>, 64 * wv,
                                                      wv * decode_vs_bytes<64>());
   if (d == 128)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<128, false, false, true>, 64 * wv,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, attn_decode_bf16_kernel<128, false, false, true, false>, 64 * wv,
                                                      wv * decode_vs_bytes<128>());
   return (e == hipSuccess && nb > 0) ? nb : 1;
 }
 
+// The affine (contiguous-cache) instantiation exists for the plain bf16 kernel; the other
+// variants read the identity table that an affine plan stores like any other.
 template <int D, bool KV8, bool FOLD>
 static void launch_cap(const RunArgs& a, dim3 grid, int waves, hipStream_t s) {
   const size_t lds = size_t(waves) * decode_vs_bytes<D>();
   if (a.soft_cap > 0.f)
-    hipLaunchKernelGGL((attn_decode_bf16_kernel<D, true, KV8, FOLD>), grid, dim3(64 * waves), lds, s, a);
+    hipLaunchKernelGGL((attn_decode_bf16_kernel<D, true, KV8, FOLD, false>), grid, dim3(64 * waves), lds, s, a);
+  else if (!KV8 && a.affine)
+    hipLaunchKernelGGL((attn_decode_bf16_kernel<D, false, KV8, FOLD, !KV8>), grid, dim3(64 * waves), lds, s, a);
   else
-    hipLaunchKernelGGL((attn_decode_bf16_kernel<D, false, KV8, FOLD>), grid, dim3(64 * waves), lds, s, a);
+    hipLaunchKernelGGL((attn_decode_bf16_kernel<D, false, KV8, FOLD, false>), grid, dim3(64 * waves), lds, s, a);
 }
 
 // Workgroups that stay resident together on the current device (per head group); items are taken

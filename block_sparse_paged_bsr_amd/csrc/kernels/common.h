@@ -34,6 +34,7 @@ struct RunArgs {
   const int32_t* imerge;  // per item (queue order): merge record of its split tile, or -1
   int32_t* arrive;        // [num_merge][H_kv]: partial states written (zero between calls)
   int32_t fold_in_kernel; // 1: the decode kernel folds split tiles; the merge pass writes empty tiles
+  int32_t affine;         // 1: indices[x] = x (contiguous KV): page ids are computed, not loaded
   float* part_o;
   float* part_lse;
   const void* q;

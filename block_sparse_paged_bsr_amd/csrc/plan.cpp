@@ -84,9 +84,15 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
   for (int32_t i = 0; i < B; ++i)
     if (p->kv_indptr[i + 1] < p->kv_indptr[i]) return fail("kv_indptr must be non-decreasing");
   const int64_t nnz = p->kv_indptr[B];
-  if (nnz > 0 && !desc->kv_indices) return fail("kv_indices is NULL");
+  // kv_indices == NULL: contiguous KV, request i's pages are kv_indptr[i] .. kv_indptr[i+1] - 1 of
+  // the pool in order (the identity table, stored like any other so that every kernel reads it)
+  p->affine = desc->kv_indices == nullptr;
   p->kv_indices.assign(nnz, 0);
-  if (nnz > 0) std::memcpy(p->kv_indices.data(), desc->kv_indices, sizeof(int32_t) * nnz);
+  if (p->affine) {
+    for (int64_t k = 0; k < nnz; ++k) p->kv_indices[k] = int32_t(k);
+  } else if (nnz > 0) {
+    std::memcpy(p->kv_indices.data(), desc->kv_indices, sizeof(int32_t) * nnz);
+  }
   for (int64_t k = 0; k < nnz; ++k)
     if (p->kv_indices[k] < 0 || p->kv_indices[k] >= p->num_pages) {
       std::ostringstream os;

@@ -65,7 +65,14 @@ typedef struct bsr_plan_desc {
   int32_t batch;                /* B >= 0 */
   const int32_t* qo_indptr;     /* host int32[B+1] or NULL (decode) */
   const int32_t* kv_indptr;     /* host int32[B+1], kv_indptr[0] = 0, non-decreasing */
-  const int32_t* kv_indices;    /* host int32[kv_indptr[B]], each in [0, num_pages) */
+  const int32_t* kv_indices;    /* host int32[kv_indptr[B]], each in [0, num_pages); or NULL
+                                   for a contiguous cache: request i's pages are kv_indptr[i]
+                                   .. kv_indptr[i+1] - 1 of the pool, in order (the identity
+                                   table; kv_indptr[B] <= num_pages).  The plan stores that
+                                   table like any other, and the decode kernel computes the
+                                   page ids instead of loading them (the affine addressing of
+                                   "FlashInfer: Engineering a Customizable, Block-Sparse
+                                   Attention Engine for LLM Inference Serving" §V.4) */
   const int32_t* last_page_len; /* host int32[B]: in [1, page_size] if n_i > 0, else 0 */
   int32_t num_pages;            /* pool size, for validation of kv_indices */
   int32_t num_qo_heads;         /* H_qo, a multiple of H_kv */

@@ -472,3 +472,26 @@ def test_composable_rejects_mismatched_levels():
         api.ComposablePlan(bad[0], num_pages=4, num_qo_heads=4, num_kv_heads=1, head_dim=128, page_size=4)
     with pytest.raises(_lib.BsrError):
         api.ComposablePlan(bad[1], num_pages=4, num_qo_heads=3, num_kv_heads=1, head_dim=128, page_size=4)
+
+
+def test_null_kv_indices_plans_a_contiguous_cache():
+    """kv_indices NULL describes a contiguous cache (request i's pages are kv_indptr[i] ..
+    kv_indptr[i+1] - 1): planned exactly as with the identity page table written out, and a
+    pool with fewer pages than kv_indptr[B] is rejected on the host."""
+    for P, qo in ((16, None), (1, None), (12, [3, 1, 40, 2, 7])):
+        kv = np.array([37, 0, 300, 5, 1000], dtype=np.int64)
+        n = int(((kv + P - 1) // P).sum())
+        ip, ix, last = I.page_table_from_lengths(kv, P, np.arange(n))
+        assert np.array_equal(ix, np.arange(n))
+        qo_ip = None if qo is None else np.concatenate([[0], np.cumsum(qo)])
+        kw = dict(num_pages=n + 5, num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=P, qo_indptr=qo_ip,
+                  causal=qo is not None, num_workers=9)
+        a, b = api.Plan(ip, ix, last, **kw), api.Plan(ip, None, last, **kw)
+        ea, eb = a.export(), b.export()
+        assert ea.keys() == eb.keys()
+        for k in ea:
+            assert np.array_equal(np.asarray(ea[k]), np.asarray(eb[k])), k
+        assert a.workspace_bytes() == b.workspace_bytes()
+        kw["num_pages"] = n - 1
+        with pytest.raises(_lib.BsrError, match="outside"):
+            api.Plan(ip, None, last, **kw)

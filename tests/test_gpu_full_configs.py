@@ -3,8 +3,11 @@
 * Ragged causal prefill (batch 16, q_len = kv_len U[256, 4096], page size 16): every row of the
   three longest requests, which run through the middle of long 128-row work items.
 * Page size 1 over a 2^20-row pool: the batch-64 decode on all 64 requests, and the batch-8 x
-  2048 causal prefill on all 8 sequences (bitwise equal to the contiguous layout everywhere;
-  against the oracle on every decode request and on sampled prefill rows).
+  2048 causal prefill on all 8 sequences (bitwise equal to the contiguous layout everywhere,
+  whether that is described by its identity page table or planned as a contiguous cache with
+  no table; against the oracle on every decode request and on sampled prefill rows).
+* Contiguous caches (kv_indices NULL) at page sizes 16 and 12, with split requests, a soft cap
+  and E4M3 KV: bitwise equal to the same cache described by its identity table.
 * Work items longer than the kernels' page-id window (2048 pages, refilled mid-item): a
   5,000-token causal request at page size 1 for every tile shape of the bf16 prefill kernels.
 
@@ -54,6 +57,55 @@ def test_ragged_prefill_longest_requests_every_row(ragged_prefill_run, rank):
     compare(o, l, ro, rl, "bf16", f"ragged prefill request {i} (all rows)")
 
 
+def _contiguous_plan(b, num_workers, soft_cap=0.0):
+    """Plan of a batch whose page table is the identity, described with kv_indices NULL."""
+    from block_sparse_paged_bsr_amd import api
+
+    assert np.array_equal(b.kv_indices, np.arange(len(b.kv_indices)))
+    return api.Plan(b.kv_indptr, None, b.last_page_len, num_pages=b.num_pages, num_qo_heads=b.num_qo_heads,
+                    num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, page_size=b.page_size,
+                    qo_indptr=b.qo_indptr, causal=b.causal, num_workers=num_workers, logits_soft_cap=soft_cap)
+
+
+@pytest.mark.parametrize("P,d,workers,soft_cap,e4m3", [
+    (16, 128, 256, 0.0, False),
+    (12, 64, 37, 0.0, False),
+    (16, 128, 256, 30.0, False),
+    (16, 128, 256, 0.0, True),
+])
+def test_contiguous_cache_decode(P, d, workers, soft_cap, e4m3):
+    """Decode over a contiguous cache planned without a page table equals, bitwise, the same
+    cache described by its identity table (the plain bf16 kernel computes the page ids; soft
+    cap and E4M3 read the stored identity table), and matches the oracle."""
+    import torch
+    from block_sparse_paged_bsr_amd import api
+
+    lens = np.random.default_rng(P + d).integers(1, 3000, size=24)
+    n = int(((lens + P - 1) // P).sum())
+    b = I.make_paged_batch(50 + P, lens, None, page_size=P, num_qo_heads=32, num_kv_heads=8, head_dim=d,
+                           num_pages=n + 7, contiguous=True, poison=True)  # (7 NaN pages past the end)
+    log(f"[contiguous decode] P={P} d={d} workers={workers} soft_cap={soft_cap} e4m3={e4m3}")
+    pt = make_plan(b, num_workers=workers, soft_cap=soft_cap)
+    pa = _contiguous_plan(b, workers, soft_cap)
+    if not e4m3:
+        ot, lt, _ = run_gpu(b, pt)
+        oa, la, _ = run_gpu(b, pa)
+        assert np.array_equal(oa, ot) and np.array_equal(la, lt)
+        ro, rl = oracle(b, soft_cap=soft_cap)
+        compare(oa, la, ro, rl, "bf16", f"contiguous decode P={P} d={d}")
+        return
+    e = I.to_e4m3(b)
+    q, k, v = e.torch_values("cuda")
+    res = []
+    for p in (pt, pa):
+        ws = api.alloc_workspace(p)
+        p.upload(ws)
+        o, lse = api.run_decode_e4m3(p, ws, q, k, v, e.k_scale, e.v_scale, sm_scale=1.0 / math.sqrt(d))
+        torch.cuda.synchronize()
+        res.append((o.float().cpu().numpy(), lse.cpu().numpy()))
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+
+
 def test_vector_sparse_decode_all_requests():
     """The batch-64 decode at page size 1 in a 2^20-row pool vs its contiguous twin."""
     from block_sparse_paged_bsr_amd import api
@@ -64,7 +116,9 @@ def test_vector_sparse_decode_all_requests():
     C_ = api.query_num_workers("decode", 32, 8, 128)
     oa, la, _ = run_gpu(a, make_plan(a, num_workers=C_))
     oc, lc, _ = run_gpu(c, make_plan(c, num_workers=C_))
+    of, lf, _ = run_gpu(c, _contiguous_plan(c, num_workers=C_))
     assert np.array_equal(oa, oc) and np.array_equal(la, lc)
+    assert np.array_equal(of, oc) and np.array_equal(lf, lc)
     ro, rl = oracle(c)
     compare(oa, la, ro, rl, "bf16", "vector-sparse decode, all 64 requests")
 
@@ -80,7 +134,9 @@ def test_vector_sparse_prefill_all_sequences():
     C_ = api.query_num_workers("prefill", 32, 8, 128)
     oa, la, _ = run_gpu(a, make_plan(a, num_workers=C_))
     oc, lc, _ = run_gpu(c, make_plan(c, num_workers=C_))
+    of, lf, _ = run_gpu(c, _contiguous_plan(c, num_workers=C_))
     assert np.array_equal(oa, oc) and np.array_equal(la, lc)
+    assert np.array_equal(of, oc) and np.array_equal(lf, lc)
     rng = np.random.default_rng(4)
     sub = {i: np.unique(np.concatenate([[0, 31, 32, 1023, 1024, 2047], rng.integers(0, 2048, 26)]))
            for i in range(8)}
