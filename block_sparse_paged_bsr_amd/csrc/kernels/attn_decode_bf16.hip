@@ -70,6 +70,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(void* p) {
   return __builtin_amdgcn_make_buffer_rsrc(p, 0, 0x7fffffff, 0x00020000);
 }
 #define BSR_DECODE_WAIT_VMCNT0() __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8))
+// vmcnt(n) for n < 16 (lgkmcnt and expcnt not waited for)
+#define BSR_DECODE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8) | ((n) & 15))
 
 // FOLD: the plan's split tiles are folded inside this kernel (RunArgs::fold_in_kernel); without
 // it the kernel carries no fold code, and the merge pass folds them.  AFF: the cache is
@@ -162,6 +164,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
   bf16x8 qb[KB], qn[KB];
   int32_t pre[NPRE];
   bool have_pre = false;
+  // the next item's first rows when a folding item issued them before its count (bf16)
+  u32x4 kr0[NL], vr0[NL];
+  bool have_rows = false;
   while (t < num_items) {
     const ItemRec item = next;
     const int item_mi = next_mi;
@@ -177,6 +182,18 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
     };
     const int kv_end = item.kv_end;
     const int64_t orow = out_row(item);
+    // a split tile's merge record and its first slot ids (lane u < kFoldSlots: slot id u), read
+    // at the item's start so that no load has to complete between the item's last stores and
+    // its count
+    int fold_ns = 0, fold_begin = 0, fold_sid = 0;
+    if constexpr (FOLD) {
+      if (item_mi >= 0) {
+        const MergeRec mr = a.merge[item_mi];
+        fold_ns = mr.slot_count;
+        fold_begin = mr.slot_begin;
+        fold_sid = a.mslots[fold_begin + min(lane % kFoldSlots, fold_ns - 1)];
+      }
+    }
     if (have_pre) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) qb[kb] = qn[kb];
@@ -204,8 +221,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
     // the row loads, which run one step ahead of the computation
     auto page_of = [&](int t) -> int32_t { return page_in(item, t); };
     // byte offset of this lane's first 16-byte piece of token t's row
-    auto row_base = [&](int t, int32_t page) -> int64_t {
-      const int tc = min(t, kv_end - 1);
+    auto row_base = [&](int t, int32_t page, int kend) -> int64_t {
+      const int tc = min(t, kend - 1);
       const int off = a.p_shift >= 0 ? (tc & ((1 << a.p_shift) - 1)) : tc - (tc / a.P) * a.P;
       return ((int64_t(page) * a.P + off) * a.Hk + hk) * (D * ES) + j * 16;
     };
@@ -215,9 +232,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
     // that token's page taken from the lane that looked it up
     constexpr int CPT = D / 8, TPI = 64 / CPT;  // 16-byte chunks per slice, tokens per load
     static_assert(KV8 || TPI * NL == 16, "one step's 16 tokens in NL loads");
+    static_assert(2 * NL < 16, "the rows of one step fit the vmcnt field of the fold's wait");
     const int vt = lane / CPT, vc = lane % CPT;
-    auto load_rows = [&](u32x4 (&kd)[NL], u32x4 (&vd)[NL], int t, int32_t page) {
-      const int64_t base = row_base(t, page);
+    auto load_rows = [&](u32x4 (&kd)[NL], u32x4 (&vd)[NL], int t, int32_t page, int kend) {
+      const int64_t base = row_base(t, page, kend);
 #pragma unroll
       for (int l = 0; l < NL; ++l) kd[l] = *reinterpret_cast<const u32x4*>(K + base + 64 * l);
       if constexpr (KV8) {
@@ -229,7 +247,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
         for (int i = 0; i < NL; ++i) {
           const int tok = TPI * i + vt;
           const int32_t pg = __shfl(page, tok, 64);
-          vd[i] = *reinterpret_cast<const u32x4*>(V + row_base(ts + tok, pg) - j * 16 + vc * 16);
+          vd[i] = *reinterpret_cast<const u32x4*>(V + row_base(ts + tok, pg, kend) - j * 16 + vc * 16);
         }
       }
     };
@@ -303,14 +321,23 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
     if constexpr (PD == 1) {
       int32_t pg_next = pre[1];
       u32x4 kr[NL], vr[NL];
-      load_rows(kr, vr, item.kv_start + n, pre[0]);
+      if (have_rows) {
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+          kr[l] = kr0[l];
+          vr[l] = vr0[l];
+        }
+      } else {
+        load_rows(kr, vr, item.kv_start + n, pre[0], kv_end);
+      }
+      have_rows = false;
       for (int t0 = item.kv_start; t0 < kv_end; t0 += 16) {
         const bool has_next = t0 + 16 < kv_end;
         const int32_t pg_after = page_of(t0 + 32 + n);
         // request the next step's rows (or, in the last step, the next item's queries and first
         // page ids) before touching this step's data
         u32x4 kn[NL], vn[NL];
-        if (has_next) load_rows(kn, vn, t0 + 16 + n, pg_next);
+        if (has_next) load_rows(kn, vn, t0 + 16 + n, pg_next, kv_end);
         if (!claimed && t0 + 32 >= kv_end) claim();
         if (!has_next) preload_next();
         pg_next = pg_after;
@@ -328,15 +355,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
       // bytes in flight as with one step of bf16 rows
       int32_t pg_next0 = pre[2], pg_next1 = pre[3];
       u32x4 kr[2][NL], vr[2][NL];
-      load_rows(kr[0], vr[0], item.kv_start + n, pre[0]);
-      load_rows(kr[1], vr[1], item.kv_start + 16 + n, pre[1]);
+      load_rows(kr[0], vr[0], item.kv_start + n, pre[0], kv_end);
+      load_rows(kr[1], vr[1], item.kv_start + 16 + n, pre[1], kv_end);
       for (int t0 = item.kv_start; t0 < kv_end; t0 += 32) {
         const bool has_next = t0 + 32 < kv_end;
         const int32_t pa0 = page_of(t0 + 64 + n), pa1 = page_of(t0 + 80 + n);
         // (unconditional: past the end the rows clamp to the chunk's last row)
         u32x4 kn[2][NL], vn[2][NL];
-        load_rows(kn[0], vn[0], t0 + 32 + n, pg_next0);
-        load_rows(kn[1], vn[1], t0 + 48 + n, pg_next1);
+        load_rows(kn[0], vn[0], t0 + 32 + n, pg_next0, kv_end);
+        load_rows(kn[1], vn[1], t0 + 48 + n, pg_next1, kv_end);
         if (!claimed && t0 + 64 >= kv_end) claim();
         if (!has_next) preload_next();
         compute(t0, kr[0], vr[0]);
@@ -358,6 +385,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
     // lane (n, j) summed tokens 4j..4j+3 of every step; add the four token groups
     l += shfl_xor(l, 16);
     l += shfl_xor(l, 32);
+    // a split item issues the next item's first rows after its stores (below); the page ids
+    // those rows need were requested in the last step: complete them before the stores, so that
+    // nothing issued before the stores has to be waited for after them
+    if constexpr (FOLD && PD == 1) BSR_DECODE_WAIT_VMCNT0();
     if (n < item.row_end - item.row_start) {
       const bool empty = !(l > 0.f);
       const float inv = empty ? 0.f : o_scale / l;
@@ -399,12 +430,21 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
     // folded it, and returns the counter to zero for the next call.
     if constexpr (FOLD) {
       if (item_mi >= 0) {  // (uniform: all waves of the workgroup run the item)
-        const MergeRec mr = a.merge[item_mi];
-        const int ns = mr.slot_count;
-        const int* __restrict__ sl = a.mslots + mr.slot_begin;
-        // lane u < kFoldSlots holds slot id u of the tile (fetched while the stores complete)
-        const int sid_lane = sl[min(lane % kFoldSlots, ns - 1)];
-        BSR_DECODE_WAIT_VMCNT0();
+        const int ns = fold_ns;
+        const int* __restrict__ sl = a.mslots + fold_begin;
+        const int sid_lane = fold_sid;
+        if (PD == 1 && more) {
+          // the next item's first rows go out before the wait, so that their latency overlaps
+          // the count and any fold; the wait then leaves exactly those 2 NL loads in flight
+          // (loads and stores complete in issue order), so this item's stores are complete
+          __builtin_amdgcn_sched_barrier(0);
+          load_rows(kr0, vr0, next.kv_start + n, pre[0], next.kv_end);
+          have_rows = true;
+          __builtin_amdgcn_sched_barrier(0);
+          BSR_DECODE_WAIT_VMCNT(2 * NL);
+        } else {
+          BSR_DECODE_WAIT_VMCNT0();
+        }
         int32_t* ctr = a.arrive + int64_t(item_mi) * a.Hk + hk;
         int arrived = 0;
         if (lane == 0) arrived = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
