@@ -164,8 +164,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
   bf16x8 qb[KB], qn[KB];
   int32_t pre[NPRE];
   bool have_pre = false;
-  // the next item's first rows when a folding item issued them before its count (bf16)
-  u32x4 kr0[NL], vr0[NL];
+  // the next item's first rows (E4M3: its first two 16-token halves) when a folding item issued
+  // them before its count
+  u32x4 kr0[PD][NL], vr0[PD][NL];
   bool have_rows = false;
   while (t < num_items) {
     const ItemRec item = next;
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
     // that token's page taken from the lane that looked it up
     constexpr int CPT = D / 8, TPI = 64 / CPT;  // 16-byte chunks per slice, tokens per load
     static_assert(KV8 || TPI * NL == 16, "one step's 16 tokens in NL loads");
-    static_assert(2 * NL < 16, "the rows of one step fit the vmcnt field of the fold's wait");
+    static_assert(2 * NL * PD < 16, "the rows of one step fit the vmcnt field of the fold's wait");
     const int vt = lane / CPT, vc = lane % CPT;
     auto load_rows = [&](u32x4 (&kd)[NL], u32x4 (&vd)[NL], int t, int32_t page, int kend) {
       const int64_t base = row_base(t, page, kend);
@@ -324,8 +325,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
       if (have_rows) {
 #pragma unroll
         for (int l = 0; l < NL; ++l) {
-          kr[l] = kr0[l];
-          vr[l] = vr0[l];
+          kr[l] = kr0[0][l];
+          vr[l] = vr0[0][l];
         }
       } else {
         load_rows(kr, vr, item.kv_start + n, pre[0], kv_end);
@@ -355,8 +356,19 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
       // bytes in flight as with one step of bf16 rows
       int32_t pg_next0 = pre[2], pg_next1 = pre[3];
       u32x4 kr[2][NL], vr[2][NL];
-      load_rows(kr[0], vr[0], item.kv_start + n, pre[0], kv_end);
-      load_rows(kr[1], vr[1], item.kv_start + 16 + n, pre[1], kv_end);
+      if (have_rows) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int l = 0; l < NL; ++l) {
+            kr[h2][l] = kr0[h2][l];
+            vr[h2][l] = vr0[h2][l];
+          }
+      } else {
+        load_rows(kr[0], vr[0], item.kv_start + n, pre[0], kv_end);
+        load_rows(kr[1], vr[1], item.kv_start + 16 + n, pre[1], kv_end);
+      }
+      have_rows = false;
       for (int t0 = item.kv_start; t0 < kv_end; t0 += 32) {
         const bool has_next = t0 + 32 < kv_end;
         const int32_t pa0 = page_of(t0 + 64 + n), pa1 = page_of(t0 + 80 + n);
@@ -388,7 +400,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
     // a split item issues the next item's first rows after its stores (below); the page ids
     // those rows need were requested in the last step: complete them before the stores, so that
     // nothing issued before the stores has to be waited for after them
-    if constexpr (FOLD && PD == 1) BSR_DECODE_WAIT_VMCNT0();
+    if constexpr (FOLD) BSR_DECODE_WAIT_VMCNT0();
     if (n < item.row_end - item.row_start) {
       const bool empty = !(l > 0.f);
       const float inv = empty ? 0.f : o_scale / l;
@@ -433,15 +445,17 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
         const int ns = fold_ns;
         const int* __restrict__ sl = a.mslots + fold_begin;
         const int sid_lane = fold_sid;
-        if (PD == 1 && more) {
+        if (more) {
           // the next item's first rows go out before the wait, so that their latency overlaps
-          // the count and any fold; the wait then leaves exactly those 2 NL loads in flight
+          // the count and any fold; the wait then leaves exactly those 2 NL PD loads in flight
           // (loads and stores complete in issue order), so this item's stores are complete
           __builtin_amdgcn_sched_barrier(0);
-          load_rows(kr0, vr0, next.kv_start + n, pre[0], next.kv_end);
+#pragma unroll
+          for (int h2 = 0; h2 < PD; ++h2)
+            load_rows(kr0[h2], vr0[h2], next.kv_start + 16 * h2 + n, pre[h2], next.kv_end);
           have_rows = true;
           __builtin_amdgcn_sched_barrier(0);
-          BSR_DECODE_WAIT_VMCNT(2 * NL);
+          BSR_DECODE_WAIT_VMCNT(2 * NL * PD);
         } else {
           BSR_DECODE_WAIT_VMCNT0();
         }
