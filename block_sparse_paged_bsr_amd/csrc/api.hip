@@ -98,6 +98,7 @@ RunArgs make_args(const bsr_plan* p, const void* ws) {
   a.mslots = reinterpret_cast<const int32_t*>(base + p->ws.mslots);
   a.mroff = reinterpret_cast<const int32_t*>(base + p->ws.mroff);
   a.lpt = reinterpret_cast<const int32_t*>(base + p->ws.lpt);
+  a.items_lpt = reinterpret_cast<const ItemRec*>(base + p->ws.items_lpt);
   a.tickets = reinterpret_cast<int32_t*>(const_cast<char*>(base) + p->ws.tickets);
   a.num_items = int32_t(p->items.size() / 8);
   a.imerge = reinterpret_cast<const int32_t*>(base + p->ws.imerge);

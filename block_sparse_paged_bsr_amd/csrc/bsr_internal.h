@@ -37,7 +37,7 @@ struct ItemRec {
   int32_t page_start; //   lengths, copied from its request record so that the attention kernels
   int32_t q_len;      //   need only this record (the custom-mask offset stays in the request
   int32_t kv_len;     //   record)
-  int32_t pad[6];
+  int32_t pad[6];      // (pad[0] of an LPT-ordered copy: the merge record of a split tile, or -1)
 };
 static_assert(sizeof(ItemRec) == 64, "ItemRec layout");
 
@@ -61,7 +61,7 @@ constexpr int kTicketGroups = 64;
 
 // Byte offsets of the workspace sections (all 256-byte aligned).
 struct WsLayout {
-  size_t req = 0, indices = 0, items = 0, qptr = 0, merge = 0, mslots = 0, mroff = 0;
+  size_t req = 0, indices = 0, items = 0, items_lpt = 0, qptr = 0, merge = 0, mslots = 0, mroff = 0;
   size_t lpt = 0;      // [num_items]: position in `items` of the t-th item in the plan's LPT order
   size_t tickets = 0;  // [kTicketGroups][2]: next ticket, finished workgroups (zero between calls)
   size_t imerge = 0;   // [num_items], queue order: merge record of the item's split tile, or -1

@@ -235,6 +235,7 @@ int build_composable_plan(const bsr_plan_desc* levels, int32_t n_levels, int32_t
   L.mslots = off;   off = al256(off + sizeof(int32_t) * std::max<size_t>(p->merge_slots.size(), 1));
   L.mroff = off;    off = al256(off + sizeof(int32_t) * std::max<size_t>(p->merge_roff.size(), 1));
   L.lpt = off;      off = al256(off + sizeof(int32_t) * std::max(M, 1));
+  L.items_lpt = off; off = al256(off + sizeof(ItemRec) * std::max(M, 1));
   L.tickets = off;  off = al256(off + sizeof(int32_t) * 2 * kTicketGroups);
   // (a query's states span several tiles: the merge pass folds them, never the attention kernel)
   L.imerge = off;   off = al256(off + sizeof(int32_t) * std::max(M, 1));
@@ -275,6 +276,12 @@ int build_composable_plan(const bsr_plan_desc* levels, int32_t n_levels, int32_t
     for (int32_t k = 0; k < M; ++k) pos[p->queue_items[k]] = k;
     auto* lpt = reinterpret_cast<int32_t*>(p->meta.data() + L.lpt);
     for (int32_t t = 0; t < M; ++t) lpt[t] = pos[order[t]];
+    // the records in that order (no merge records: the merge pass folds composable plans)
+    auto* ql = reinterpret_cast<ItemRec*>(p->meta.data() + L.items_lpt);
+    for (int32_t t = 0; t < M; ++t) {
+      ql[t] = qi[lpt[t]];
+      ql[t].pad[0] = -1;
+    }
   }
   auto* mr = reinterpret_cast<MergeRec*>(p->meta.data() + L.merge);
   for (int32_t k = 0; k < NM; ++k)

@@ -159,8 +159,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
   constexpr int NPRE = KV8 ? 4 : 2;  // page ids of the first two steps (16 tokens each)
   const int num_items = a.num_items;
   int t = blockIdx.x;
-  ItemRec next = a.items[a.lpt[t < num_items ? t : 0]];
-  int next_mi = FOLD ? a.imerge[a.lpt[t < num_items ? t : 0]] : -1;
+  ItemRec next = a.items_lpt[t < num_items ? t : 0];
+  int next_mi = FOLD ? next.pad[0] : -1;
   bf16x8 qb[KB], qn[KB];
   int32_t pre[NPRE];
   bool have_pre = false;
@@ -176,8 +176,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void attn_decode_bf16_kernel(Run
       t = draw();
       more = t < num_items;
       if (more) {
-        next = a.items[a.lpt[t]];
-        if constexpr (FOLD) next_mi = a.imerge[a.lpt[t]];
+        next = a.items_lpt[t];
+        if constexpr (FOLD) next_mi = next.pad[0];
       }
       claimed = true;
     };

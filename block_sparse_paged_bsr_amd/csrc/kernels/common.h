@@ -29,6 +29,7 @@ struct RunArgs {
   const int32_t* mslots;
   const int32_t* mroff;  // partial-row offset per merge slot (records with has_roff)
   const int32_t* lpt;    // items in the plan's LPT order, as positions in `items`
+  const ItemRec* items_lpt;  // copies of the items in that order; pad[0] = their merge record or -1
   int32_t* tickets;      // per workgroup group: next ticket, finished workgroups (zero between calls)
   int32_t num_items;
   const int32_t* imerge;  // per item (queue order): merge record of its split tile, or -1

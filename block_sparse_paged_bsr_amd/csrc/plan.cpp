@@ -282,6 +282,7 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
   L.mslots = off;   off = align256(off + sizeof(int32_t) * std::max<size_t>(p->merge_slots.size(), 1));
   L.mroff = off;    off = align256(off + sizeof(int32_t));  // (no row offsets in a single-level plan)
   L.lpt = off;      off = align256(off + sizeof(int32_t) * std::max(M, 1));
+  L.items_lpt = off; off = align256(off + sizeof(ItemRec) * std::max(M, 1));
   L.tickets = off;  off = align256(off + sizeof(int32_t) * 2 * kTicketGroups);
   L.imerge = off;   off = align256(off + sizeof(int32_t) * std::max(M, 1));
   L.arrive = off;   off = align256(off + sizeof(int32_t) * std::max<int64_t>(int64_t(NM) * p->Hk, 1));
@@ -344,6 +345,14 @@ int build_plan(const bsr_plan_desc* desc, bsr_plan* p) {
       im[k] = it.slot >= 0 ? tile_merge[it.tile] : -1;
     }
     p->item_folds = true;
+    // the records in LPT order, each with its merge record, so that the decode kernel takes an
+    // item with one dependent load
+    const auto* lpt = reinterpret_cast<const int32_t*>(p->meta.data() + L.lpt);
+    auto* ql = reinterpret_cast<ItemRec*>(p->meta.data() + L.items_lpt);
+    for (int32_t t = 0; t < M; ++t) {
+      ql[t] = qi[lpt[t]];
+      ql[t].pad[0] = im[lpt[t]];
+    }
   }
   return BSR_OK;
 }
